@@ -1,0 +1,193 @@
+/*
+ * fixedm.h - C ABI of the fixed-m ("const-max") attention forward library (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [CM] "Kernel reference: ring_attention_const_max_fwd const-max ring attention"
+ *        (AWS Neuron documentation page)
+ *   [FM] "feat(attention): fixed-m splash attention kernel with dynamic bounds and
+ *        safety fallbacks" (maxdiffusion pull request #477)
+ *   [UR] "feat(attention): 2D Ulysses+Ring attention with Global Virtual K-Centering"
+ *        (maxdiffusion pull request #478)
+ *
+ * What the library computes: non-causal softmax attention O = softmax(s Q K^T) V where,
+ * for every (batch, head, q-block) that passes the gate, the online-softmax running max
+ * is replaced by a fixed integer shift m = ceil(U) - C(N) and the numerator and the
+ * row sum accumulate in fp32 by pure addition across K/V chunks ([FM] Summary; [CM]
+ * "A static bound makes the ring reduction pure addition").  Blocks that fail the gate
+ * take an exact online-softmax body instead ([UR] Summary, "Cross-Ring Safety Fallback").
+ * One final O = acc / l normalises ([CM] "Accumulate, then normalize once").
+ *
+ * Call sequence (one rank of the ring, on one GPU):
+ *   fixedm_bounds      once per forward: norms, k_mean, U, m, eligibility;
+ *   fixedm_run_init    once per forward: resets the host-side ring state;
+ *   fixedm_attn_fwd    once per visiting K/V chunk (or once with several chunks);
+ *   fixedm_finalize    once (or more): O = acc / l, optional log-sum-exp.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are described by fixedm_tensor: a device pointer plus element strides for
+ *     the batch, sequence and head axes; the head_dim axis is contiguous (stride 1).
+ *     Layout is token-major [B, S, H, D] as in the [CM] Interface table, but any strides
+ *     are accepted.  ptr must be 16-byte aligned and every stride a multiple of 8
+ *     elements (bf16) or 4 elements (fp32).
+ *   - Every device pointer and the stream belong to the caller.  The library never
+ *     allocates, frees or synchronises, and keeps no pointer after a call returns.
+ *     Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default stream).
+ *   - Host-checkable errors are returned before anything is enqueued.  A failed launch
+ *     returns FIXEDM_ERR_HIP.  Data-dependent ineligibility is never an error: it selects
+ *     the exact fallback body ([FM] commit message: contracts fail loudly, data picks the
+ *     path; [CM] Best practices: no selector for the only correct path).
+ *   - Only bf16 and fp32 inputs exist in this ABI.  fp16/fp8 would overflow the fixed-m
+ *     exponent window ([FM] commit message, dtype safety) and have no enum value.
+ */
+#ifndef FIXEDM_H
+#define FIXEDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FIXEDM_ABI_VERSION 1
+
+typedef enum {
+  FIXEDM_OK = 0,
+  FIXEDM_ERR_INVALID_ARGUMENT = -1,  /* null pointer, negative size, bad enum, bad abi_version */
+  FIXEDM_ERR_UNSUPPORTED_DTYPE = -2, /* dtype not bf16/fp32, or a path that lacks it */
+  FIXEDM_ERR_UNSUPPORTED_SHAPE = -3, /* head_dim, q_block, alignment or strides not supported */
+  FIXEDM_ERR_BOUNDS_MISMATCH = -4,   /* descriptor token/dims disagree with the call */
+  FIXEDM_ERR_STATE = -5,             /* ring state misuse, e.g. finalize before all N keys */
+  FIXEDM_ERR_HIP = -6                /* a HIP launch or runtime call failed */
+} fixedm_status;
+
+typedef enum { FIXEDM_BF16 = 1, FIXEDM_F32 = 2 } fixedm_dtype;
+
+/* Virtual K-centring ([FM] Summary; [UR] Summary).  The centring mode is recorded in the
+ * bounds descriptor and used by both the bound and the logits, so the unsound pairing of
+ * a raw-key bound with centred logits ([FM] "This PR is additive") cannot be expressed. */
+typedef enum {
+  FIXEDM_CENTER_NONE = 0,     /* k_mean = 0 */
+  FIXEDM_CENTER_SUPPLIED = 1, /* caller's fp32 [B, H, D] mean */
+  FIXEDM_CENTER_COMPUTE = 2   /* mean of the real keys of all chunks, fp64 sum, fp32 result */
+} fixedm_center;
+
+typedef struct {
+  const void* ptr;  /* device pointer to element [0, 0, 0, 0] */
+  int64_t stride_b; /* element strides; the head_dim axis has stride 1 */
+  int64_t stride_s;
+  int64_t stride_h;
+} fixedm_tensor;
+
+typedef struct {
+  int32_t abi_version;   /* must be FIXEDM_ABI_VERSION */
+  int32_t dtype;         /* fixedm_dtype of q, k and v */
+  int64_t batch;         /* B >= 1 */
+  int64_t heads;         /* H >= 1; MHA only (K/V have the same H as Q) */
+  int64_t head_dim;      /* D: 128 (bf16 and fp32) or 64 (fp32 only) */
+  int64_t sq;            /* resident query rows, >= 1 */
+  int64_t sk_total;      /* N: real keys over all chunks, >= 1 (unpadded, [UR] Summary) */
+  int64_t q_block;       /* rows per shift/eligibility block: positive multiple of 64 */
+  float softmax_scale;   /* s; 0 selects fp32(1/sqrt(D)) ([CM] Interface table) */
+  int32_t center;        /* fixedm_center */
+} fixedm_problem;
+
+/* Filled by fixedm_bounds; the caller owns it and must not modify it afterwards. */
+typedef struct {
+  fixedm_problem p;      /* copy of the problem, softmax_scale resolved */
+  int32_t log2_n;        /* ceil(log2 N) */
+  int32_t C;             /* C(N) = 127 - ceil(log2 N) - ceil(log2 256) ([FM] Summary) */
+  int32_t W;             /* W(N) = C(N) + 125 */
+  int32_t gate;          /* floor(W / 2) ([FM] "Why the gate is halved") */
+  int64_t n_qblocks;     /* ceil(sq / q_block) */
+  float alpha;           /* fp32(softmax_scale * log2(e)): base-2 logit factor */
+  int32_t reserved;
+  void* dev;             /* caller's device buffer of fixedm_bounds_bytes() bytes */
+  uint64_t token;        /* binds run states and calls to this descriptor */
+} fixedm_bounds_t;
+
+/* Host-side ring state: the first chunk visit initialises the accumulator, later
+ * visits add to it ([CM] Overview ring figure; "Accumulate, then normalize once"). */
+typedef struct {
+  uint64_t token;
+  int64_t kv_visited;    /* keys folded in so far */
+  int32_t calls;         /* fixedm_attn_fwd calls so far */
+  int32_t reserved;
+} fixedm_run_t;
+
+/* Byte offsets of the arrays fixedm_bounds writes into the descriptor's device buffer.
+ * m: int32 [B, H, nQB]; elig: uint8 [B, H, nQB] (1 = fixed-m body); u: fp64 [B, H, nQB];
+ * q2: fp64 [B, H, nQB] (max of sum_d q^2 over the block's real rows); k2: fp64 [B, H]
+ * (max of sum_d (k - k_mean)^2 over all keys); k_mean: fp32 [B, H, D]; v_bad: int32
+ * (count of V elements with !(|v| <= 256); v_ok = (v_bad == 0)). */
+typedef struct {
+  size_t m, elig, u, q2, k2, k_mean, v_bad, scratch, total;
+} fixedm_bounds_layout_t;
+
+/* Size of the device buffer fixedm_bounds needs, or 0 if the problem is invalid. */
+size_t fixedm_bounds_bytes(const fixedm_problem* p);
+
+/* Offsets of the arrays inside that buffer.  Returns FIXEDM_ERR_* on an invalid problem. */
+fixedm_status fixedm_bounds_layout(const fixedm_problem* p, fixedm_bounds_layout_t* out);
+
+/* Size of the accumulator workspace fixedm_attn_fwd/fixedm_finalize use (fp32 acc, row
+ * sum l and row shift r for every padded query row), or 0 if the problem is invalid. */
+size_t fixedm_workspace_bytes(const fixedm_problem* p);
+
+/* Host-only constants of [FM] Summary for n >= 1 keys:
+ * log2_n = ceil(log2 n), C = 127 - log2_n - 8, W = C + 125, gate = floor(W / 2).
+ * Any output pointer may be NULL.  n < 1 -> FIXEDM_ERR_INVALID_ARGUMENT. */
+fixedm_status fixedm_constants(int64_t n, int32_t* log2_n, int32_t* C, int32_t* W,
+                               int32_t* gate);
+
+/* Bounds and gate ([FM] Summary; [CM] "Picking a max that is safe without measuring it",
+ * "Transpose prologue with fused norms"; [UR] Summary, merged norm reduction):
+ *   k_mean  per centring mode (COMPUTE: fp32(fp64 sum of all real keys / N));
+ *   q2[b,h,beta] = max over the block's real rows of sum_d q_d^2        (fp64);
+ *   k2[b,h]      = max over all keys of all chunks of sum_d (k_d - k_mean_d)^2 (fp64);
+ *   u  = alpha64 * sqrt(q2 * k2), alpha64 = fp64(s) * log2(e);  m = ceil(u) - C;
+ *   elig = (no |v| > 256 anywhere in V) && u <= gate && u finite.
+ * q: [B, sq, H, D]; k_chunks/v_chunks: n_chunks tensors of [B, chunk_len[c], H, D];
+ * sum(chunk_len) must equal p->sk_total.  k_mean_in: device fp32 [B, H, D] contiguous,
+ * required iff center == SUPPLIED.  bounds_dev: device buffer of fixedm_bounds_bytes(p)
+ * bytes, 256-byte aligned.  On success *out describes the result (valid once the stream
+ * reaches this point).  Enqueues 4-5 kernels; no host synchronisation. */
+fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q,
+                            const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
+                            const int64_t* chunk_len, int32_t n_chunks,
+                            const float* k_mean_in, void* bounds_dev,
+                            fixedm_bounds_t* out, void* stream);
+
+/* Starts a new ring pass over the descriptor's K/V: zero keys visited. */
+fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run);
+
+/* One or more ring steps ([CM] Overview ring figure, "The ring loop"): folds n_chunks
+ * K/V chunks (in the given order) into the caller's workspace.  The first keys of a run
+ * initialise the workspace, later ones add to it: pure addition for eligible blocks,
+ * the online-softmax rescale merge for the others.  q: [B, sq, H, D] (the same rows the
+ * bounds were computed from); chunks as in fixedm_bounds.  workspace: device buffer of
+ * fixedm_workspace_bytes() bytes, 256-byte aligned.  Errors: FIXEDM_ERR_BOUNDS_MISMATCH
+ * if run->token does not match the descriptor, FIXEDM_ERR_STATE if the keys visited
+ * would exceed sk_total.  Updates *run on success. */
+fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run,
+                              fixedm_tensor q, const fixedm_tensor* k_chunks,
+                              const fixedm_tensor* v_chunks, const int64_t* chunk_len,
+                              int32_t n_chunks, void* workspace, void* stream);
+
+/* O = acc / l, cast to out_dtype (bf16 by round-to-nearest-even, or fp32), written to
+ * out [B, sq, H, D]; if lse is non-NULL also lse[b, h, i] = ln2 * (r_i + log2 l_i), the
+ * natural-log log-sum-exp of row i ([CM] Interface table, training output), as a
+ * contiguous fp32 [B, H, sq] device array.  Requires run->kv_visited == sk_total
+ * (FIXEDM_ERR_STATE otherwise).  Reads the workspace only, so it may be called again. */
+fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run,
+                              const void* workspace, fixedm_tensor out, int32_t out_dtype,
+                              float* lse, void* stream);
+
+/* Static string naming a status code. */
+const char* fixedm_status_string(fixedm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIXEDM_H */

@@ -1,0 +1,338 @@
+"""Pins of the fp64 oracle against things other than itself: numbers printed on the pages
+(tests/golden, each with its citation), closed forms, textbook special cases, brute force
+with pure-Python loops, independent library routines (scipy.special) and the method's
+invariants.  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+from dit_amd import workloads as WL
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- constants -----------
+def test_printed_constants(golden_dir):
+    for case in _load(golden_dir, "printed_constants.json")["cases"]:
+        L, C, W, gate = O.constants(case["n"])
+        assert W == case["W"], case["cite"]
+        assert gate == case["gate"], case["cite"]
+        if "C" in case:
+            assert C == case["C"], case["cite"]
+
+
+def test_ceil_log2_bruteforce():
+    for n in list(range(1, 5000)) + [2**k + d for k in range(13, 40) for d in (-1, 0, 1)]:
+        L = 0
+        while (1 << L) < n:
+            L += 1
+        assert O.ceil_log2(n) == L, n
+    with pytest.raises(ValueError):
+        O.ceil_log2(0)
+
+
+def test_constants_closed_form():
+    for n in [1, 2, 3, 255, 256, 257, 4096, 37800, 75600, 131072, 131073]:
+        L, C, W, gate = O.constants(n)
+        assert C == 127 - L - 8 and W == C + 125 and gate == W // 2
+        # fp32 headroom: N * 2^C * Vmax <= 2^127 < the largest fp32
+        assert n * 2.0**C * O.VMAX <= 2.0**127
+
+
+def test_gate_is_tight_window_sweep():
+    """Every U <= gate keeps the worst shifted exponent >= -125, and every U just above
+    the gate breaks it ([FM] Summary inequality): floor(W/2) is exactly the largest
+    admissible integer bound."""
+    for n in [256, 4096, 37800, 75600]:
+        L, C, W, gate = O.constants(n)
+        for u in np.arange(0.0, gate + 1e-9, 1e-3):
+            assert O.window_lower_edge(float(u), C) >= -125.0
+        for eps in (1e-6, 1e-3, 0.5, 1.0):
+            assert O.window_lower_edge(gate + eps, C) < -125.0
+
+
+# ---------------------------------------------------------------- soundness cases -----
+def test_raw_key_bound_unsound(golden_dir):
+    g = _load(golden_dir, "raw_key_unsound.json")
+    r = O.raw_key_unsound_case(g["n_keys"], g["key_norm"])
+    assert r["raw_u"] == g["raw_bound"] and r["gate"] == g["gate"]
+    assert r["raw_passes_gate"]
+    assert abs(r["centred_max_logit"] - g["centred_max_logit_approx"]) <= g["centred_max_logit_abs_tol"]
+    assert r["max_exponent"] > g["min_shifted_exponent_exceeds"]
+    assert r["verdict"] == "rejected"
+    # the sound pairing: the bound measured on the centred keys fails the gate
+    assert not r["centred_passes_gate"] and r["centred_u"] > g["gate"]
+
+
+def test_adversarial_query_fails_halved_gate(golden_dir):
+    g = _load(golden_dir, "adversarial_gate.json")
+    rng = np.random.default_rng(7)
+    n, d = g["n_keys"], 16
+    keys = rng.standard_normal((n, d))
+    keys -= keys.mean(axis=0)
+    keys /= np.linalg.norm(keys, axis=1).max()
+    scale = 0.25
+    alpha = O.alpha_of(scale)
+    qdir = rng.standard_normal((8, d))
+    q = qdir / np.linalg.norm(qdir, axis=1, keepdims=True) * (g["query_base2_norm"] / alpha)
+    b = O.bounds(q[None, :, None, :], [keys[None, :, None, :]], [np.zeros((1, n, 1, d))],
+                 scale=scale, q_block=8, center="none", dtype="fp32")
+    assert (b.W, b.gate) == (g["W"], g["gate"])
+    u = float(b.u[0, 0, 0])
+    assert abs(u - g["query_base2_norm"]) < 1e-9
+    assert u <= b.W            # would pass a full-W gate
+    assert not b.elig[0, 0, 0]  # the halved gate rejects it
+    assert int(b.m[0, 0, 0]) == math.ceil(u) - b.C == 125
+
+
+# ---------------------------------------------------------------- bounds --------------
+def _bounds_bruteforce(q, kc, vc, scale, q_block, kbar):
+    """Pure-Python loops over the same definition (fsum for the k mean)."""
+    B, Sq, H, D = q.shape
+    keys = np.concatenate(kc, axis=1)
+    N = keys.shape[1]
+    out = {}
+    for b in range(B):
+        for h in range(H):
+            k2 = 0.0
+            for j in range(N):
+                s = 0.0
+                for d in range(D):
+                    t = float(keys[b, j, h, d]) - float(kbar[b, h, d])
+                    s += t * t
+                k2 = max(k2, s)
+            for beta in range(-(-Sq // q_block)):
+                q2 = 0.0
+                for i in range(beta * q_block, min((beta + 1) * q_block, Sq)):
+                    s = 0.0
+                    for d in range(D):
+                        s += float(q[b, i, h, d]) ** 2
+                    q2 = max(q2, s)
+                u = float(np.float32(scale)) * 1.4426950408889634 * math.sqrt(q2 * k2)
+                out[(b, h, beta)] = (q2, k2, u)
+    return out
+
+
+@pytest.mark.parametrize("center", ["none", "compute", "supplied"])
+def test_bounds_bruteforce(center):
+    inp = WL.generic_inputs(11, "bf16", 2, 3, 8, 21, (7, 6), q_block=8, center=center,
+                            k_offset=2.0 if center != "none" else 0.0)
+    q, kc, vc = inp.q, inp.k, inp.v
+    scale = 0.3
+    kmean = inp.k_mean if center == "supplied" else None
+    b = O.bounds(q, kc, vc, scale=scale, q_block=8, center=center, k_mean=kmean)
+    keys = np.concatenate(kc, axis=1).astype(np.float64)
+    N = keys.shape[1]
+    if center == "compute":
+        exact = np.zeros(b.k_mean.shape, dtype=np.float32)
+        for bb in range(2):
+            for h in range(3):
+                for d in range(8):
+                    col = [Fraction(float(x)) for x in keys[bb, :, h, d]]
+                    exact[bb, h, d] = np.float32(float(sum(col)) / N)
+        assert np.array_equal(exact, b.k_mean)
+        kbar = exact
+    elif center == "supplied":
+        kbar = inp.k_mean
+        assert np.array_equal(b.k_mean, kbar)
+    else:
+        kbar = np.zeros((2, 3, 8), np.float32)
+        assert not b.k_mean.any()
+    ref = _bounds_bruteforce(q, kc, vc, scale, 8, kbar)
+    L, C, W, gate = O.constants(N)
+    for (bb, h, beta), (q2, k2, u) in ref.items():
+        assert b.q2[bb, h, beta] == q2
+        assert b.k2[bb, h] == k2
+        assert b.u[bb, h, beta] == u
+        assert b.m[bb, h, beta] == math.ceil(u) - C
+        assert bool(b.elig[bb, h, beta]) == (u <= gate)
+
+
+def test_v_bound_inclusive_and_nan():
+    q = np.ones((1, 4, 1, 4))
+    k = [np.ones((1, 5, 1, 4))]
+    for vmax, ok in [(256.0, True), (np.nextafter(256.0, 1e9), False), (-256.0, True), (-257.0, False)]:
+        v = np.zeros((1, 5, 1, 4))
+        v[0, 2, 0, 1] = vmax
+        b = O.bounds(q, k, [v], scale=0.5, q_block=64)
+        assert b.v_ok == ok and bool(b.elig.all()) == ok
+    v = np.zeros((1, 5, 1, 4))
+    v[0, 0, 0, 0] = np.nan
+    b = O.bounds(q, k, [v], scale=0.5, q_block=64)
+    assert not b.v_ok and not b.elig.any()
+
+
+def test_dtype_and_nonfinite():
+    q = np.ones((1, 4, 1, 4))
+    k = [np.ones((1, 5, 1, 4))]
+    v = [np.zeros((1, 5, 1, 4))]
+    assert not O.bounds(q, k, v, scale=0.5, q_block=64, dtype="fp16").elig.any()
+    assert O.bounds(q, k, v, scale=0.5, q_block=64, dtype="fp32").elig.all()
+    qi = q.copy()
+    qi[0, 1, 0, 2] = np.inf
+    b = O.bounds(qi, k, v, scale=0.5, q_block=64)
+    assert not b.elig.any() and b.m[0, 0, 0] == O.INT32_MAX
+
+
+# ---------------------------------------------------------------- attention -----------
+def test_attention_bruteforce_and_scipy():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 5, 3, 4))
+    k = rng.standard_normal((2, 7, 3, 4))
+    v = rng.standard_normal((2, 7, 3, 4))
+    o, lse = O.attention(q, k, v, 0.7)
+    ob = O.attention_bruteforce(q, k, v, 0.7)
+    assert np.max(np.abs(o - ob)) < 1e-13
+    s = float(np.float32(0.7)) * np.einsum("bqhd,bkhd->bhqk", q, k)
+    w = scipy.special.softmax(s, axis=-1)
+    oref = np.einsum("bhqk,bkhd->bqhd", w, v)
+    assert np.max(np.abs(o - oref)) < 1e-13
+    assert np.max(np.abs(lse - scipy.special.logsumexp(s, axis=-1))) < 1e-12
+
+
+def test_attention_special_cases(golden_dir):
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((1, 9, 2, 4))
+    v = rng.standard_normal((1, 9, 2, 4))
+    # q = 0: every weight equal, O = mean of v
+    o, lse = O.attention(np.zeros((1, 3, 2, 4)), k, v, 1.0)
+    assert np.allclose(o, v.mean(axis=1, keepdims=True), atol=1e-14)
+    assert np.allclose(lse, math.log(9), atol=1e-14)
+    # a single key: O = v
+    q = rng.standard_normal((1, 3, 2, 4))
+    o, _ = O.attention(q, k[:, :1], v[:, :1], 1.0)
+    assert np.allclose(o, np.broadcast_to(v[:, :1], o.shape), atol=1e-14)
+    # identical keys: O = mean of v
+    kk = np.broadcast_to(k[:, :1], k.shape)
+    o, _ = O.attention(q, kk, v, 1.0)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), atol=1e-13)
+    # the printed layout example: two heads, 3 tokens, head_dim 1
+    g = _load(golden_dir, "layout_example.json")
+    vals = np.array(g["values_per_head"]).T[None, :, :, None]      # [1, 3, 2, 1]
+    o, _ = O.attention(np.zeros((1, 3, 2, 1)), np.zeros((1, 3, 2, 1)), vals, 1.0)
+    assert np.allclose(o[0, :, :, 0], np.array(g["expected_per_head"])[None, :], atol=1e-14)
+    assert not np.allclose(o[0, 0, :, 0], g["buggy_per_head"])
+
+
+def test_mass_is_one_per_row():
+    inp = WL.make_inputs(1)
+    q = inp.q[0, :, 0].astype(np.float64)
+    k = np.concatenate(inp.k, axis=1)[0, :, 0].astype(np.float64)
+    v = np.concatenate(inp.v, axis=1)[0, :, 0].astype(np.float64)
+    _, lse = O.attention(q[None, :, None], k[None, :, None], v[None, :, None], inp.wl.scale)
+    mass = O.softmax_mass(q, k, inp.wl.scale, lse[0, 0])
+    assert np.max(np.abs(mass - 1.0)) < 1e-12
+
+
+# ---------------------------------------------------------------- the two bodies ------
+def _cfg1_head():
+    inp = WL.make_inputs(1)
+    q = inp.q[0, :, 0].astype(np.float64)
+    kc = [c[0, :, 0].astype(np.float64) for c in inp.k]
+    vc = [c[0, :, 0].astype(np.float64) for c in inp.v]
+    return inp, q, kc, vc
+
+
+def test_fixed_m_body_equals_softmax_and_is_shift_invariant():
+    inp, q, kc, vc = _cfg1_head()
+    scale = inp.wl.scale
+    b = O.bounds(q[None, :, None], [c[None, :, None] for c in kc], [c[None, :, None] for c in vc],
+                 scale=scale, q_block=256)
+    assert b.elig.all()
+    ref, lse_ref = O.attention(q[None, :, None], np.concatenate(kc)[None, :, None],
+                               np.concatenate(vc)[None, :, None], scale)
+    ref, lse_ref = ref[0, :, 0], lse_ref[0, 0]
+    m = int(b.m[0, 0, 0])
+    o, lse, e0, e1 = O.fixed_m_emulate(q, kc, vc, scale=scale, k_mean=np.zeros(64), m=m, C=b.C)
+    assert -125 <= e0 and e1 <= b.C
+    assert np.max(np.abs(o - ref)) < 1e-12 and np.max(np.abs(lse - lse_ref)) < 1e-12
+    for dm in (-3, 3):
+        o2, lse2, _, _ = O.fixed_m_emulate(q, kc, vc, scale=scale, k_mean=np.zeros(64),
+                                           m=m + dm, C=b.C, check_window=False)
+        assert np.max(np.abs(o2 - ref)) < 1e-12 and np.max(np.abs(lse2 - lse_ref)) < 1e-12
+    kbar = np.random.default_rng(5).standard_normal(64).astype(np.float32)
+    o3, lse3, _, _ = O.fixed_m_emulate(q, kc, vc, scale=scale, k_mean=kbar, m=m, C=b.C,
+                                       check_window=False)
+    assert np.max(np.abs(o3 - ref)) < 1e-12 and np.max(np.abs(lse3 - lse_ref)) < 1e-12
+    # chunk order does not matter (pure addition)
+    o4, _, _, _ = O.fixed_m_emulate(q, kc[::-1], vc[::-1], scale=scale, k_mean=np.zeros(64), m=m, C=b.C)
+    assert np.max(np.abs(o4 - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("block", [1, 7, 64, 1000])
+def test_online_body_equals_softmax(block):
+    inp, q, kc, vc = _cfg1_head()
+    ref, lse_ref = O.attention(q[None, :, None], np.concatenate(kc)[None, :, None],
+                               np.concatenate(vc)[None, :, None], inp.wl.scale)
+    o, lse = O.online_softmax_emulate(q, kc, vc, scale=inp.wl.scale, block=block)
+    assert np.max(np.abs(o - ref[0, :, 0])) < 1e-12
+    assert np.max(np.abs(lse - lse_ref[0, 0])) < 1e-12
+
+
+@pytest.mark.parametrize("q_block", [64, 256])
+def test_method_forward_tiny_config(q_block):
+    inp = WL.make_inputs(1)
+    wl = inp.wl
+    b = O.bounds(inp.q, inp.k, inp.v, scale=wl.scale, q_block=q_block, center=wl.center)
+    o, lse, windows = O.method_forward(inp.q, inp.k, inp.v, b, scale=wl.scale, q_block=q_block)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), wl.scale)
+    assert np.max(np.abs(o - ref)) < 1e-12 and np.max(np.abs(lse - lse_ref)) < 1e-12
+    assert len(windows) == b.elig.sum() > 0
+    for (_, _, _, e0, e1) in windows:
+        assert e0 >= -125 and e1 <= b.C
+
+
+def test_method_forward_mixed_bodies_and_centring():
+    """Offset keys with centring on, one adversarial head that must fall back."""
+    inp = WL.generic_inputs(21, "fp32", 1, 3, 16, 70, (40, 33), q_block=64, k_offset=3.0)
+    q = inp.q.astype(np.float64)
+    q[:, :, 2] *= 60.0                      # head 2 loud: fails the gate
+    scale = 0.25
+    b = O.bounds(q, inp.k, inp.v, scale=scale, q_block=64, center="compute", dtype="fp32")
+    assert b.elig[0, :2].all() and not b.elig[0, 2].any()
+    o, lse, windows = O.method_forward(q, inp.k, inp.v, b, scale=scale, q_block=64, block=16)
+    ref, lse_ref = O.attention(q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), scale)
+    assert np.max(np.abs(o - ref)) < 1e-11 and np.max(np.abs(lse - lse_ref)) < 1e-11
+
+
+# ---------------------------------------------------------------- planted mistakes ----
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
+    """Mistakes planted in the oracle (on the CPU) trip the pins above."""
+    mod = O.fixedm_oracle
+    cases = _load(golden_dir, "printed_constants.json")["cases"]
+    real_constants = mod.constants
+    # 1. floor instead of ceil for log2 N: the printed W values no longer match
+    monkeypatch.setattr(mod, "ceil_log2", lambda n: max(n.bit_length() - 1, 0))
+    assert any(mod.constants(c["n"])[2] != c["W"] for c in cases)
+    monkeypatch.undo()
+    # 2. the full window W used as the gate: the adversarial query becomes eligible
+    monkeypatch.setattr(mod, "constants", lambda n, vmax=O.VMAX: real_constants(n, vmax)[:3]
+                        + (real_constants(n, vmax)[2],))
+    rng = np.random.default_rng(7)
+    keys = rng.standard_normal((4096, 16))
+    keys -= keys.mean(axis=0)
+    keys /= np.linalg.norm(keys, axis=1).max()
+    q = np.ones((1, 4, 1, 16)) / 4.0 * (231.01 / mod.alpha_of(0.25))
+    b = mod.bounds(q, [keys[None, :, None]], [np.zeros((1, 4096, 1, 16))], scale=0.25, q_block=64)
+    assert b.elig.all()          # test_adversarial_query_fails_halved_gate would fail
+    monkeypatch.undo()
+    # 3. a sign error in the fixed-m exponent: the body no longer equals softmax
+    inp, qh, kc, vc = _cfg1_head()
+    ref, _ = O.attention(qh[None, :, None], np.concatenate(kc)[None, :, None],
+                         np.concatenate(vc)[None, :, None], inp.wl.scale)
+    o_bad, _, _, _ = O.fixed_m_emulate(-qh, kc, vc, scale=inp.wl.scale, k_mean=np.zeros(64),
+                                       m=0, C=200, check_window=False)
+    assert np.max(np.abs(o_bad - ref[0, :, 0])) > 1e-3
+    # 4. a transposed operand (keys used as values) is caught by the brute-force pin
+    rng = np.random.default_rng(3)
+    qq, kk, vv = (rng.standard_normal((1, 5, 1, 4)) for _ in range(3))
+    assert np.max(np.abs(O.attention(qq, kk, kk, 0.7)[0] - O.attention_bruteforce(qq, kk, vv, 0.7))) > 1e-3
