@@ -1,0 +1,392 @@
+// C ABI of libfixedm: argument validation, descriptor/state bookkeeping and kernel dispatch.
+// Every host-checkable error is reported before anything is enqueued.
+//
+// Sources (page title, section):
+//   [FM] "feat(attention): fixed-m splash attention kernel with dynamic bounds and safety
+//        fallbacks": Summary (C(N), W(N), gate), commit message (metadata contracts raise
+//        at entry; fp16/fp8 rejected).
+//   [CM] "Kernel reference: ring_attention_const_max_fwd const-max ring attention":
+//        Interface table (softmax_scale defaults to 1/sqrt(d)), Overview ring figure (step 0
+//        initialises, later steps add), Best practices (no selector for the only path).
+#include <math.h>
+#include <string.h>
+
+#include "fixedm_internal.h"
+
+using namespace fixedm;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;  // log2(e), fp64
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int32_t ceil_log2_i64(int64_t n) {
+  int32_t L = 0;
+  while (L < 63 && ((int64_t)1 << L) < n) ++L;
+  return L;
+}
+
+fixedm_status check_problem(const fixedm_problem* p) {
+  if (p == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->abi_version != FIXEDM_ABI_VERSION) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->dtype != FIXEDM_BF16 && p->dtype != FIXEDM_F32) return FIXEDM_ERR_UNSUPPORTED_DTYPE;
+  if (p->batch < 1 || p->heads < 1 || p->sq < 1 || p->sk_total < 1 || p->head_dim < 1)
+    return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->center < FIXEDM_CENTER_NONE || p->center > FIXEDM_CENTER_COMPUTE)
+    return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (!(p->softmax_scale >= 0.0f) || !isfinite(p->softmax_scale)) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->dtype == FIXEDM_BF16 && p->head_dim != 128) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->dtype == FIXEDM_F32 && p->head_dim != 64 && p->head_dim != 128) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->q_block < 64 || p->q_block % 64 != 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  // grid limits of the kernels (y dimension = B*H; 32-bit row indices)
+  if (p->batch * p->heads > 65535) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->sq > (int64_t)1 << 30 || p->sk_total > ((int64_t)1 << 40)) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  const int64_t n_qtiles = (p->sq + kQTile - 1) / kQTile;
+  if (p->batch * p->heads * n_qtiles > ((int64_t)1 << 31) - 1) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  return FIXEDM_OK;
+}
+
+float resolved_scale(const fixedm_problem& p) {
+  if (p.softmax_scale > 0.0f) return p.softmax_scale;
+  return (float)(1.0 / sqrt((double)p.head_dim));
+}
+
+fixedm_status check_tensor(const fixedm_problem& p, const fixedm_tensor& t) {
+  if (t.ptr == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)t.ptr & 15) != 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  const int64_t vec = p.dtype == FIXEDM_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (t.stride_b % vec || t.stride_s % vec || t.stride_h % vec) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  return FIXEDM_OK;
+}
+
+fixedm_status check_out_tensor(const fixedm_problem& p, const fixedm_tensor& t, int32_t dt) {
+  if (t.ptr == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)t.ptr & 15) != 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  const int64_t vec = dt == FIXEDM_BF16 ? 4 : 4;  // 4 elements per store (8 or 16 bytes)
+  if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (t.stride_b % vec || t.stride_s % vec || t.stride_h % vec) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  (void)p;
+  return FIXEDM_OK;
+}
+
+fixedm_status check_chunks(const fixedm_problem& p, const fixedm_tensor* kc, const fixedm_tensor* vc,
+                           const int64_t* len, int32_t n, int64_t* total) {
+  if (n < 1 || kc == nullptr || vc == nullptr || len == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  int64_t s = 0;
+  for (int32_t c = 0; c < n; ++c) {
+    if (len[c] < 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+    if (len[c] == 0) continue;
+    fixedm_status st = check_tensor(p, kc[c]);
+    if (st != FIXEDM_OK) return st;
+    st = check_tensor(p, vc[c]);
+    if (st != FIXEDM_OK) return st;
+    s += len[c];
+  }
+  *total = s;
+  return FIXEDM_OK;
+}
+
+uint64_t fnv1a(uint64_t h, const void* data, size_t n) {
+  const unsigned char* c = static_cast<const unsigned char*>(data);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= c[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+uint64_t descriptor_token(const fixedm_bounds_t& b) {
+  uint64_t h = 14695981039346656037ull;
+  const fixedm_problem& p = b.p;
+  h = fnv1a(h, &p.abi_version, sizeof p.abi_version);
+  h = fnv1a(h, &p.dtype, sizeof p.dtype);
+  h = fnv1a(h, &p.batch, sizeof p.batch);
+  h = fnv1a(h, &p.heads, sizeof p.heads);
+  h = fnv1a(h, &p.head_dim, sizeof p.head_dim);
+  h = fnv1a(h, &p.sq, sizeof p.sq);
+  h = fnv1a(h, &p.sk_total, sizeof p.sk_total);
+  h = fnv1a(h, &p.q_block, sizeof p.q_block);
+  h = fnv1a(h, &p.softmax_scale, sizeof p.softmax_scale);
+  h = fnv1a(h, &p.center, sizeof p.center);
+  h = fnv1a(h, &b.log2_n, sizeof b.log2_n);
+  h = fnv1a(h, &b.C, sizeof b.C);
+  h = fnv1a(h, &b.W, sizeof b.W);
+  h = fnv1a(h, &b.gate, sizeof b.gate);
+  h = fnv1a(h, &b.n_qblocks, sizeof b.n_qblocks);
+  h = fnv1a(h, &b.alpha, sizeof b.alpha);
+  h = fnv1a(h, &b.dev, sizeof b.dev);
+  return h | 1ull;  // never 0, so a zeroed run state never matches
+}
+
+fixedm_status check_descriptor(const fixedm_bounds_t* b) {
+  if (b == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (b->dev == nullptr || b->token == 0) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  if (check_problem(&b->p) != FIXEDM_OK) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  if (descriptor_token(*b) != b->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  return FIXEDM_OK;
+}
+
+ChunkDesc make_chunk(const fixedm_tensor& k, const fixedm_tensor& v, int64_t len, int64_t start) {
+  ChunkDesc c;
+  c.k = k.ptr;
+  c.v = v.ptr;
+  c.k_sb = k.stride_b; c.k_ss = k.stride_s; c.k_sh = k.stride_h;
+  c.v_sb = v.stride_b; c.v_ss = v.stride_s; c.v_sh = v.stride_h;
+  c.len = len;
+  c.start = start;
+  return c;
+}
+
+}  // namespace
+
+namespace fixedm {
+
+bool bounds_layout(const fixedm_problem& p, BoundsLayout* out) {
+  if (check_problem(&p) != FIXEDM_OK) return false;
+  const size_t nqb = (size_t)((p.sq + p.q_block - 1) / p.q_block);
+  const size_t bh = (size_t)(p.batch * p.heads);
+  size_t off = 0;
+  out->m = off; off = align256(off + bh * nqb * 4);
+  out->elig = off; off = align256(off + bh * nqb);
+  out->u = off; off = align256(off + bh * nqb * 8);
+  out->q2 = off; off = align256(off + bh * nqb * 8);
+  out->k2 = off; off = align256(off + bh * 8);
+  out->k_mean = off; off = align256(off + bh * (size_t)p.head_dim * 4);
+  out->v_bad = off; off = align256(off + 4);
+  out->scratch = off;
+  if (p.center == FIXEDM_CENTER_COMPUTE) off = align256(off + (size_t)kKmeanSlabs * bh * p.head_dim * 8);
+  out->total = off;
+  return true;
+}
+
+bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out) {
+  if (check_problem(&p) != FIXEDM_OK) return false;
+  out->n_qtiles = (p.sq + kQTile - 1) / kQTile;
+  out->sq_pad = out->n_qtiles * kQTile;
+  const size_t rows = (size_t)(p.batch * p.heads * out->sq_pad);
+  size_t off = 0;
+  out->acc = off; off = align256(off + rows * (size_t)p.head_dim * 4);
+  out->l = off; off = align256(off + rows * 4);
+  out->r = off; off = align256(off + rows * 4);
+  out->total = off;
+  return true;
+}
+
+}  // namespace fixedm
+
+extern "C" {
+
+const char* fixedm_status_string(fixedm_status s) {
+  switch (s) {
+    case FIXEDM_OK: return "FIXEDM_OK";
+    case FIXEDM_ERR_INVALID_ARGUMENT: return "FIXEDM_ERR_INVALID_ARGUMENT";
+    case FIXEDM_ERR_UNSUPPORTED_DTYPE: return "FIXEDM_ERR_UNSUPPORTED_DTYPE";
+    case FIXEDM_ERR_UNSUPPORTED_SHAPE: return "FIXEDM_ERR_UNSUPPORTED_SHAPE";
+    case FIXEDM_ERR_BOUNDS_MISMATCH: return "FIXEDM_ERR_BOUNDS_MISMATCH";
+    case FIXEDM_ERR_STATE: return "FIXEDM_ERR_STATE";
+    case FIXEDM_ERR_HIP: return "FIXEDM_ERR_HIP";
+  }
+  return "FIXEDM_UNKNOWN_STATUS";
+}
+
+fixedm_status fixedm_constants(int64_t n, int32_t* log2_n, int32_t* C, int32_t* W, int32_t* gate) {
+  if (n < 1) return FIXEDM_ERR_INVALID_ARGUMENT;
+  const int32_t L = ceil_log2_i64(n);
+  const int32_t c = 127 - L - 8;  // ceil(log2 Vmax) = 8 for Vmax = 256
+  const int32_t w = c + 125;
+  if (log2_n) *log2_n = L;
+  if (C) *C = c;
+  if (W) *W = w;
+  if (gate) *gate = w >= 0 ? w / 2 : -((-w + 1) / 2);  // floor(w / 2)
+  return FIXEDM_OK;
+}
+
+size_t fixedm_bounds_bytes(const fixedm_problem* p) {
+  BoundsLayout l;
+  if (p == nullptr || !bounds_layout(*p, &l)) return 0;
+  return l.total;
+}
+
+fixedm_status fixedm_bounds_layout(const fixedm_problem* p, fixedm_bounds_layout_t* out) {
+  const fixedm_status st = check_problem(p);
+  if (st != FIXEDM_OK) return st;
+  if (out == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  BoundsLayout l;
+  bounds_layout(*p, &l);
+  out->m = l.m; out->elig = l.elig; out->u = l.u; out->q2 = l.q2; out->k2 = l.k2;
+  out->k_mean = l.k_mean; out->v_bad = l.v_bad; out->scratch = l.scratch; out->total = l.total;
+  return FIXEDM_OK;
+}
+
+size_t fixedm_workspace_bytes(const fixedm_problem* p) {
+  WorkspaceLayout w;
+  if (p == nullptr || !workspace_layout(*p, &w)) return 0;
+  return w.total;
+}
+
+fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
+                            const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
+                            const float* k_mean_in, void* bounds_dev, fixedm_bounds_t* out, void* stream) {
+  fixedm_status st = check_problem(p);
+  if (st != FIXEDM_OK) return st;
+  if (out == nullptr || bounds_dev == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)bounds_dev & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if ((st = check_tensor(*p, q)) != FIXEDM_OK) return st;
+  if (n_chunks > kMaxBoundsChunks) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  int64_t total = 0;
+  if ((st = check_chunks(*p, k_chunks, v_chunks, chunk_len, n_chunks, &total)) != FIXEDM_OK) return st;
+  if (total != p->sk_total) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->center == FIXEDM_CENTER_SUPPLIED) {
+    if (k_mean_in == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)k_mean_in & 3) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  }
+
+  fixedm_bounds_t d;
+  memset(&d, 0, sizeof d);
+  d.p = *p;
+  d.p.softmax_scale = resolved_scale(*p);
+  fixedm_constants(p->sk_total, &d.log2_n, &d.C, &d.W, &d.gate);
+  d.n_qblocks = (p->sq + p->q_block - 1) / p->q_block;
+  const double alpha64 = (double)d.p.softmax_scale * kLog2e;
+  d.alpha = (float)alpha64;
+  d.dev = bounds_dev;
+  d.token = descriptor_token(d);
+
+  BoundsLayout lay;
+  bounds_layout(*p, &lay);
+  char* base = static_cast<char*>(bounds_dev);
+  BoundsArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_ss = q.stride_s; a.q_sh = q.stride_h;
+  int32_t nc = 0;
+  int64_t start = 0;
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    if (chunk_len[c] == 0) continue;
+    a.ch[nc++] = make_chunk(k_chunks[c], v_chunks[c], chunk_len[c], start);
+    start += chunk_len[c];
+  }
+  a.n_chunks = nc;
+  a.dtype = p->dtype;
+  a.B = (int32_t)p->batch; a.H = (int32_t)p->heads; a.D = (int32_t)p->head_dim;
+  a.Sq = p->sq; a.N = p->sk_total; a.q_block = p->q_block; a.nqb = d.n_qblocks;
+  a.center = p->center;
+  a.k_mean_in = k_mean_in;
+  a.alpha64 = alpha64;
+  a.C = d.C; a.gate = d.gate;
+  a.m = reinterpret_cast<int32_t*>(base + lay.m);
+  a.elig = reinterpret_cast<uint8_t*>(base + lay.elig);
+  a.u = reinterpret_cast<double*>(base + lay.u);
+  a.q2 = reinterpret_cast<unsigned long long*>(base + lay.q2);
+  a.k2 = reinterpret_cast<unsigned long long*>(base + lay.k2);
+  a.k_mean = reinterpret_cast<float*>(base + lay.k_mean);
+  a.v_bad = reinterpret_cast<int32_t*>(base + lay.v_bad);
+  a.kpart = reinterpret_cast<double*>(base + lay.scratch);
+  if (launch_bounds(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
+  *out = d;
+  return FIXEDM_OK;
+}
+
+fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run) {
+  const fixedm_status st = check_descriptor(bounds);
+  if (st != FIXEDM_OK) return st;
+  if (run == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  run->token = bounds->token;
+  run->kv_visited = 0;
+  run->calls = 0;
+  run->reserved = 0;
+  return FIXEDM_OK;
+}
+
+fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
+                              const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
+                              const int64_t* chunk_len, int32_t n_chunks, void* workspace, void* stream) {
+  fixedm_status st = check_descriptor(bounds);
+  if (st != FIXEDM_OK) return st;
+  if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  const fixedm_problem& p = bounds->p;
+  if ((st = check_tensor(p, q)) != FIXEDM_OK) return st;
+  int64_t total = 0;
+  if ((st = check_chunks(p, k_chunks, v_chunks, chunk_len, n_chunks, &total)) != FIXEDM_OK) return st;
+  if (run->kv_visited < 0 || run->kv_visited + total > p.sk_total) return FIXEDM_ERR_STATE;
+  if (total == 0) return FIXEDM_OK;
+
+  BoundsLayout lay;
+  bounds_layout(p, &lay);
+  WorkspaceLayout wl;
+  workspace_layout(p, &wl);
+  const char* bbase = static_cast<const char*>(bounds->dev);
+  char* wbase = static_cast<char*>(workspace);
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q.ptr; a.q_sb = q.stride_b; a.q_ss = q.stride_s; a.q_sh = q.stride_h;
+  a.B = (int32_t)p.batch; a.H = (int32_t)p.heads; a.D = (int32_t)p.head_dim;
+  a.Sq = (int32_t)p.sq; a.n_qtiles = (int32_t)wl.n_qtiles; a.sq_pad = (int32_t)wl.sq_pad;
+  a.q_block = (int32_t)p.q_block; a.nqb = (int32_t)bounds->n_qblocks;
+  a.m = reinterpret_cast<const int32_t*>(bbase + lay.m);
+  a.elig = reinterpret_cast<const uint8_t*>(bbase + lay.elig);
+  a.k_mean = reinterpret_cast<const float*>(bbase + lay.k_mean);
+  a.alpha = bounds->alpha;
+  a.alpha64 = (double)p.softmax_scale * kLog2e;
+  a.acc = reinterpret_cast<float*>(wbase + wl.acc);
+  a.l = reinterpret_cast<float*>(wbase + wl.l);
+  a.r = reinterpret_cast<float*>(wbase + wl.r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int64_t visited = run->kv_visited;
+  int32_t c = 0;
+  while (c < n_chunks) {
+    a.n_chunks = 0;
+    while (c < n_chunks && a.n_chunks < kMaxChunksPerLaunch) {
+      if (chunk_len[c] > 0) a.ch[a.n_chunks++] = make_chunk(k_chunks[c], v_chunks[c], chunk_len[c], 0);
+      ++c;
+    }
+    if (a.n_chunks == 0) break;
+    int64_t launched = 0;
+    for (int32_t i = 0; i < a.n_chunks; ++i) launched += a.ch[i].len;
+    a.accumulate = visited > 0 ? 1 : 0;
+    const hipError_t e = p.dtype == FIXEDM_BF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    if (e != hipSuccess) return FIXEDM_ERR_HIP;
+    visited += launched;
+  }
+  run->kv_visited = visited;
+  run->calls += 1;
+  return FIXEDM_OK;
+}
+
+fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run, const void* workspace,
+                              fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
+  fixedm_status st = check_descriptor(bounds);
+  if (st != FIXEDM_OK) return st;
+  if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (out_dtype != FIXEDM_BF16 && out_dtype != FIXEDM_F32) return FIXEDM_ERR_UNSUPPORTED_DTYPE;
+  const fixedm_problem& p = bounds->p;
+  if ((st = check_out_tensor(p, out, out_dtype)) != FIXEDM_OK) return st;
+  if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (run->kv_visited != p.sk_total) return FIXEDM_ERR_STATE;
+
+  WorkspaceLayout wl;
+  workspace_layout(p, &wl);
+  const char* wbase = static_cast<const char*>(workspace);
+  FinalizeArgs a;
+  memset(&a, 0, sizeof a);
+  a.acc = reinterpret_cast<const float*>(wbase + wl.acc);
+  a.l = reinterpret_cast<const float*>(wbase + wl.l);
+  a.r = reinterpret_cast<const float*>(wbase + wl.r);
+  a.out = const_cast<void*>(out.ptr);
+  a.o_sb = out.stride_b; a.o_ss = out.stride_s; a.o_sh = out.stride_h;
+  a.out_dtype = out_dtype;
+  a.lse = lse;
+  a.B = (int32_t)p.batch; a.H = (int32_t)p.heads; a.D = (int32_t)p.head_dim;
+  a.Sq = (int32_t)p.sq; a.n_qtiles = (int32_t)wl.n_qtiles; a.sq_pad = (int32_t)wl.sq_pad;
+  a.reg_layout = p.dtype == FIXEDM_BF16 ? 1 : 0;
+  if (launch_finalize(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
+  return FIXEDM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Finalize: O = acc / l once at the end, cast to the output dtype, optional log-sum-exp.
+//
+// Sources (page title, section):
+//   [CM] "Kernel reference: ring_attention_const_max_fwd const-max ring attention",
+//        "Accumulate, then normalize once" (a single division at the end) and the Interface
+//        table (lse = c_i + log(sum_exp) when training).
+//
+// The row sum is positive on every real row: under the gate every shifted exponent is at
+// least -125, so each term is a normal fp32 and l >= N * 2^-125; on fallback rows the
+// largest term is 2^0.  The page's 1e-37 clamp therefore never binds and is not applied.
+// lse is returned in natural-log units: ln 2 * (r + log2 l), where r is the row's shift
+// (m + alpha q.k_mean for fixed-m rows, the running max for fallback rows).
+#include <math.h>
+
+#include "fixedm_internal.h"
+
+namespace fixedm {
+namespace {
+
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline void store4(const FinalizeArgs& a, int b, int q, int h, int d0, float4 v) {
+  if (a.out_dtype == FIXEDM_F32) {
+    float* o = reinterpret_cast<float*>(a.out) + b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + d0;
+    *reinterpret_cast<float4*>(o) = v;
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + d0;
+    uint2 w;
+    w.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+    w.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2*>(o) = w;
+  }
+}
+
+__device__ inline float lse_of(float r, float l) {
+  return 0.69314718055994531f * (r + log2f(l));
+}
+
+// acc in the bf16 kernel's register order: [tile][wave 4][n 2][m 4][j 4][lane 64][4].
+__global__ void finalize_reg_kernel(FinalizeArgs a) {
+  const int64_t total = (int64_t)a.B * a.H * a.n_qtiles * 8192;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t tile = idx / 8192;
+  const int rem = (int)(idx % 8192);
+  const int lane = rem & 63, jj = (rem >> 6) & 3, m = (rem >> 8) & 3, n = (rem >> 10) & 1, wave = rem >> 11;
+  const int bh = (int)(tile / a.n_qtiles), qt = (int)(tile % a.n_qtiles);
+  const int q = qt * kQTile + wave * 64 + n * 32 + (lane & 31);
+  if (q >= a.Sq) return;
+  const int d0 = 32 * m + 8 * jj + 4 * (lane >> 5);
+  const int64_t rowi = (int64_t)bh * a.sq_pad + q;
+  const float l = a.l[rowi];
+  const float4 acc = reinterpret_cast<const float4*>(a.acc)[idx];
+  const float4 v = make_float4(__fdiv_rn(acc.x, l), __fdiv_rn(acc.y, l), __fdiv_rn(acc.z, l), __fdiv_rn(acc.w, l));
+  store4(a, bh / a.H, q, bh % a.H, d0, v);
+  if (a.lse != nullptr && m == 0 && jj == 0 && lane < 32)
+    a.lse[(int64_t)bh * a.Sq + q] = lse_of(a.r[rowi], l);
+}
+
+// acc row-major: [bh][sq_pad][D].
+__global__ void finalize_row_kernel(FinalizeArgs a) {
+  const int per_row = a.D / 4;
+  const int64_t total = (int64_t)a.B * a.H * a.Sq * per_row;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c4 = (int)(idx % per_row);
+  const int64_t rq = idx / per_row;
+  const int q = (int)(rq % a.Sq);
+  const int bh = (int)(rq / a.Sq);
+  const int64_t rowi = (int64_t)bh * a.sq_pad + q;
+  const float l = a.l[rowi];
+  const float4 acc = reinterpret_cast<const float4*>(a.acc + rowi * a.D)[c4];
+  const float4 v = make_float4(__fdiv_rn(acc.x, l), __fdiv_rn(acc.y, l), __fdiv_rn(acc.z, l), __fdiv_rn(acc.w, l));
+  store4(a, bh / a.H, q, bh % a.H, 4 * c4, v);
+  if (a.lse != nullptr && c4 == 0) a.lse[(int64_t)bh * a.Sq + q] = lse_of(a.r[rowi], l);
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+  if (a.reg_layout) {
+    const int64_t total = (int64_t)a.B * a.H * a.n_qtiles * 8192;
+    finalize_reg_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+  } else {
+    const int64_t total = (int64_t)a.B * a.H * a.Sq * (a.D / 4);
+    finalize_row_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fixedm

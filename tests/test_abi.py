@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared function, and its
+host logic (constants, sizes, argument validation) answers before any launch."""
+import ctypes
+
+import pytest
+
+import oracle as O
+from dit_amd import fixedm as F
+
+
+@pytest.fixture(scope="module")
+def L():
+    return F.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = F.declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in F.STATUS.items():
+        assert L.fixedm_status_string(code).decode() == name
+    assert L.fixedm_status_string(17).decode() == "FIXEDM_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 255, 256, 257, 4096, 37800, 75600, 2**31, 2**40 + 1])
+def test_constants_match_oracle(n):
+    assert F.constants(n) == O.constants(n)
+
+
+def test_constants_rejects_nonpositive(L):
+    assert L.fixedm_constants(0, None, None, None, None) == -1
+    assert L.fixedm_constants(-5, None, None, None, None) == -1
+    assert L.fixedm_constants(1, None, None, None, None) == 0
+
+
+def _p(**kw):
+    base = dict(dtype="bf16", batch=1, heads=40, head_dim=128, sq=18900, sk_total=75600,
+                q_block=256, softmax_scale=0.0, center="compute")
+    base.update(kw)
+    return F.make_problem(**base)
+
+
+def test_sizes_of_valid_problems():
+    p = _p()
+    lay = F.bounds_layout(p)
+    offs = [lay.m, lay.elig, lay.u, lay.q2, lay.k2, lay.k_mean, lay.v_bad, lay.scratch, lay.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert F.bounds_bytes(p) == lay.total
+    nqt = -(-18900 // 256)
+    rows = 40 * nqt * 256
+    ws = F.workspace_bytes(p)
+    assert ws >= rows * (128 + 2) * 4 and ws % 256 == 0
+    assert F.bounds_bytes(_p(dtype="fp32", head_dim=64, center="none")) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -2),                      # fp16-like: no such dtype in the ABI
+    (dict(dtype=0), -2),
+    (dict(head_dim=64), -3),                  # bf16 path is head_dim 128
+    (dict(dtype="fp32", head_dim=96), -3),
+    (dict(q_block=100), -3),
+    (dict(q_block=32), -3),
+    (dict(q_block=0), -3),
+    (dict(batch=0), -1),
+    (dict(sq=-1), -1),
+    (dict(sk_total=0), -1),
+    (dict(center=5), -1),
+    (dict(softmax_scale=-0.1), -1),
+    (dict(softmax_scale=float("nan")), -1),
+    (dict(batch=2, heads=40000), -3),
+])
+def test_invalid_problems(kw, code):
+    p = _p(**kw)
+    assert F.bounds_bytes(p) == 0
+    assert F.workspace_bytes(p) == 0
+    with pytest.raises(F.FixedmError) as e:
+        F.bounds_layout(p)
+    assert e.value.status == code
+
+
+def test_bad_abi_version():
+    p = _p()
+    p.abi_version = 2
+    assert F.bounds_bytes(p) == 0
+
+
+def _call_bounds(L, p, q=None, kc=None, vc=None, lens=None, n=1, kmean=None, dev=0x10000,
+                 out=True):
+    T = F.Tensor
+    q = q if q is not None else T(0x20000, 0, 40 * 128, 128)
+    kc = kc if kc is not None else (T * 1)(T(0x40000, 0, 40 * 128, 128))
+    vc = vc if vc is not None else (T * 1)(T(0x80000, 0, 40 * 128, 128))
+    lens = lens if lens is not None else (ctypes.c_int64 * 1)(p.sk_total)
+    desc = F.BoundsDesc()
+    return L.fixedm_bounds(ctypes.byref(p), q, kc, vc, lens, n, kmean, dev,
+                           ctypes.byref(desc) if out else None, None)
+
+
+def test_bounds_argument_errors_before_launch(L):
+    p = _p(sk_total=1000, sq=100)
+    T = F.Tensor
+    assert _call_bounds(L, p, out=False) == -1                              # no descriptor
+    assert _call_bounds(L, p, dev=0) == -1                                  # no buffer
+    assert _call_bounds(L, p, dev=0x10010) == -1                            # buffer not 256-aligned
+    assert _call_bounds(L, p, q=T(0, 0, 5120, 128)) == -1                   # null q
+    assert _call_bounds(L, p, q=T(0x20008, 0, 5120, 128)) == -3             # q not 16-aligned
+    assert _call_bounds(L, p, q=T(0x20000, 0, 5121, 128)) == -3             # stride not 8-multiple
+    assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(999)) == -1         # sum != sk_total
+    assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(-1)) == -1
+    assert _call_bounds(L, p, n=0) == -1
+    assert _call_bounds(L, p, n=33) == -3                                   # too many chunks
+    ps = _p(sk_total=1000, sq=100, center="supplied")
+    assert _call_bounds(L, ps) == -1                                        # k_mean missing
+    assert _call_bounds(L, _p(dtype=3)) == -2
+
+
+def test_forged_descriptor_is_rejected(L):
+    d = F.BoundsDesc()
+    run = F.RunState()
+    assert L.fixedm_run_init(ctypes.byref(d), ctypes.byref(run)) == -4       # zeroed descriptor
+    d.p = _p()
+    d.dev = 0x10000
+    d.token = 12345
+    assert L.fixedm_run_init(ctypes.byref(d), ctypes.byref(run)) == -4       # token does not match
+    T = F.Tensor
+    kc = (T * 1)(T(0x40000, 0, 5120, 128))
+    lens = (ctypes.c_int64 * 1)(10)
+    assert L.fixedm_attn_fwd(ctypes.byref(d), ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc,
+                             lens, 1, 0x100000, None) == -4
+    assert L.fixedm_finalize(ctypes.byref(d), ctypes.byref(run), 0x100000, T(0x20000, 0, 5120, 128),
+                             1, None, None) == -4
+    assert L.fixedm_attn_fwd(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
+                             0x100000, None) == -1

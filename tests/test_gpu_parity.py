@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on seeded inputs.
+
+Bounds (k_mean, Q2, K2, U, m, eligibility) are compared bit for bit on every config; the
+output within the acceptance tolerances (_parity.TOL).  Configs 1, 2 and 5 are compared in
+full; configs 3 and 4 (the Wan 720p rank share and the ragged one) on sampled rows of every
+head, including the ragged last q-block, at the full sizes and in the launch configuration
+the benchmark times (bounds + one fixedm_attn_fwd per ring chunk + finalize)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from dit_amd import workloads as WL
+
+from _parity import (LSE_TOL, bf16_rne_bits, check_bounds, check_output, device_inputs,
+                     gpu_bounds_dict, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dit_amd import fixedm
+    fixedm.lib()   # raises if the library is missing: no fallback exists
+    return fixedm
+
+
+def _run(F, inp, *, q_block=None, order=None, out_dtype=None, want_lse=True):
+    import torch
+    wl = inp.wl
+    q, ks, vs, km = device_inputs(inp)
+    if order is not None:
+        ks, vs = [ks[i] for i in order], [vs[i] for i in order]
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=q_block or wl.q_block, center=wl.center,
+                                    k_mean=km, out_dtype=out_dtype or torch.float32,
+                                    want_lse=want_lse)
+    torch.cuda.synchronize()
+    return out, lse, desc, buf, (q, ks, vs, km)
+
+
+def _oracle_bounds(inp, q_block=None):
+    wl = inp.wl
+    return O.bounds(inp.q, inp.k, inp.v, scale=wl.scale, q_block=q_block or wl.q_block,
+                    center=wl.center, k_mean=inp.k_mean, dtype=wl.dtype)
+
+
+# ------------------------------------------------------------------ full configs ------
+@pytest.mark.parametrize("q_block", [64, 256])
+def test_config1_tiny_fp32(F, q_block):
+    say(f"config 1 q_block={q_block}")
+    inp = WL.make_inputs(1)
+    out, lse, desc, buf, _ = _run(F, inp, q_block=q_block)
+    ob = _oracle_bounds(inp, q_block)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(out.cpu().numpy(), ref, "fp32")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["fp32"]
+
+
+def test_config2_wan_block_bf16(F):
+    import torch
+    say("config 2")
+    inp = WL.make_inputs(2)
+    out, lse, desc, buf, dev = _run(F, inp)
+    ob = _oracle_bounds(inp)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    assert ob.elig.all()
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    got = out.cpu().numpy()
+    check_output(got, ref, "bf16")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
+    # bf16 output is the round-to-nearest-even of the fp32 output, bit for bit
+    out16, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, center="none",
+                               out_dtype=torch.bfloat16)
+    bits = out16.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, bf16_rne_bits(got))
+
+
+def _sample_rows(sq, q_block):
+    last_lo = ((sq - 1) // q_block) * q_block
+    rows = list(range(0, 64)) + list(range(max(sq - 64, last_lo), sq))
+    return np.array(sorted(set(rows)))
+
+
+@pytest.fixture(scope="module")
+def cfg3(F):
+    say("config 3: drawing inputs")
+    return WL.make_inputs(3)
+
+
+def test_config3_bounds_bitexact(F, cfg3):
+    say("config 3 bounds")
+    inp = cfg3
+    import torch
+    q, ks, vs, km = device_inputs(inp)
+    p = F.make_problem("bf16", 1, 40, 128, inp.wl.sq, inp.wl.sk, 256, 0.0, "compute")
+    desc, buf = F.bounds(p, q, ks, vs)
+    torch.cuda.synchronize()
+    ob = _oracle_bounds(inp)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    assert ob.elig.all() and (ob.C, ob.gate) == (102, 113)
+    say(f"  U range {ob.u.min():.3f}..{ob.u.max():.3f}, m range {ob.m.min()}..{ob.m.max()}")
+
+
+def test_config3_output_sampled_rows(F, cfg3):
+    say("config 3 output (ring order 0,3,2,1)")
+    inp = cfg3
+    out, lse, desc, buf, _ = _run(F, inp, order=(0, 3, 2, 1))
+    rows = _sample_rows(inp.wl.sq, 256)
+    ref, lse_ref = O.attention_rows(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1),
+                                    inp.wl.scale, rows)
+    check_output(out.cpu().numpy()[:, rows], ref, "bf16")
+    assert np.abs(lse.cpu().numpy()[:, :, rows] - lse_ref).max() <= LSE_TOL["bf16"]
+    assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_config4_ragged_offset(F):
+    say("config 4")
+    inp = WL.make_inputs(4)
+    out, lse, desc, buf, _ = _run(F, inp)
+    ob = _oracle_bounds(inp)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    assert ob.elig.all()
+    rows = _sample_rows(inp.wl.sq, 256)
+    ref, lse_ref = O.attention_rows(inp.q, inp.k[0], inp.v[0], inp.wl.scale, rows)
+    check_output(out.cpu().numpy()[:, rows], ref, "bf16")
+    assert np.abs(lse.cpu().numpy()[:, :, rows] - lse_ref).max() <= LSE_TOL["bf16"]
+
+
+def test_config5_adversarial_fp32(F):
+    say("config 5")
+    inp = WL.make_inputs(5)
+    out, lse, desc, buf, _ = _run(F, inp)
+    ob = _oracle_bounds(inp)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    assert ob.elig[0, :4].all() and not ob.elig[0, 4:].any()
+    assert (ob.m[0, 4:] == 125).all()
+    kall = np.concatenate(inp.k, 1)
+    ref, lse_ref = O.attention(inp.q, kall, np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(out.cpu().numpy(), ref, "fp32")
+    lse_g = lse.cpu().numpy()
+    for h in range(8):
+        mass = O.softmax_mass(inp.q[0, :, h], kall[0, :, h], inp.wl.scale, lse_g[0, h])
+        assert np.abs(mass - 1.0).max() <= 1e-5, (h, np.abs(mass - 1.0).max())
+
+
+# ------------------------------------------------------------------ edge cases --------
+def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_scale=1.0,
+             k_offset=0.0, v_poke=None, loud_rows=None):
+    import torch
+    inp = WL.generic_inputs(seed, dtype, B, H, D, Sq, chunks, q_block=q_block, center=center,
+                            q_scale=q_scale, k_offset=k_offset)
+    if loud_rows is not None:                      # (head, lo, hi, factor): a loud q-block
+        h, lo, hi, fac = loud_rows
+        qf = inp.q.copy()
+        qf[:, lo:hi, h] *= np.float32(fac)
+        inp.q_store = WL.bf16_bits_from_f32(qf) if dtype == "bf16" else qf
+    if v_poke is not None:
+        c, idx, val = v_poke
+        if dtype == "bf16":
+            inp.v_store[c][idx] = WL.bf16_bits_from_f32(np.array([val], np.float32))[0]
+        else:
+            inp.v_store[c][idx] = val
+    kmean = inp.k_mean if center == "supplied" else None
+    if center != "supplied":
+        inp.k_mean = None
+    q, ks, vs, km = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=q_block, center=center, k_mean=km,
+                                    out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=q_block, center=center,
+                  k_mean=kmean, dtype=dtype)
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(out.cpu().numpy(), ref, dtype)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL[dtype]
+    return ob, out
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("fp32", 128)])
+def test_single_query_single_key(F, dtype, D):
+    say(f"edge: 1x1 {dtype} D={D}")
+    _generic(F, 31, dtype, 1, 2, D, 1, (1,))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_ragged_everything(F, dtype, D):
+    say(f"edge: ragged {dtype}")
+    _generic(F, 32, dtype, 2, 3, D, 300, (1, 63, 64, 65, 130), q_block=64, center="compute",
+             k_offset=2.0)
+
+
+def test_supplied_centre_bf16(F):
+    say("edge: supplied k_mean")
+    _generic(F, 33, "bf16", 1, 4, 128, 513, (700, 300), q_block=128, center="supplied", k_offset=3.0)
+
+
+def test_mixed_bodies_in_one_workgroup(F):
+    """q_block 64 with a loud query block: four waves of one workgroup take different bodies."""
+    say("edge: mixed bodies")
+    ob, _ = _generic(F, 34, "bf16", 1, 2, 128, 256, (400, 300), q_block=64,
+                     loud_rows=(0, 64, 128, 14.0))
+    assert ob.elig.any() and not ob.elig.all()
+
+
+def test_v_magnitude_forces_fallback(F):
+    say("edge: |v| > 256")
+    ob, _ = _generic(F, 35, "bf16", 1, 2, 128, 200, (150, 100), q_block=64,
+                     v_poke=(1, (0, 7, 1, 3), 300.0))
+    assert not ob.v_ok and not ob.elig.any()
+
+
+def test_every_element_written_and_deterministic(F):
+    import torch
+    say("edge: NaN sentinel + determinism")
+    inp = WL.generic_inputs(36, "bf16", 1, 5, 128, 700, (333, 444), q_block=64)
+    q, ks, vs, _ = device_inputs(inp)
+    N = 777
+    p = F.make_problem("bf16", 1, 5, 128, 700, N, 64)
+    outs = []
+    for _ in range(2):
+        desc, buf = F.bounds(p, q, ks, vs)
+        ws = F.alloc_workspace(p, q.device)
+        run = F.run_init(desc)
+        for k, v in zip(ks, vs):
+            F.attn_fwd(desc, run, q, [k], [v], ws)
+        out = torch.full((1, 700, 5, 128), float("nan"), device="cuda")
+        F.finalize(desc, run, ws, out)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_strided_layout_and_chunk_order(F):
+    """[B, H, S, D]-strided views give the same result; chunk order changes only rounding."""
+    import torch
+    say("edge: strides + order")
+    inp = WL.generic_inputs(37, "bf16", 1, 3, 128, 260, (100, 90, 70), q_block=64)
+    q, ks, vs, _ = device_inputs(inp)
+    base, _, _, _ = F.forward(q, ks, vs, q_block=64, out_dtype=torch.float32)
+    qt = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)     # stride_s = D, stride_h = S*D
+    kt = [k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for k in ks]
+    vt = [v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for v in vs]
+    o2, _, _, _ = F.forward(qt, kt, vt, q_block=64, out_dtype=torch.float32)
+    assert torch.equal(base, o2)
+    o3, _, _, _ = F.forward(q, ks[::-1], vs[::-1], q_block=64, out_dtype=torch.float32)
+    assert (base - o3).abs().max().item() < 1e-5
+
+
+def test_state_contracts(F):
+    import torch
+    say("edge: state contracts")
+    inp = WL.generic_inputs(38, "bf16", 1, 2, 128, 64, (64, 64), q_block=64)
+    q, ks, vs, _ = device_inputs(inp)
+    p = F.make_problem("bf16", 1, 2, 128, 64, 128, 64)
+    desc, buf = F.bounds(p, q, ks, vs)
+    ws = F.alloc_workspace(p, q.device)
+    run = F.run_init(desc)
+    F.attn_fwd(desc, run, q, ks[:1], vs[:1], ws)
+    out = torch.empty((1, 64, 2, 128), device="cuda")
+    with pytest.raises(F.FixedmError) as e:
+        F.finalize(desc, run, ws, out)                 # only half the keys visited
+    assert e.value.status == -5
+    F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)
+    with pytest.raises(F.FixedmError) as e:
+        F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)   # more keys than sk_total
+    assert e.value.status == -5
+    F.finalize(desc, run, ws, out)
+    out16 = torch.empty((1, 64, 2, 128), device="cuda", dtype=torch.bfloat16)
+    F.finalize(desc, run, ws, out16)                   # finalize again, other dtype
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out.to(torch.bfloat16))
+    other, _ = F.bounds(p, q, ks, vs)
+    with pytest.raises(F.FixedmError) as e:
+        F.attn_fwd(other, run, q, ks[:1], vs[:1], ws)  # run state of another descriptor
+    assert e.value.status == -4
+    desc.gate += 1                                     # a modified descriptor
+    with pytest.raises(F.FixedmError) as e:
+        F.run_init(desc)
+    assert e.value.status == -4
