@@ -174,7 +174,18 @@ def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_s
                   k_mean=kmean, dtype=dtype)
     check_bounds(gpu_bounds_dict(desc, buf), ob)
     ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
-    check_output(out.cpu().numpy(), ref, dtype)
+    got = out.cpu().numpy()
+    if v_poke is None:
+        check_output(got, ref, dtype)
+    else:
+        # bf16 probability rounding scales the error with |v|: the poked (head, dim) column
+        # holds one value of magnitude |val|, so its tolerance scales by |val| / 4
+        c, (b0, j0, h0, d0), val = v_poke
+        keep = np.ones(got.shape, bool)
+        keep[:, :, h0, d0] = False
+        check_output(got[keep], ref[keep], dtype, "O (other columns)")
+        col = np.abs(got[:, :, h0, d0] - ref[:, :, h0, d0]).max()
+        assert col <= 1e-2 * abs(val) / 4.0, col
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL[dtype]
     return ob, out
 
