@@ -22,8 +22,14 @@
 //     already the B operand of O^T += V^T P^T with no transpose (the K-stationary layout of
 //     [CM]).  The matching key order on the V^T operand comes from the gfx950 LDS transpose
 //     read ds_read_b64_tr_b16.
-//   * K/V blocks of 64 keys are staged in LDS (16 KB each, double-buffered), XOR-swizzled so
-//     both the K row reads and the V transpose reads are bank-conflict free.
+//   * K/V tiles of 32 keys stream through an 8-stage LDS ring (K ring in the first 64 KB,
+//     V ring in the next 64 KB) with direct global->LDS loads (global_load_lds_dwordx4)
+//     issued six tiles ahead; no VGPR staging.  Tiles are XOR-swizzled so both the K row
+//     reads and the V transpose reads are bank-conflict free.  The main loop is unrolled
+//     over the 8 stages, so every LDS address is a per-lane base plus an immediate.
+//   * Fixed-m body, software-pipelined per 32-key tile t: the MFMAs of O += V(t-1) P(t-1)
+//     are independent of the VALU work exp2(alpha S(t) - shift), so the matrix cores and
+//     the vector ALUs overlap within one wave.
 //   * The body (fixed-m or online softmax) is chosen per wave from the eligibility byte of
 //     its q-block: a wave-uniform branch, no divergence on the eligible path.
 //   * One launch folds one K/V chunk (one ring step) into the workspace.
@@ -41,43 +47,36 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kD = 128;
-constexpr int kKB = 64;                  // keys per LDS block
-constexpr int kRowBytes = kD * 2;        // 256 bytes per key row
-constexpr int kTileBytes = kKB * kRowBytes;  // 16 KB
+constexpr int kKT = 32;                        // keys per pipeline tile
+constexpr int kRowBytes = kD * 2;              // 256 bytes per key row
+constexpr int kTileBytes = kKT * kRowBytes;    // 8 KB: K (or V) of one tile
+constexpr int kStages = 8;                     // LDS ring depth in tiles
+constexpr int kAhead = kStages - 2;            // tiles in flight ahead of the current one
+constexpr int kLoadsPerTile = 4;               // global->LDS instructions per wave per tile
+constexpr int kVRing = kStages * kTileBytes;   // the V ring starts after the K ring
+constexpr int kLdsBytes = 2 * kStages * kTileBytes;   // 128 KB
 
-// LDS placement of 16-byte chunk `c` of key row `r`.
-__device__ inline int k_lds_off(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
-__device__ inline int v_lds_off(int r, int c) { return r * kRowBytes + ((c ^ ((r & 3) << 2)) << 4); }
-
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  // round-to-nearest-even of two fp32 (finite or +-inf; NaN cannot occur here)
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
-  b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
-  return a | b;
+// s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Packs 8 probabilities to bf16 (the MFMA's B operand) and adds the same rounded values to
-// the row sum, so numerator and denominator see identical weights.
-__device__ inline bf16x8 pack8_sum(const f32x16& p, int base, float& lsum) {
-  uint32_t w[4];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[i] = pack_bf16x2(p[base + 2 * i], p[base + 2 * i + 1]);
-    bf16x2 pair;
-    __builtin_memcpy(&pair, &w[i], 4);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
-  }
-  bf16x8 r;
-  __builtin_memcpy(&r, w, 16);
-  return r;
+// Workgroup barrier without the memory fence __syncthreads() adds: the ring's prefetch
+// loads must stay in flight across it.  LDS visibility is ensured by the explicit vmcnt
+// wait that precedes every barrier.
+__device__ inline void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ inline int remap_tile(int bid, int nb) {
@@ -88,149 +87,303 @@ __device__ inline int remap_tile(int bid, int nb) {
   return bid;
 }
 
-template <bool kFixed>
-__device__ __attribute__((always_inline)) void process_block(const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vs,
-                                     const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4], float (&lsum)[2],
-                                     float (&shift)[2], float alpha, int valid, int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
-  // ---- S^T = K Q^T: two 32-key tiles x two 32-query tiles
-  f32x16 s[2][2];
+// One 16-byte-per-lane global->LDS load; lane L's 16 bytes land at LDS byte lds + 16 L.
+// Written as inline asm so the compiler's wait-count pass does not treat every later LDS
+// read as aliasing an in-flight DMA (it would insert vmcnt(0) and drain the ring); the
+// ring's vmcnt waits are explicit instead.  M0 carries the wave-uniform LDS address; no
+// compiler-generated instruction in this kernel reads M0.
+__device__ inline void dma16_saddr(uint32_t voff, uint64_t sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ inline void dma16_vaddr(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+}
+
+__device__ inline uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Per-workgroup context of one chunk: source rows, DMA lane offsets, LDS read bases.
+struct Ring {
+  uint64_t kbase, vbase;        // byte address of key row 0 of this (b, h) in K and V
+  uint64_t ktile, vtile;        // bytes between consecutive 32-key tiles
+  int64_t len;                  // real keys in the chunk
+  int64_t k_ss, v_ss;           // row strides (elements)
+  uint32_t kdma[2], vdma[2];    // lane byte offsets of this wave's two rows in a tile
+  int row[2];                   // those rows (0..31)
+  int ck[2], cv[2];             // logical 16-byte chunk each lane fetches
+  int wave;
+  uint32_t koff[8];             // K fragment LDS offsets (stage 0) for k-steps 0..7
+  uint32_t voff[4];             // V^T fragment LDS offsets (stage 0) for dim tiles 0..3
+};
+
+// Issues this wave's share (4 rows of K and 4 of V, 1 KB each) of tile t into LDS stage
+// `stage`.  Lane L of instruction i lands at row 4 (2 w + i) + L / 16, physical chunk
+// L % 16, and fetches the logical chunk the swizzle puts there.  Tiles that reach past the
+// chunk's end re-read its last row for the missing keys (masked later).
+// kFull: the caller guarantees the tile lies wholly inside the chunk.
+template <bool kFull = false>
+__device__ __attribute__((always_inline)) void issue_tile(const Ring& g, int t, int stage) {
+  const uint32_t kl = (uint32_t)(stage * kTileBytes), vl = (uint32_t)(kVRing + stage * kTileBytes);
+  if (kFull || (int64_t)(t + 1) * kKT <= g.len) {
+    const uint64_t kt = uniform_u64(g.kbase + (uint64_t)t * g.ktile);
+    const uint64_t vt = uniform_u64(g.vbase + (uint64_t)t * g.vtile);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
+      dma16_saddr(g.kdma[i], kt, kl + blk);
+      dma16_saddr(g.vdma[i], vt, vl + blk);
+    }
+  } else {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) s[a][n] = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int row = 32 * a + lq;
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + k_lds_off(row, 2 * kk + hh));
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        s[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[n][kk], s[a][n], 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
+      int64_t key = (int64_t)t * kKT + g.row[i];
+      if (key >= g.len) key = g.len - 1;
+      dma16_vaddr((const void*)(g.kbase + (uint64_t)(key * g.k_ss * 2) + 16 * g.ck[i]), kl + blk);
+      dma16_vaddr((const void*)(g.vbase + (uint64_t)(key * g.v_ss * 2) + 16 * g.cv[i]), vl + blk);
     }
   }
-  // ---- probabilities
-  const bool partial = valid < kKB;
-  bf16x8 p[2][4];
+}
+
+// S^T(tile) = K(tile) Q^T for one 32-key tile and two 32-query tiles: 16 MFMAs.
+__device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const Ring& g, int stage,
+                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2]) {
+  const uint8_t* ks = smem + stage * kTileBytes;
+  bf16x8 kf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], f32x16{}, 0, 0, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+  for (int kk = 1; kk < 8; ++kk) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], s[1], 0, 0, 0);
+  }
+}
+
+// O^T += V(tile)^T P(tile)^T: four 32-dim tiles x two 16-key steps x two query tiles.
+// The V^T operand (lane: one dim, 8 keys in the P register order) comes from two LDS
+// transpose reads, each giving 4 keys x 16 dims to a 16-lane group.
+__device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, const Ring& g, int stage,
+                                                          const bf16x8 (&p)[2][2], f32x16 (&o)[2][4]) {
+  const uint8_t* vs = smem + stage * kTileBytes;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* a0 = vs + g.voff[m] + 4096 * st;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 2048));
+      const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[0][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[0][st], o[0][m], 0, 0, 0);
+      o[1][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[1][st], o[1][m], 0, 0, 0);
+    }
+  }
+}
+
+// Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
+// and adds the same rounded values to the row sum, so numerator and denominator see
+// identical weights.
+__device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int base, float& lsum) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x2 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[i] = __builtin_convertvector((f32x2){e[base + 2 * i], e[base + 2 * i + 1]}, bf16x2);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(w[i], ones, lsum, false);
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, w, 16);
+  return r;
+}
+
+// Key index within the tile held by accumulator register r of this lane.
+__device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// Fixed-m probabilities of one tile: p = 2^(alpha S - (m + c_i)), no max, no rescale.
+template <bool kPartial>
+__device__ __attribute__((always_inline)) void softmax_fixed(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
+                                                             float (&lsum)[2], const float (&nshift)[2],
+                                                             float alpha, int valid, int hh) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    if (!kFixed) {
-      float mx = -INFINITY;
+    f32x16 e;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * a + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const float v = (partial && key >= valid) ? -INFINITY : s[a][n][r];
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float rn = fmaxf(shift[n], alpha * mx);
-      const float f = __builtin_amdgcn_exp2f(shift[n] - rn);
-      shift[n] = rn;
-      lsum[n] *= f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[n][m][r] *= f;
+    for (int r = 0; r < 16; ++r) {
+      float x = __builtin_fmaf(alpha, s[n][r], nshift[n]);
+      if (kPartial && tile_key(r, hh) >= valid) x = -INFINITY;
+      e[r] = __builtin_amdgcn_exp2f(x);
     }
-    const float nshift = -shift[n];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      f32x16 e;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = __builtin_fmaf(alpha, s[a][n][r], nshift);
-        if (partial) {
-          const int key = 32 * a + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= valid) x = -INFINITY;
-        }
-        e[r] = __builtin_amdgcn_exp2f(x);
-      }
-      p[n][2 * a] = pack8_sum(e, 0, lsum[n]);
-      p[n][2 * a + 1] = pack8_sum(e, 8, lsum[n]);
-    }
+    p[n][0] = pack8_sum(e, 0, lsum[n]);
+    p[n][1] = pack8_sum(e, 8, lsum[n]);
   }
-  // ---- O^T += V^T P^T: four 32-dim tiles, four 16-key steps
-  const int g = lane >> 4, j = lane & 15;
-  const int dhalf = g & 1;
+}
+
+// Online-softmax probabilities of one tile (the fallback body): raise the running max,
+// rescale the accumulator and the row sum, then exponentiate against the new max.
+__device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
+                                                              float (&lsum)[2], float (&rmax)[2],
+                                                              f32x16 (&o)[2][4], float alpha, int valid,
+                                                              int hh) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
+  for (int n = 0; n < 2; ++n) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tile_key(r, hh) < valid ? s[n][r] : -INFINITY);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float rn = fmaxf(rmax[n], alpha * mx);
+    const float f = __builtin_amdgcn_exp2f(rmax[n] - rn);
+    rmax[n] = rn;
+    lsum[n] *= f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o[n][m] *= f;
+    f32x16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = tile_key(r, hh) < valid ? __builtin_fmaf(alpha, s[n][r], -rn) : -INFINITY;
+      e[r] = __builtin_amdgcn_exp2f(x);
+    }
+    p[n][0] = pack8_sum(e, 0, lsum[n]);
+    p[n][1] = pack8_sum(e, 8, lsum[n]);
+  }
+}
+
+// Ring bookkeeping at the top of every tile step, identical in both bodies so the waves of
+// one workgroup meet at the same barriers: wait for this wave's part of tile t+1, meet the
+// other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
+// loading tile t+kAhead into stage t-2.
+template <bool kFull = false>
+__device__ __attribute__((always_inline)) void ring_step(const Ring& g, int t, int stage) {
+  wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
+  barrier();
+  issue_tile<kFull>(g, t + kAhead, (stage + kAhead) % kStages);
+}
+
+// Fixed-m step for a full middle tile t (1 <= t <= n_tiles - 2) whose ring stage is
+// `stage`.  Phase 1: the 16 MFMAs of O += V(t-1) P(t-1) run while the VALUs turn S(t)
+// into P(t); phase 2: the 16 MFMAs of S(t+1) = K(t+1) Q^T overwrite S.
+template <bool kFull = false>
+__device__ __attribute__((always_inline)) void fixed_mid(const uint8_t* smem, const Ring& g, int t, int stage,
+                                                         const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
+                                                         float (&lsum)[2], const float (&nshift)[2], float alpha,
+                                                         int hh, f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
+                                                         bf16x8 (&p_cur)[2][2]) {
+  ring_step<kFull>(g, t, stage);
+  compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
+  softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
+  compute_s(smem, g, (stage + 1) % kStages, qf, s);
+}
+
+// Last tile t = n_tiles - 1 >= 1 (possibly partial): O += V(t-1) P(t-1); P(t); O += V(t) P(t).
+__device__ __attribute__((always_inline)) void fixed_last(const uint8_t* smem, const Ring& g, int t, int stage,
+                                                          f32x16 (&o)[2][4], float (&lsum)[2],
+                                                          const float (&nshift)[2], float alpha, int hh,
+                                                          const f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
+                                                          bf16x8 (&p_cur)[2][2]) {
+  ring_step(g, t, stage);
+  compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
+  const int valid = (int)(g.len - (int64_t)t * kKT);
+  if (valid >= kKT) softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
+  else softmax_fixed<true>(s, p_cur, lsum, nshift, alpha, valid, hh);
+  compute_pv(smem, g, stage, p_cur, o);
+}
+
+template <bool kFixed>
+__device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, const uint8_t* smem,
+                                                         const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
+                                                         float (&lsum)[2], float (&shift)[2], int b, int h) {
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const ChunkDesc& cd = a.ch[0];
+  Ring g;
+  g.wave = tid >> 6;
+  g.len = cd.len;
+  g.k_ss = cd.k_ss;
+  g.v_ss = cd.v_ss;
+  g.kbase = (uint64_t)(reinterpret_cast<const uint16_t*>(cd.k) + b * cd.k_sb + h * cd.k_sh);
+  g.vbase = (uint64_t)(reinterpret_cast<const uint16_t*>(cd.v) + b * cd.v_sb + h * cd.v_sh);
+  g.ktile = (uint64_t)(kKT * cd.k_ss * 2);
+  g.vtile = (uint64_t)(kKT * cd.v_ss * 2);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (2 * g.wave + i) + (lane >> 4);
+    const int phys = lane & 15;
+    g.row[i] = row;
+    g.ck[i] = phys ^ (row & 15);
+    g.cv[i] = phys ^ ((row & 3) << 2);
+    g.kdma[i] = (uint32_t)(row * cd.k_ss * 2 + 16 * g.ck[i]);
+    g.vdma[i] = (uint32_t)(row * cd.v_ss * 2 + 16 * g.cv[i]);
+  }
+  {
+    const int lq = lane & 31, grp = lane >> 4, j = lane & 15, dhalf = grp & 1;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) g.koff[kk] = (uint32_t)(lq * kRowBytes + (((2 * kk + hh) ^ (lq & 15)) << 4));
+    const int r0 = 4 * hh + (j >> 2);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int chunk = 4 * m + 2 * dhalf + ((j & 3) >> 1);
-      const int byte = (j & 1) * 8;
-      const int r0 = 16 * st + 4 * hh + (j >> 2);
-      const int r1 = r0 + 8;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(vs + v_lds_off(r0, chunk) + byte));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(vs + v_lds_off(r1, chunk) + byte));
-      const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        o[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[n][st], o[n][m], 0, 0, 0);
+      g.voff[m] = (uint32_t)(kVRing + r0 * kRowBytes + ((chunk ^ ((r0 & 3) << 2)) << 4) + (j & 1) * 8);
     }
   }
-}
-
-__device__ __attribute__((always_inline)) void stage_load(uint4 (&sk)[4], uint4 (&sv)[4], const ChunkDesc& cd,
-                                                       int b, int h, int64_t key0, int tid) {
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(cd.k) + b * cd.k_sb + h * cd.k_sh;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(cd.v) + b * cd.v_sb + h * cd.v_sh;
+  const int n_tiles = (int)((cd.len + kKT - 1) / kKT);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int row = idx >> 4, c = idx & 15;
-    int64_t key = key0 + row;
-    if (key >= cd.len) key = cd.len - 1;
-    sk[i] = *reinterpret_cast<const uint4*>(kb + key * cd.k_ss + 8 * c);
-    sv[i] = *reinterpret_cast<const uint4*>(vb + key * cd.v_ss + 8 * c);
-  }
-}
-
-__device__ __attribute__((always_inline)) void stage_store(const uint4 (&sk)[4], const uint4 (&sv)[4], uint8_t* ks,
-                                                        uint8_t* vs, int tid) {
+  for (int t = 0; t < kAhead; ++t) issue_tile(g, t, t);
+  wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
+  barrier();
+  if (kFixed) {
+    const float nshift[2] = {-shift[0], -shift[1]};
+    const float alpha = a.alpha;
+    f32x16 s[2];
+    bf16x8 pA[2][2], pB[2][2];   // P(t) lives in pA for even t, pB for odd t
+    compute_s(smem, g, 0, qf, s);
+    ring_step(g, 0, 0);
+    if (n_tiles == 1) {
+      const int valid = (int)cd.len;
+      if (valid >= kKT) softmax_fixed<false>(s, pA, lsum, nshift, alpha, kKT, hh);
+      else softmax_fixed<true>(s, pA, lsum, nshift, alpha, valid, hh);
+      compute_pv(smem, g, 0, pA, o);
+    } else {
+      softmax_fixed<false>(s, pA, lsum, nshift, alpha, kKT, hh);
+      compute_s(smem, g, 1, qf, s);
+      // middle tiles 1 .. n_tiles-2: groups of kStages with static ring stages while
+      // every tile the group prefetches is a full one, then one step at a time
+      const int n_full = (int)(cd.len / kKT);
+      int t = 1;
+      for (; t + kStages + kAhead <= n_full; t += kStages) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int row = idx >> 4, c = idx & 15;
-    *reinterpret_cast<uint4*>(ks + k_lds_off(row, c)) = sk[i];
-    *reinterpret_cast<uint4*>(vs + v_lds_off(row, c)) = sv[i];
+        for (int jj = 0; jj < kStages; ++jj) {
+          const int stage = (1 + jj) % kStages;
+          if (jj & 1) fixed_mid<true>(smem, g, t + jj, stage, qf, o, lsum, nshift, alpha, hh, s, pB, pA);
+          else fixed_mid<true>(smem, g, t + jj, stage, qf, o, lsum, nshift, alpha, hh, s, pA, pB);
+        }
+      }
+      for (; t < n_tiles - 1; ++t) {
+        if (t & 1) fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, alpha, hh, s, pA, pB);
+        else fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, alpha, hh, s, pB, pA);
+      }
+      if (t & 1) fixed_last(smem, g, t, t % kStages, o, lsum, nshift, alpha, hh, s, pA, pB);
+      else fixed_last(smem, g, t, t % kStages, o, lsum, nshift, alpha, hh, s, pB, pA);
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) {
+      const int stage = t % kStages;
+      ring_step(g, t, stage);
+      f32x16 s[2];
+      bf16x8 p[2][2];
+      compute_s(smem, g, stage, qf, s);
+      const int64_t rem = cd.len - (int64_t)t * kKT;
+      softmax_online(s, p, lsum, shift, o, a.alpha, rem < kKT ? (int)rem : kKT, hh);
+      compute_pv(smem, g, stage, p, o);
+    }
   }
-}
-
-template <bool kFixed>
-__device__ __attribute__((always_inline)) void run_chunks(const AttnArgs& a, uint8_t* smem, const bf16x8 (&qf)[2][8],
-                           f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2], int b, int h) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  int buf = 0;
-  uint4 sk[4], sv[4];
-  const ChunkDesc& cd = a.ch[0];
-  int64_t key0 = 0;
-  stage_load(sk, sv, cd, b, h, key0, tid);
-  stage_store(sk, sv, smem, smem + kTileBytes, tid);
-  __syncthreads();
-  while (true) {
-    const int64_t kn = key0 + kKB;
-    const bool more = kn < cd.len;
-    if (more) stage_load(sk, sv, cd, b, h, kn, tid);
-    const int64_t rem = cd.len - key0;
-    const int valid = rem < kKB ? (int)rem : kKB;
-    uint8_t* cur = smem + buf * 2 * kTileBytes;
-    process_block<kFixed>(cur, cur + kTileBytes, qf, o, lsum, shift, a.alpha, valid, lane);
-    if (!more) break;
-    uint8_t* nxt = smem + (buf ^ 1) * 2 * kTileBytes;
-    stage_store(sk, sv, nxt, nxt + kTileBytes, tid);
-    __syncthreads();
-    buf ^= 1;
-    key0 = kn;
-  }
+  wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is released
+  barrier();
 }
 
 __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   const int tile = remap_tile(blockIdx.x, gridDim.x);
   const int qt = tile % a.n_qtiles;
   const int bh = tile / a.n_qtiles;
@@ -244,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   const bool fixed = a.elig[bq] != 0;
   const int mshift = a.m[bq];
 
-  // resident query fragments (B operand of S^T = K Q^T)
+  // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean
   bf16x8 qf[2][8];
   float cdot[2];
   const float* km = a.k_mean + (int64_t)bh * kD;
@@ -280,10 +433,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   if (fixed) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + a.alpha * cdot[n];
-    run_chunks<true>(a, smem, qf, o, lsum, shift, b, h);
+    run_chunk<true>(a, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;
-    run_chunks<false>(a, smem, qf, o, lsum, shift, b, h);
+    run_chunk<false>(a, smem, qf, o, lsum, shift, b, h);
   }
 
   // ---- fold into the workspace: acc in register order (one 1 KB coalesced float4 store
