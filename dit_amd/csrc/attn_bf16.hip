@@ -90,12 +90,14 @@ __device__ inline int remap_tile(int bid, int nb) {
 // One 16-byte-per-lane global->LDS load; lane L's 16 bytes land at LDS byte lds + 16 L.
 // Written as inline asm so the compiler's wait-count pass does not treat every later LDS
 // read as aliasing an in-flight DMA (it would insert vmcnt(0) and drain the ring); the
-// ring's vmcnt waits are explicit instead.  M0 carries the wave-uniform LDS address; no
-// compiler-generated instruction in this kernel reads M0.
-__device__ inline void dma16_saddr(uint32_t voff, uint64_t sbase, uint32_t lds) {
+// ring's vmcnt waits are explicit instead.  The destination is passed as an LDS pointer
+// (with a memory clobber) so the compiler knows the asm writes the shared buffer.  M0
+// carries the wave-uniform LDS address; no compiler-generated instruction here reads M0.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ inline void dma16_saddr(uint32_t voff, uint64_t sbase, lds_u8* lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
-__device__ inline void dma16_vaddr(const void* g, uint32_t lds) {
+__device__ inline void dma16_vaddr(const void* g, lds_u8* lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
 }
 
@@ -125,21 +127,22 @@ struct Ring {
 // chunk's end re-read its last row for the missing keys (masked later).
 // kFull: the caller guarantees the tile lies wholly inside the chunk.
 template <bool kFull = false>
-__device__ __attribute__((always_inline)) void issue_tile(const Ring& g, int t, int stage) {
-  const uint32_t kl = (uint32_t)(stage * kTileBytes), vl = (uint32_t)(kVRing + stage * kTileBytes);
+__device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const Ring& g, int t, int stage) {
+  lds_u8* kl = (lds_u8*)(smem + stage * kTileBytes);
+  lds_u8* vl = (lds_u8*)(smem + kVRing + stage * kTileBytes);
   if (kFull || (int64_t)(t + 1) * kKT <= g.len) {
     const uint64_t kt = uniform_u64(g.kbase + (uint64_t)t * g.ktile);
     const uint64_t vt = uniform_u64(g.vbase + (uint64_t)t * g.vtile);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
+      const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
       dma16_saddr(g.kdma[i], kt, kl + blk);
       dma16_saddr(g.vdma[i], vt, vl + blk);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
+      const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
       int64_t key = (int64_t)t * kKT + g.row[i];
       if (key >= g.len) key = g.len - 1;
       dma16_vaddr((const void*)(g.kbase + (uint64_t)(key * g.k_ss * 2) + 16 * g.ck[i]), kl + blk);
@@ -256,10 +259,10 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
 // other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
 // loading tile t+kAhead into stage t-2.
 template <bool kFull = false>
-__device__ __attribute__((always_inline)) void ring_step(const Ring& g, int t, int stage) {
+__device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ring& g, int t, int stage) {
   wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
   barrier();
-  issue_tile<kFull>(g, t + kAhead, (stage + kAhead) % kStages);
+  issue_tile<kFull>(smem, g, t + kAhead, (stage + kAhead) % kStages);
 }
 
 // Fixed-m step for a full middle tile t (1 <= t <= n_tiles - 2) whose ring stage is
@@ -271,7 +274,7 @@ __device__ __attribute__((always_inline)) void fixed_mid(const uint8_t* smem, co
                                                          float (&lsum)[2], const float (&nshift)[2], float alpha,
                                                          int hh, f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
                                                          bf16x8 (&p_cur)[2][2]) {
-  ring_step<kFull>(g, t, stage);
+  ring_step<kFull>(const_cast<uint8_t*>(smem), g, t, stage);
   compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
   softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
   compute_s(smem, g, (stage + 1) % kStages, qf, s);
@@ -283,7 +286,7 @@ __device__ __attribute__((always_inline)) void fixed_last(const uint8_t* smem, c
                                                           const float (&nshift)[2], float alpha, int hh,
                                                           const f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
                                                           bf16x8 (&p_cur)[2][2]) {
-  ring_step(g, t, stage);
+  ring_step(const_cast<uint8_t*>(smem), g, t, stage);
   compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
   const int valid = (int)(g.len - (int64_t)t * kKT);
   if (valid >= kKT) softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
@@ -329,7 +332,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   }
   const int n_tiles = (int)((cd.len + kKT - 1) / kKT);
 #pragma unroll
-  for (int t = 0; t < kAhead; ++t) issue_tile(g, t, t);
+  for (int t = 0; t < kAhead; ++t) issue_tile(const_cast<uint8_t*>(smem), g, t, t);
   wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
   barrier();
   if (kFixed) {
@@ -338,7 +341,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
     f32x16 s[2];
     bf16x8 pA[2][2], pB[2][2];   // P(t) lives in pA for even t, pB for odd t
     compute_s(smem, g, 0, qf, s);
-    ring_step(g, 0, 0);
+    ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
     if (n_tiles == 1) {
       const int valid = (int)cd.len;
       if (valid >= kKT) softmax_fixed<false>(s, pA, lsum, nshift, alpha, kKT, hh);
@@ -369,7 +372,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   } else {
     for (int t = 0; t < n_tiles; ++t) {
       const int stage = t % kStages;
-      ring_step(g, t, stage);
+      ring_step(const_cast<uint8_t*>(smem), g, t, stage);
       f32x16 s[2];
       bf16x8 p[2][2];
       compute_s(smem, g, stage, qf, s);
@@ -422,6 +425,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
     const float other = __shfl_xor(dot, 32, 64);
     cdot[n] = hh == 0 ? dot + other : other + dot;
   }
+  // The query fragments are read only as MFMA B operands, which may sit in accumulation
+  // registers: pin them there so the 256 architectural VGPRs hold S, P and the K/V
+  // fragments of the pipeline.
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qf[n][kk]));
 
   f32x16 o[2][4];
 #pragma unroll
