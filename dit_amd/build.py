@@ -35,9 +35,15 @@ def _hipcc() -> str:
     return "hipcc"
 
 
+# Per-file flags.  The bf16 attention kernel keeps its MFMA accumulators in architectural
+# VGPRs (so the exp2 work reads the scores without v_accvgpr_read copies) and pins the
+# resident query fragments in the accumulation registers instead.
+EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

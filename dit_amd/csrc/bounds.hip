@@ -78,6 +78,14 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
   }
 }
 
+// Row j of the global key order (chunk by chunk) for this (b, h), in K or in V.
+template <typename T>
+__device__ inline const T* key_row(const BoundsArgs& a, int b, int h, int64_t j, bool v) {
+  const ChunkDesc& cd = a.ch[find_chunk(a, j)];
+  return v ? reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + (j - cd.start) * cd.v_ss + h * cd.v_sh
+           : reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (j - cd.start) * cd.k_ss + h * cd.k_sh;
+}
+
 // Partial key sums for the COMPUTE centring mode: slab s of the global key range, one
 // (b, h) per blockIdx.y.  Thread (rg, c) sums keys rg, rg + nrg, ... of the slab for the
 // 8 dims of column chunk c; the row groups are then added in rg order.
@@ -89,18 +97,19 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(BoundsArgs a) {
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t s0 = a.N * blockIdx.x / kKmeanSlabs, s1 = a.N * (blockIdx.x + 1) / kKmeanSlabs;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (rg < nrg) {
-    int ci = 0;
-    for (int64_t j = s0 + rg; j < s1; j += nrg) {
-      while (ci + 1 < a.n_chunks && j >= a.ch[ci + 1].start) ++ci;
-      const ChunkDesc& cd = a.ch[ci];
-      const T* row = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (j - cd.start) * cd.k_ss +
-                     h * cd.k_sh + 8 * c;
-      float f[8];
-      load8(row, f);
+  // eight rows in flight per thread; they are added in increasing key order
+  for (int64_t j = s0 + rg; j < s1; j += 8 * nrg) {
+    float f[8][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[i];
+    for (int u = 0; u < 8; ++u) {
+      const int64_t jj = j + (int64_t)u * nrg;
+      if (jj < s1) load8(key_row<T>(a, b, h, jj, false) + 8 * c, f[u]);
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j + (int64_t)u * nrg < s1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[u][i];
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = acc[i];
@@ -127,43 +136,73 @@ __global__ void kmean_final_kernel(BoundsArgs a) {
   }
 }
 
-// One key per thread: K2 = max over keys of sum_d (k_d - k_mean_d)^2 (fp64, d in order),
-// and the V-magnitude check on the same key's value row.
+// One row per thread in the norm kernels: every 16-byte piece of the row is loaded before
+// any arithmetic, so a wave keeps 16 loads per lane in flight; the row is then summed in
+// index order.  Loads a row of D elements (D = 64 or 128; 128 or 256 bytes for bf16, 256 or 512 for fp32)
+// as 16-byte pieces into registers.
+template <typename T>
+struct RowRegs {
+  static constexpr int kPieces = 128 * (int)sizeof(T) / 16;   // for D = 128
+  uint4 p[kPieces];
+  __device__ inline void load(const T* row, int D) {
+    const int n = D * (int)sizeof(T) / 16;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      if (i < n) p[i] = reinterpret_cast<const uint4*>(row)[i];
+  }
+  __device__ inline float elem(int d) const {   // d in [0, D)
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+    if (sizeof(T) == 2) {
+      const uint32_t u = w[d >> 1];
+      return __uint_as_float((d & 1) ? (u & 0xffff0000u) : (u << 16));
+    }
+    return __uint_as_float(w[d]);
+  }
+};
+
+// fp64 sum over d in index order of (x_d - c_d)^2.
+template <typename T>
+__device__ inline double row_sumsq(const RowRegs<T>& r, const float* c, int D) {
+  double s = 0.0;
+#pragma unroll
+  for (int d = 0; d < 128; ++d) {
+    if (d < D) {
+      const double t = (double)r.elem(d) - (double)c[d];
+      s = s + t * t;
+    }
+  }
+  return s;
+}
+
+// 256 keys of one (b, h) per workgroup: K2 = max over keys of sum_d (k_d - k_mean_d)^2
+// (fp64, d in order), and the V-magnitude check on the same keys' value rows.
 template <typename T>
 __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
+  __shared__ float km[128];
   __shared__ unsigned long long wmax[4];
   __shared__ int wbad[4];
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  if (tid < a.D) km[tid] = a.k_mean[(int64_t)bh * a.D + tid];
+  __syncthreads();
   unsigned long long best = 0ull;
   int bad = 0;
   if (j < a.N) {
-    const int ci = find_chunk(a, j);
-    const ChunkDesc& cd = a.ch[ci];
-    const int64_t jj = j - cd.start;
-    const T* krow = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + jj * cd.k_ss + h * cd.k_sh;
-    const T* vrow = reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + jj * cd.v_ss + h * cd.v_sh;
-    const float* km = a.k_mean + (int64_t)bh * a.D;
-    double s = 0.0;
-    for (int d0 = 0; d0 < a.D; d0 += 8) {
-      float f[8], g[8];
-      load8(krow + d0, f);
-      load8(vrow + d0, g);
+    RowRegs<T> kr, vr;
+    kr.load(key_row<T>(a, b, h, j, false), a.D);
+    vr.load(key_row<T>(a, b, h, j, true), a.D);
+    best = (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km, a.D));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double t = (double)f[i] - (double)km[d0 + i];
-        s = s + t * t;
-        bad |= !(fabsf(g[i]) <= 256.0f);
-      }
-    }
-    best = (unsigned long long)__double_as_longlong(s);
+    for (int d = 0; d < 128; ++d)
+      if (d < a.D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
   }
   best = wave_max_u64(best);
   const int any_bad = __any(bad) ? 1 : 0;
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { wmax[w] = best; wbad[w] = any_bad; }
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) { wmax[w] = best; wbad[w] = any_bad; }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     unsigned long long m = wmax[0];
     int vb = wbad[0];
     for (int i = 1; i < 4; ++i) { m = wmax[i] > m ? wmax[i] : m; vb |= wbad[i]; }
@@ -173,26 +212,25 @@ __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
 }
 
 // One query row per thread: Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2.
+// Each wave's 64 rows lie in one q-block (q_block is a multiple of 64).
 template <typename T>
 __global__ __launch_bounds__(256) void qnorm_kernel(BoundsArgs a) {
+  __shared__ float zero[128];
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t i0 = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63);  // wave's first row
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i0 >= a.Sq) return;  // whole wave past the end
+  const int tid = threadIdx.x;
+  if (tid < 128) zero[tid] = 0.0f;
+  __syncthreads();
+  const int64_t iw = (int64_t)blockIdx.x * 256 + (tid & ~63);   // the wave's first row
+  const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+  if (iw >= a.Sq) return;
   unsigned long long v = 0ull;
   if (i < a.Sq) {
-    const T* row = reinterpret_cast<const T*>(a.q) + b * a.q_sb + i * a.q_ss + h * a.q_sh;
-    double s = 0.0;
-    for (int d0 = 0; d0 < a.D; d0 += 8) {
-      float f[8];
-      load8(row + d0, f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s = s + (double)f[k] * (double)f[k];
-    }
-    v = (unsigned long long)__double_as_longlong(s);
+    RowRegs<T> qr;
+    qr.load(reinterpret_cast<const T*>(a.q) + b * a.q_sb + i * a.q_ss + h * a.q_sh, a.D);
+    v = (unsigned long long)__double_as_longlong(row_sumsq<T>(qr, zero, a.D));
   }
   v = wave_max_u64(v);
-  if ((threadIdx.x & 63) == 0) atomicMax(a.q2 + (int64_t)bh * a.nqb + i0 / a.q_block, v);
+  if ((tid & 63) == 0) atomicMax(a.q2 + (int64_t)bh * a.nqb + iw / a.q_block, v);
 }
 
 // U = alpha64 * sqrt(Q2 * K2); m = ceil(U) - C; elig = v_ok && U <= gate && U finite.
