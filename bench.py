@@ -31,9 +31,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("attn_bf16.hip", "fixed_loop.inc")
+
+
 def kernel_source_hash() -> str:
-    with open(os.path.join(ROOT, "dit_amd", "csrc", "attn_bf16.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dit_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -50,9 +50,20 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _generate() -> None:
+    """Writes the generated kernel sources (the assembly main loop of the bf16 kernel)."""
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_fixed_loop
+    finally:
+        sys.path.remove(CSRC)
+    gen_fixed_loop.main()
+
+
 def build(verbose: bool = False) -> str:
-    """Compiles every source and links dit_amd/libfixedm.so; returns its path."""
+    """Generates and compiles every source and links dit_amd/libfixedm.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    _generate()
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

@@ -167,9 +167,25 @@ __device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, co
   }
 }
 
+// V^T fragments of one tile (the A operands of O^T += V^T P^T): for each 16-key step st and
+// 32-dim tile m, a lane holds one dim and 8 keys in the P register order.  Each fragment
+// comes from two LDS transpose reads, each giving 4 keys x 16 dims to a 16-lane group.
+__device__ __attribute__((always_inline)) void load_v(const uint8_t* smem, const Ring& g, int stage,
+                                                      bf16x8 (&vf)[2][4]) {
+  const uint8_t* vs = smem + stage * kTileBytes;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* a0 = vs + g.voff[m] + 4096 * st;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 2048));
+      vf[st][m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
 // O^T += V(tile)^T P(tile)^T: four 32-dim tiles x two 16-key steps x two query tiles.
-// The V^T operand (lane: one dim, 8 keys in the P register order) comes from two LDS
-// transpose reads, each giving 4 keys x 16 dims to a 16-lane group.
 __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, const Ring& g, int stage,
                                                           const bf16x8 (&p)[2][2], f32x16 (&o)[2][4]) {
   const uint8_t* vs = smem + stage * kTileBytes;
@@ -186,6 +202,9 @@ __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, c
     }
   }
 }
+
+// The steady-state fixed-m loop, written out instruction by instruction (generated).
+#include "fixed_loop.inc"
 
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
 // and adds the same rounded values to the row sum, so numerator and denominator see
@@ -354,13 +373,24 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       // every tile the group prefetches is a full one, then one step at a time
       const int n_full = (int)(cd.len / kKT);
       int t = 1;
-      for (; t + kStages + kAhead <= n_full; t += kStages) {
+      // groups of kStages steps whose prefetched tiles are all full ones
+      const int groups = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
+      if (groups > 0) {
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
+        uint32_t koff[8], voff[4];
 #pragma unroll
-        for (int jj = 0; jj < kStages; ++jj) {
-          const int stage = (1 + jj) % kStages;
-          if (jj & 1) fixed_mid<true>(smem, g, t + jj, stage, qf, o, lsum, nshift, alpha, hh, s, pB, pA);
-          else fixed_mid<true>(smem, g, t + jj, stage, qf, o, lsum, nshift, alpha, hh, s, pA, pB);
-        }
+        for (int kk = 0; kk < 8; ++kk) koff[kk] = lds0 + g.koff[kk];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
+        const uint32_t dma[4] = {g.kdma[0], g.kdma[1], g.vdma[0], g.vdma[1]};
+        const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * g.wave);
+        const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(1 + kAhead) * g.ktile);
+        const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(1 + kAhead) * g.vtile);
+        bf16x8 vf[2][4];
+        load_v(smem, g, 0, vf);   // V^T fragments of tile 0, consumed by the first step
+        fixed_loop_asm(o, qf, s, pA, vf, lsum, nshift, koff, voff, dma, kt, vt, uniform_u64(g.ktile),
+                       uniform_u64(g.vtile), lds_wave, alpha, (uint32_t)groups);
+        t += groups * kStages;
       }
       for (; t < n_tiles - 1; ++t) {
         if (t & 1) fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, alpha, hh, s, pA, pB);

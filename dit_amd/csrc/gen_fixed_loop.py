@@ -1,0 +1,289 @@
+"""Generates fixed_loop.inc: the steady-state fixed-m attention loop for gfx950 as one inline
+assembly block with every value in a named register.
+
+    python dit_amd/csrc/gen_fixed_loop.py      # run by dit_amd.build before compiling
+
+Why assembly: one wave per SIMD must overlap the matrix cores with the vector ALUs.  The
+exp2/convert/row-sum work of a 32-key tile is about three VALU instructions per MFMA, and a
+wave only hides them if they sit between its MFMAs; the compiler keeps the output
+accumulator in VGPRs, runs out of registers for prefetched fragments, and bunches the VALU
+work behind one half of the MFMAs.  Here the register classes and the instruction order
+are fixed by hand:
+
+  AGPR  a[0:127]    O^T accumulators o[n][m]      (n: 32-query tile, m: 32-dim tile)
+        a[128:191]  resident query fragments q[n][kk]
+        a[192:255]  K fragments, double buffered by tile parity
+  VGPR  v[0:63]     S^T scores, double buffered by tile parity (v[32:63] holds the odd tiles)
+        v[64:95]    packed bf16 probabilities P, double buffered (v[64:79] even tiles)
+        v[96:159]   V^T fragments, double buffered (v[96:127] even tiles)
+        v160-161    row sums l[n];  v162-163  -(m + c_i) per query column
+        v164-171    K fragment LDS addresses;  v172-175  V^T fragment LDS addresses
+        v176-179    DMA lane offsets (K row 0/1, V row 0/1)
+  SGPR  s[60:61] next K tile address, s[62:63] next V tile address, s[64:65] / s[66:67]
+        bytes between tiles, s68 this wave's LDS DMA base, s69 alpha, s70 group count
+
+One step handles tile t (its stage in the 8-deep LDS ring is static inside the unrolled
+group of 8 steps):
+  wait for this wave's part of tile t+1, barrier, read K(t+1) fragments, start the DMA of
+  tile t+6 into the stage tile t-2 used; then 16 MFMAs O += V(t-1) P(t-1) and 16 MFMAs
+  S(t+1) = K(t+1) Q^T, with the 96 VALU instructions that turn S(t) into P(t) and the row
+  sums spread three to an MFMA, and the 16 LDS transpose reads of V(t) (used next step)
+  spread over the second half.
+
+Hazards the assembler does not resolve are covered by construction and checked here:
+  * a VALU read of an MFMA result (S) waits >= 12 wait states after the producing MFMA
+    (16 enforced);
+  * M0 written by SALU is followed by one wait state before the LDS DMA that reads it;
+  * every register an LDS read or VALU op overwrites was last read by an MFMA at least one
+    whole step earlier (double buffers), and every LDS read is waited for (lgkmcnt) before
+    its value is used or the block ends;
+  * the block starts and ends with 16 wait states so compiler code on either side sees no
+    MFMA or VALU hazard across the boundary.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+STAGES = 8
+AHEAD = 6
+TILE_BYTES = 8192
+V_RING = STAGES * TILE_BYTES          # the V ring starts 64 KB into the shared buffer
+DMA_WAIT = (AHEAD - 2) * 4            # DMA instructions allowed in flight at a step start
+
+O_BASE, Q_BASE, K_BASE = 0, 128, 192
+S_BASE, P_BASE, V_BASE = 0, 64, 96
+LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
+S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_ALPHA, S_CNT = 60, 62, 64, 66, 68, 69, 70
+ONES_BF16X2 = "0x3f803f80"
+
+
+def areg(base, n=1):
+    return f"a{base}" if n == 1 else f"a[{base}:{base + n - 1}]"
+
+
+def vreg(base, n=1):
+    return f"v{base}" if n == 1 else f"v[{base}:{base + n - 1}]"
+
+
+def o_reg(n, m):
+    return areg(O_BASE + 16 * (4 * n + m), 16)
+
+
+def q_reg(n, kk):
+    return areg(Q_BASE + 32 * n + 4 * kk, 4)
+
+
+def k_reg(buf, kk):
+    return areg(K_BASE + 32 * buf + 4 * kk, 4)
+
+
+def s_first(buf, n):
+    return S_BASE + 32 * buf + 16 * n
+
+
+def p_first(buf, n):
+    return P_BASE + 16 * buf + 8 * n
+
+
+def v_first(buf, st, m):
+    return V_BASE + 32 * buf + 4 * (4 * st + m)
+
+
+def softmax_ops(buf):
+    """The 96 VALU instructions turning S(t) (scores buffer `buf`) into P(t) and adding the
+    bf16-rounded probabilities to the row sums, ordered so that dependent instructions are
+    several slots apart.  Each op is (text, whether it reads the scores buffer)."""
+    ops = []
+    for g in range(4):
+        for n in range(2):
+            for r in range(4 * g, 4 * g + 4):
+                x = s_first(buf, n) + r
+                ops.append((f"v_fma_f32 v{x}, s{S_ALPHA}, v{x}, v{NSHIFT + n}", True))
+        for n in range(2):
+            for r in range(4 * g, 4 * g + 4):
+                x = s_first(buf, n) + r
+                ops.append((f"v_exp_f32 v{x}, v{x}", True))
+        for n in range(2):
+            for i in (2 * g, 2 * g + 1):
+                x = s_first(buf, n) + 2 * i
+                ops.append((f"v_cvt_pk_bf16_f32 v{p_first(buf, n) + i}, v{x}, v{x + 1}", True))
+        for i in (2 * g, 2 * g + 1):
+            for n in range(2):
+                ops.append((f"v_dot2c_f32_bf16_e32 v{LSUM + n}, {ONES_BF16X2}, v{p_first(buf, n) + i}", False))
+    assert len(ops) == 96
+    return ops
+
+
+class Emitter:
+    """Collects the instruction lines and pads VALU reads of MFMA-written score registers."""
+
+    MIN_WAIT = 16
+
+    def __init__(self):
+        self.lines = []
+        self.count = 0                          # instructions emitted (each >= 1 wait state)
+        self.s_written = {0: -10**9, 1: -10**9}  # index of the last MFMA writing each S buffer
+
+    def emit(self, text, reads_sbuf=None, writes_sbuf=None):
+        if reads_sbuf is not None:
+            gap = self.count - self.s_written[reads_sbuf] - 1
+            if gap < self.MIN_WAIT:
+                self.lines.append(f"s_nop {self.MIN_WAIT - gap - 1}")
+                self.count += self.MIN_WAIT - gap
+        self.lines.append(text)
+        if writes_sbuf is not None:
+            self.s_written[writes_sbuf] = self.count
+        self.count += 1
+
+
+def step(e: Emitter, jj: int):
+    """Step jj of the unrolled group: tile t with t = 1 + jj (mod 8)."""
+    t_mod = 1 + jj
+    cur = t_mod % 2            # parity of t: S(t), P(t), V(t) buffers
+    prv = 1 - cur              # parity of t-1 (= parity of t+1)
+    stage_t = t_mod % STAGES
+    stage_next = (t_mod + 1) % STAGES
+    stage_dma = (t_mod + AHEAD) % STAGES
+
+    e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
+    e.emit("s_barrier")
+    e.emit("s_waitcnt lgkmcnt(0)")
+    # K(t+1) fragments into the K buffer of parity t+1
+    for kk in range(8):
+        e.emit(f"ds_read_b128 {k_reg(prv, kk)}, v{KOFF + kk} offset:{stage_next * TILE_BYTES}")
+    # DMA of tile t+6 into the stage of tile t-2: K rows then V rows of this wave
+    for i in range(2):
+        e.emit(f"s_add_u32 m0, s{S_LDS}, {stage_dma * TILE_BYTES + 1024 * i}")
+        e.emit("s_nop 0")
+        e.emit(f"global_load_lds_dwordx4 v{DMA + i}, s[{S_KT}:{S_KT + 1}]")
+        e.emit(f"s_add_u32 m0, s{S_LDS}, {V_RING + stage_dma * TILE_BYTES + 1024 * i}")
+        e.emit("s_nop 0")
+        e.emit(f"global_load_lds_dwordx4 v{DMA + 2 + i}, s[{S_VT}:{S_VT + 1}]")
+    e.emit(f"s_add_u32 s{S_KT}, s{S_KT}, s{S_KTILE}")
+    e.emit(f"s_addc_u32 s{S_KT + 1}, s{S_KT + 1}, s{S_KTILE + 1}")
+    e.emit(f"s_add_u32 s{S_VT}, s{S_VT}, s{S_VTILE}")
+    e.emit(f"s_addc_u32 s{S_VT + 1}, s{S_VT + 1}, s{S_VTILE + 1}")
+
+    valu = softmax_ops(cur)
+    vi = 0
+
+    def valu3():
+        nonlocal vi
+        for _ in range(3):
+            text, reads = valu[vi]
+            e.emit(text, reads_sbuf=cur if reads else None)
+            vi += 1
+
+    # O^T += V(t-1)^T P(t-1)^T
+    for st in range(2):
+        for m in range(4):
+            for n in range(2):
+                vf = vreg(v_first(prv, st, m), 4)
+                p = vreg(p_first(prv, n) + 4 * st, 4)
+                e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
+                valu3()
+    # S(t+1) = K(t+1) Q^T, with the V(t) transpose reads in the first half
+    e.emit("s_waitcnt lgkmcnt(0)")
+    tr = [(st, m, h) for st in range(2) for m in range(4) for h in range(2)]
+    ti = 0
+    for kk in range(8):
+        for n in range(2):
+            s0 = s_first(prv, n)
+            src_c = "0" if kk == 0 else vreg(s0, 16)
+            e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(prv, kk)}, {q_reg(n, kk)}, {src_c}",
+                   writes_sbuf=prv)
+            if ti < len(tr):
+                for _ in range(2):
+                    st, m, h = tr[ti]
+                    dst = vreg(v_first(cur, st, m) + 2 * h, 2)
+                    off = stage_t * TILE_BYTES + 4096 * st + 2048 * h
+                    e.emit(f"ds_read_b64_tr_b16 {dst}, v{VOFF + m} offset:{off}")
+                    ti += 1
+            valu3()
+    assert vi == 96 and ti == 16
+
+
+def generate() -> str:
+    e = Emitter()
+    e.emit("s_nop 7")
+    e.emit("s_nop 7")
+    e.lines.append("L_fixedm_group_%=:")
+    for jj in range(STAGES):
+        step(e, jj)
+    e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
+    e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
+    e.emit("s_cbranch_scc1 L_fixedm_group_%=")
+    e.emit("s_waitcnt lgkmcnt(0)")
+    e.emit("s_nop 7")
+    e.emit("s_nop 7")
+    body = "\n".join(f'      "{l}\\n"' for l in e.lines)
+
+    outs = []
+    for n in range(2):
+        for m in range(4):
+            outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
+    for n in range(2):
+        outs.append(f'"+{{{vreg(s_first(1, n), 16)}}}"(s[{n}])')
+    for n in range(2):
+        for st in range(2):
+            outs.append(f'"+{{{vreg(p_first(0, n) + 4 * st, 4)}}}"(p[{n}][{st}])')
+    for st in range(2):
+        for m in range(4):
+            outs.append(f'"+{{{vreg(v_first(0, st, m), 4)}}}"(vf[{st}][{m}])')
+    outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
+             f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
+             f'"+{{s{S_CNT}}}"(groups)']
+    ins = []
+    for n in range(2):
+        for kk in range(8):
+            ins.append(f'"{{{q_reg(n, kk)}}}"(qf[{n}][{kk}])')
+    ins += [f'"{{v{NSHIFT}}}"(nshift[0])', f'"{{v{NSHIFT + 1}}}"(nshift[1])']
+    ins += [f'"{{v{KOFF + kk}}}"(koff[{kk}])' for kk in range(8)]
+    ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
+    ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
+    ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
+            f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s{S_ALPHA}}}"(alpha)']
+    clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
+            + [f"v{i}" for i in range(V_BASE + 32, V_BASE + 64)] + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
+            + ["scc", "memory"])
+    clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
+
+    def join(items):
+        return ",\n        ".join(items)
+
+    return f"""// Generated by gen_fixed_loop.py; do not edit by hand.
+// The steady-state fixed-m loop: `groups` groups of 8 pipelined 32-key steps, tiles
+// t0 .. t0 + 8 groups - 1 with t0 = 1 (mod 8).  On entry: s = S(t0) (odd-tile buffer), p =
+// P(t0 - 1), vf = the V^T fragments of tile t0 - 1, kt / vt = the addresses of tile t0 + 6,
+// tiles up to t0 + 5 issued and tile t0 in LDS.  On exit the same invariants hold for
+// t0 + 8 groups; every LDS read has completed.
+__device__ __attribute__((always_inline)) inline void fixed_loop_asm(
+    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], f32x16 (&s)[2], bf16x8 (&p)[2][2], bf16x8 (&vf)[2][4],
+    float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
+    const uint32_t (&dma)[4], uint64_t kt, uint64_t vt, uint64_t ktile, uint64_t vtile, uint32_t lds_wave,
+    float alpha, uint32_t groups) {{
+  asm volatile(
+{body}
+      : {join(outs)}
+      : {join(ins)}
+      : {clob_text});
+}}
+"""
+
+
+def main(out_path=None):
+    out_path = out_path or os.path.join(os.path.dirname(os.path.abspath(__file__)), "fixed_loop.inc")
+    text = generate()
+    old = None
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            old = f.read()
+    if old != text:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(main(sys.argv[1] if len(sys.argv) > 1 else None))
