@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB fp32 read+write kernel (3 times): the reference "
+                         "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,6 +130,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 1 << 30, "calibrate_copy_bytes_written": 1 << 30}),
+              flush=True)
+        return
 
     from dit_amd import fixedm as F
     from dit_amd import workloads as WL
