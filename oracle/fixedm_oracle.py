@@ -163,6 +163,8 @@ def bounds(q, k_chunks, v_chunks, *, scale: float, q_block: int, center: str = "
     # K2[b,h] = max_j sum_d (k_jd - kbar_d)^2 over every real key of every chunk.
     k2 = np.zeros((B, H), dtype=np.float64)
     for c in kc:
+        if c.shape[1] == 0:                              # an empty chunk has no keys
+            continue
         diff = c - kbar64[:, None, :, :]                 # [B, Sc, H, D]
         k2 = np.maximum(k2, _rowsum_sq_in_order(diff).max(axis=1))
 

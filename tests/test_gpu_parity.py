@@ -216,6 +216,25 @@ def test_mixed_bodies_in_one_workgroup(F):
     assert ob.elig.any() and not ob.elig.all()
 
 
+def test_mixed_bodies_with_assembly_loop(F):
+    """Long chunks (the fixed-m waves run the assembly main loop) next to online-softmax waves
+    of the same workgroups: both bodies must meet at the same ring barriers."""
+    say("edge: mixed bodies, long chunks")
+    ob, _ = _generic(F, 39, "bf16", 1, 2, 128, 256, (1000, 737), q_block=64,
+                     loud_rows=(1, 128, 192, 14.0))
+    assert ob.elig.any() and not ob.elig.all()
+
+
+@pytest.mark.parametrize("chunks", [
+    (448, 480, 481),          # 14, 15 and 15 + 1 tiles: no assembly group, one group, one + partial
+    (735, 0, 736, 1000),      # 22 and 23 full tiles (one / two groups) and an empty chunk
+    (32 * (7 + 8 * 3) + 31,), # three groups and a 31-key last tile
+])
+def test_assembly_loop_boundaries(F, chunks):
+    say(f"edge: assembly-loop boundaries {chunks}")
+    _generic(F, 40 + len(chunks), "bf16", 1, 2, 128, 300, chunks, q_block=64, center="compute")
+
+
 def test_v_magnitude_forces_fallback(F):
     say("edge: |v| > 256")
     ob, _ = _generic(F, 35, "bf16", 1, 2, 128, 200, (150, 100), q_block=64,

@@ -304,6 +304,24 @@ def test_method_forward_mixed_bodies_and_centring():
     assert np.max(np.abs(o - ref)) < 1e-11 and np.max(np.abs(lse - lse_ref)) < 1e-11
 
 
+def test_empty_chunk_changes_nothing():
+    """A ring step with no keys: the bounds and the method's output equal those of the same
+    keys without it (the maxima and sums run over real keys only)."""
+    inp = WL.generic_inputs(22, "fp32", 1, 2, 16, 40, (30, 0, 25), q_block=32, k_offset=1.0)
+    kk = [inp.k[0], inp.k[2]]
+    vv = [inp.v[0], inp.v[2]]
+    scale = 0.25
+    b0 = O.bounds(inp.q, inp.k, inp.v, scale=scale, q_block=32, center="compute", dtype="fp32")
+    b1 = O.bounds(inp.q, kk, vv, scale=scale, q_block=32, center="compute", dtype="fp32")
+    for f in ("m", "elig", "q2", "k2", "k_mean"):
+        assert np.array_equal(getattr(b0, f), getattr(b1, f)), f
+    o0, l0, _ = O.method_forward(inp.q, inp.k, inp.v, b0, scale=scale, q_block=32, block=16)
+    o1, l1, _ = O.method_forward(inp.q, kk, vv, b1, scale=scale, q_block=32, block=16)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(kk, 1), np.concatenate(vv, 1), scale)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    assert np.max(np.abs(o0 - ref)) < 1e-12 and np.max(np.abs(l0 - lse_ref)) < 1e-12
+
+
 # ---------------------------------------------------------------- planted mistakes ----
 def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     """Mistakes planted in the oracle (on the CPU) trip the pins above."""
