@@ -18,7 +18,7 @@
 //   * In the 32x32 accumulator layout each lane owns ONE query column and 16 keys, so the
 //     fixed-m exponent e = alpha*S - (m + c_i) is one FMA with a per-lane constant, the
 //     row sum is a per-lane running fp32 sum (of the same bf16-rounded probabilities the
-//     PV product consumes, one v_dot2 per pair), and the exp2'd scores, packed to bf16, are
+//     PV product consumes), and the exp2'd scores, packed to bf16, are
 //     already the B operand of O^T += V^T P^T with no transpose (the K-stationary layout of
 //     [CM]).  The matching key order on the V^T operand comes from the gfx950 LDS transpose
 //     read ds_read_b64_tr_b16.
@@ -207,15 +207,17 @@ __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, c
 #include "fixed_loop.inc"
 
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
-// and adds the same rounded values to the row sum, so numerator and denominator see
-// identical weights.
+// and adds the same rounded values to the row sum (low half then high half of each pair,
+// unpacked with integer ops), so numerator and denominator see identical weights.
 __device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int base, float& lsum) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x2 w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     w[i] = __builtin_convertvector((f32x2){e[base + 2 * i], e[base + 2 * i + 1]}, bf16x2);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(w[i], ones, lsum, false);
+    uint32_t u;
+    __builtin_memcpy(&u, &w[i], 4);
+    lsum += __uint_as_float(u << 16);
+    lsum += __uint_as_float(u & 0xffff0000u);
   }
   bf16x8 r;
   __builtin_memcpy(&r, w, 16);

@@ -4,7 +4,7 @@ assembly block with every value in a named register.
     python dit_amd/csrc/gen_fixed_loop.py      # run by dit_amd.build before compiling
 
 Why assembly: one wave per SIMD must overlap the matrix cores with the vector ALUs.  The
-exp2/convert/row-sum work of a 32-key tile is about three VALU instructions per MFMA, and a
+exp2/convert/row-sum work of a 32-key tile is four to five VALU instructions per MFMA, and a
 wave only hides them if they sit between its MFMAs; the compiler keeps the output
 accumulator in VGPRs, runs out of registers for prefetched fragments, and bunches the VALU
 work behind one half of the MFMAs.  Here the register classes and the instruction order
@@ -17,6 +17,7 @@ are fixed by hand:
         v[64:95]    packed bf16 probabilities P, double buffered (v[64:79] even tiles)
         v[96:159]   V^T fragments, double buffered (v[96:127] even tiles)
         v160-161    row sums l[n];  v162-163  -(m + c_i) per query column
+        v180-187    temporaries of the row-sum unpacking
         v164-171    K fragment LDS addresses;  v172-175  V^T fragment LDS addresses
         v176-179    DMA lane offsets (K row 0/1, V row 0/1)
   SGPR  s[60:61] next K tile address, s[62:63] next V tile address, s[64:65] / s[66:67]
@@ -24,11 +25,17 @@ are fixed by hand:
 
 One step handles tile t (its stage in the 8-deep LDS ring is static inside the unrolled
 group of 8 steps):
-  wait for this wave's part of tile t+1, barrier, read K(t+1) fragments, start the DMA of
-  tile t+6 into the stage tile t-2 used; then 16 MFMAs O += V(t-1) P(t-1) and 16 MFMAs
-  S(t+1) = K(t+1) Q^T, with the 96 VALU instructions that turn S(t) into P(t) and the row
-  sums spread three to an MFMA, and the 16 LDS transpose reads of V(t) (used next step)
-  spread over the second half.
+  wait for this wave's part of tile t+1, barrier; then 16 MFMAs O += V(t-1) P(t-1) and 16
+  MFMAs S(t+1) = K(t+1) Q^T, with the 144 VALU instructions that turn S(t) into P(t) and
+  the row sums spread over all 32, the K(t+1) fragment reads and the DMA of tile t+6 (into
+  the stage tile t-2 used) between the first PV MFMAs, and the 16 LDS transpose reads of
+  V(t) (used next step) in the first half of the S MFMAs.
+
+Measured choices (shader-clock cycles per step, s_memtime-instrumented builds on gfx950):
+issuing the K reads and the DMA as a block after the barrier left the matrix cores idle
+(-7.5% when spread between the MFMAs); summing the bf16 pairs with v_dot2c_f32_bf16 costs
+~9 cycles of matrix-core time per instruction, while unpacking each pair with a shift and a
+mask and adding in fp32 (four plain VALU ops) overlaps the MFMAs (-3.7%).
 
 Hazards the assembler does not resolve are covered by construction and checked here:
   * a VALU read of an MFMA result (S) waits >= 12 wait states after the producing MFMA
@@ -55,7 +62,7 @@ O_BASE, Q_BASE, K_BASE = 0, 128, 192
 S_BASE, P_BASE, V_BASE = 0, 64, 96
 LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
 S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_ALPHA, S_CNT = 60, 62, 64, 66, 68, 69, 70
-ONES_BF16X2 = "0x3f803f80"
+TMP = 180                             # v180-v187: bf16 -> f32 unpacking temporaries
 
 
 def areg(base, n=1):
@@ -91,7 +98,7 @@ def v_first(buf, st, m):
 
 
 def softmax_ops(buf):
-    """The 96 VALU instructions turning S(t) (scores buffer `buf`) into P(t) and adding the
+    """The 144 VALU instructions turning S(t) (scores buffer `buf`) into P(t) and adding the
     bf16-rounded probabilities to the row sums, ordered so that dependent instructions are
     several slots apart.  Each op is (text, whether it reads the scores buffer)."""
     ops = []
@@ -108,10 +115,19 @@ def softmax_ops(buf):
             for i in (2 * g, 2 * g + 1):
                 x = s_first(buf, n) + 2 * i
                 ops.append((f"v_cvt_pk_bf16_f32 v{p_first(buf, n) + i}, v{x}, v{x + 1}", True))
+        # row sums of the bf16-rounded pairs: the low half as f32 is the pair shifted left by
+        # 16, the high half is the pair with its low 16 bits cleared; add low then high
         for i in (2 * g, 2 * g + 1):
             for n in range(2):
-                ops.append((f"v_dot2c_f32_bf16_e32 v{LSUM + n}, {ONES_BF16X2}, v{p_first(buf, n) + i}", False))
-    assert len(ops) == 96
+                t = TMP + 4 * (i % 2) + 2 * n
+                w = p_first(buf, n) + i
+                ops.append((f"v_lshlrev_b32 v{t}, 16, v{w}", False))
+                ops.append((f"v_and_b32 v{t + 1}, 0xffff0000, v{w}", False))
+            for n in range(2):
+                ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n}", False))
+            for n in range(2):
+                ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n + 1}", False))
+    assert len(ops) == 144
     return ops
 
 
@@ -149,40 +165,48 @@ def step(e: Emitter, jj: int):
     e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
     e.emit("s_barrier")
     e.emit("s_waitcnt lgkmcnt(0)")
-    # K(t+1) fragments into the K buffer of parity t+1
-    for kk in range(8):
-        e.emit(f"ds_read_b128 {k_reg(prv, kk)}, v{KOFF + kk} offset:{stage_next * TILE_BYTES}")
-    # DMA of tile t+6 into the stage of tile t-2: K rows then V rows of this wave
+    # The matrix cores start right after the barrier; the K(t+1) fragment reads and the DMA
+    # of tile t+6 into the stage of tile t-2 (K rows then V rows of this wave) ride between
+    # the first PV MFMAs (issued back to back after the barrier they left the matrix cores
+    # idle for ~180 cycles a step).  Each M0 write is separated from the DMA that reads it
+    # by at least one instruction, the wait state that hazard needs.
+    kreads = [f"ds_read_b128 {k_reg(prv, kk)}, v{KOFF + kk} offset:{stage_next * TILE_BYTES}" for kk in range(8)]
+    extra = []
     for i in range(2):
-        e.emit(f"s_add_u32 m0, s{S_LDS}, {stage_dma * TILE_BYTES + 1024 * i}")
-        e.emit("s_nop 0")
-        e.emit(f"global_load_lds_dwordx4 v{DMA + i}, s[{S_KT}:{S_KT + 1}]")
-        e.emit(f"s_add_u32 m0, s{S_LDS}, {V_RING + stage_dma * TILE_BYTES + 1024 * i}")
-        e.emit("s_nop 0")
-        e.emit(f"global_load_lds_dwordx4 v{DMA + 2 + i}, s[{S_VT}:{S_VT + 1}]")
-    e.emit(f"s_add_u32 s{S_KT}, s{S_KT}, s{S_KTILE}")
-    e.emit(f"s_addc_u32 s{S_KT + 1}, s{S_KT + 1}, s{S_KTILE + 1}")
-    e.emit(f"s_add_u32 s{S_VT}, s{S_VT}, s{S_VTILE}")
-    e.emit(f"s_addc_u32 s{S_VT + 1}, s{S_VT + 1}, s{S_VTILE + 1}")
+        for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, S_KT),
+                                    (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, S_VT)):
+            extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", kreads.pop(0),
+                          f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
+    extra += [[kr] for kr in kreads]
+    extra.append([f"s_add_u32 s{S_KT}, s{S_KT}, s{S_KTILE}", f"s_addc_u32 s{S_KT + 1}, s{S_KT + 1}, s{S_KTILE + 1}"])
+    extra.append([f"s_add_u32 s{S_VT}, s{S_VT}, s{S_VTILE}", f"s_addc_u32 s{S_VT + 1}, s{S_VT + 1}, s{S_VTILE + 1}"])
 
     valu = softmax_ops(cur)
     vi = 0
 
+    slot = 0
+
     def valu3():
-        nonlocal vi
-        for _ in range(3):
+        nonlocal vi, slot
+        want = (len(valu) * (slot + 1)) // 32
+        while vi < want:
             text, reads = valu[vi]
             e.emit(text, reads_sbuf=cur if reads else None)
             vi += 1
+        slot += 1
 
-    # O^T += V(t-1)^T P(t-1)^T
+    # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first ten MFMAs
     for st in range(2):
         for m in range(4):
             for n in range(2):
                 vf = vreg(v_first(prv, st, m), 4)
                 p = vreg(p_first(prv, n) + 4 * st, 4)
                 e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
+                if extra:
+                    for ins in extra.pop(0):
+                        e.emit(ins)
                 valu3()
+    assert not extra
     # S(t+1) = K(t+1) Q^T, with the V(t) transpose reads in the first half
     e.emit("s_waitcnt lgkmcnt(0)")
     tr = [(st, m, h) for st in range(2) for m in range(4) for h in range(2)]
@@ -201,7 +225,7 @@ def step(e: Emitter, jj: int):
                     e.emit(f"ds_read_b64_tr_b16 {dst}, v{VOFF + m} offset:{off}")
                     ti += 1
             valu3()
-    assert vi == 96 and ti == 16
+    assert vi == len(valu) and ti == 16
 
 
 def generate() -> str:
@@ -209,6 +233,8 @@ def generate() -> str:
     e.emit("s_nop 7")
     e.emit("s_nop 7")
     e.lines.append("L_fixedm_group_%=:")
+    # the loop's back edge: the previous group's last S MFMAs may be a few instructions away
+    e.s_written = {0: e.count - 1, 1: e.count - 1}
     for jj in range(STAGES):
         step(e, jj)
     e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
@@ -245,7 +271,8 @@ def generate() -> str:
     ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
             f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s{S_ALPHA}}}"(alpha)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
-            + [f"v{i}" for i in range(V_BASE + 32, V_BASE + 64)] + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
+            + [f"v{i}" for i in range(V_BASE + 32, V_BASE + 64)] + [f"v{i}" for i in range(TMP, TMP + 8)]
+            + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
             + ["scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
