@@ -151,15 +151,23 @@ __device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const R
   }
 }
 
-// S^T(tile) = K(tile) Q^T for one 32-key tile and two 32-query tiles: 16 MFMAs.
+// S^T(tile) = K(tile) Q^T + init for one 32-key tile and two 32-query tiles: 16 MFMAs.  The
+// fixed-m body starts the chain from -(m + c_i) so S arrives as the exponent; the online
+// body starts from 0.
 __device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const Ring& g, int stage,
-                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2]) {
+                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2],
+                                                         const float (&init)[2]) {
   const uint8_t* ks = smem + stage * kTileBytes;
   bf16x8 kf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
-  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], f32x16{}, 0, 0, 0);
-  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], f32x16{}, 0, 0, 0);
+  f32x16 c[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[n][r] = init[n];
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], c[0], 0, 0, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], c[1], 0, 0, 0);
 #pragma unroll
   for (int kk = 1; kk < 8; ++kk) {
     s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], s[0], 0, 0, 0);
@@ -227,17 +235,18 @@ __device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int 
 // Key index within the tile held by accumulator register r of this lane.
 __device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-// Fixed-m probabilities of one tile: p = 2^(alpha S - (m + c_i)), no max, no rescale.
+// Fixed-m probabilities of one tile: S already holds the exponent alpha q.k - (m + c_i) (the
+// query fragments are pre-scaled by alpha and the MFMA chain starts from -(m + c_i)), so
+// p = 2^S: no max, no rescale.
 template <bool kPartial>
 __device__ __attribute__((always_inline)) void softmax_fixed(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
-                                                             float (&lsum)[2], const float (&nshift)[2],
-                                                             float alpha, int valid, int hh) {
+                                                             float (&lsum)[2], int valid, int hh) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     f32x16 e;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = __builtin_fmaf(alpha, s[n][r], nshift[n]);
+      float x = s[n][r];
       if (kPartial && tile_key(r, hh) >= valid) x = -INFINITY;
       e[r] = __builtin_amdgcn_exp2f(x);
     }
@@ -288,30 +297,29 @@ __device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ri
 
 // Fixed-m step for a full middle tile t (1 <= t <= n_tiles - 2) whose ring stage is
 // `stage`.  Phase 1: the 16 MFMAs of O += V(t-1) P(t-1) run while the VALUs turn S(t)
-// into P(t); phase 2: the 16 MFMAs of S(t+1) = K(t+1) Q^T overwrite S.
+// into P(t); phase 2: the 16 MFMAs of S(t+1) = K(t+1) Q^T - (m + c) overwrite S.
 template <bool kFull = false>
 __device__ __attribute__((always_inline)) void fixed_mid(const uint8_t* smem, const Ring& g, int t, int stage,
                                                          const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
-                                                         float (&lsum)[2], const float (&nshift)[2], float alpha,
-                                                         int hh, f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
+                                                         float (&lsum)[2], const float (&init)[2], int hh,
+                                                         f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
                                                          bf16x8 (&p_cur)[2][2]) {
   ring_step<kFull>(const_cast<uint8_t*>(smem), g, t, stage);
   compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
-  softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
-  compute_s(smem, g, (stage + 1) % kStages, qf, s);
+  softmax_fixed<false>(s, p_cur, lsum, kKT, hh);
+  compute_s(smem, g, (stage + 1) % kStages, qf, s, init);
 }
 
 // Last tile t = n_tiles - 1 >= 1 (possibly partial): O += V(t-1) P(t-1); P(t); O += V(t) P(t).
 __device__ __attribute__((always_inline)) void fixed_last(const uint8_t* smem, const Ring& g, int t, int stage,
-                                                          f32x16 (&o)[2][4], float (&lsum)[2],
-                                                          const float (&nshift)[2], float alpha, int hh,
+                                                          f32x16 (&o)[2][4], float (&lsum)[2], int hh,
                                                           const f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
                                                           bf16x8 (&p_cur)[2][2]) {
   ring_step(const_cast<uint8_t*>(smem), g, t, stage);
   compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
   const int valid = (int)(g.len - (int64_t)t * kKT);
-  if (valid >= kKT) softmax_fixed<false>(s, p_cur, lsum, nshift, alpha, kKT, hh);
-  else softmax_fixed<true>(s, p_cur, lsum, nshift, alpha, valid, hh);
+  if (valid >= kKT) softmax_fixed<false>(s, p_cur, lsum, kKT, hh);
+  else softmax_fixed<true>(s, p_cur, lsum, valid, hh);
   compute_pv(smem, g, stage, p_cur, o);
 }
 
@@ -358,24 +366,22 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   barrier();
   if (kFixed) {
     const float nshift[2] = {-shift[0], -shift[1]};
-    const float alpha = a.alpha;
     f32x16 s[2];
     bf16x8 pA[2][2], pB[2][2];   // P(t) lives in pA for even t, pB for odd t
-    compute_s(smem, g, 0, qf, s);
+    compute_s(smem, g, 0, qf, s, nshift);
     ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
     if (n_tiles == 1) {
       const int valid = (int)cd.len;
-      if (valid >= kKT) softmax_fixed<false>(s, pA, lsum, nshift, alpha, kKT, hh);
-      else softmax_fixed<true>(s, pA, lsum, nshift, alpha, valid, hh);
+      if (valid >= kKT) softmax_fixed<false>(s, pA, lsum, kKT, hh);
+      else softmax_fixed<true>(s, pA, lsum, valid, hh);
       compute_pv(smem, g, 0, pA, o);
     } else {
-      softmax_fixed<false>(s, pA, lsum, nshift, alpha, kKT, hh);
-      compute_s(smem, g, 1, qf, s);
-      // middle tiles 1 .. n_tiles-2: groups of kStages with static ring stages while
-      // every tile the group prefetches is a full one, then one step at a time
+      softmax_fixed<false>(s, pA, lsum, kKT, hh);
+      compute_s(smem, g, 1, qf, s, nshift);
+      // middle tiles 1 .. n_tiles-2: groups of kStages steps (the assembly loop) while every
+      // tile a group prefetches is a full one, then one step at a time
       const int n_full = (int)(cd.len / kKT);
       int t = 1;
-      // groups of kStages steps whose prefetched tiles are all full ones
       const int groups = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
       if (groups > 0) {
         const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
@@ -391,15 +397,15 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
         bf16x8 vf[2][4];
         load_v(smem, g, 0, vf);   // V^T fragments of tile 0, consumed by the first step
         fixed_loop_asm(o, qf, s, pA, vf, lsum, nshift, koff, voff, dma, kt, vt, uniform_u64(g.ktile),
-                       uniform_u64(g.vtile), lds_wave, alpha, (uint32_t)groups);
+                       uniform_u64(g.vtile), lds_wave, (uint32_t)groups);
         t += groups * kStages;
       }
       for (; t < n_tiles - 1; ++t) {
-        if (t & 1) fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, alpha, hh, s, pA, pB);
-        else fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, alpha, hh, s, pB, pA);
+        if (t & 1) fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, hh, s, pA, pB);
+        else fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, hh, s, pB, pA);
       }
-      if (t & 1) fixed_last(smem, g, t, t % kStages, o, lsum, nshift, alpha, hh, s, pA, pB);
-      else fixed_last(smem, g, t, t % kStages, o, lsum, nshift, alpha, hh, s, pB, pA);
+      if (t & 1) fixed_last(smem, g, t, t % kStages, o, lsum, hh, s, pA, pB);
+      else fixed_last(smem, g, t, t % kStages, o, lsum, hh, s, pB, pA);
     }
   } else {
     for (int t = 0; t < n_tiles; ++t) {
@@ -407,7 +413,8 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       ring_step(const_cast<uint8_t*>(smem), g, t, stage);
       f32x16 s[2];
       bf16x8 p[2][2];
-      compute_s(smem, g, stage, qf, s);
+      const float zero[2] = {0.0f, 0.0f};
+      compute_s(smem, g, stage, qf, s, zero);
       const int64_t rem = cd.len - (int64_t)t * kKT;
       softmax_online(s, p, lsum, shift, o, a.alpha, rem < kKT ? (int)rem : kKT, hh);
       compute_pv(smem, g, stage, p, o);
@@ -432,7 +439,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   const bool fixed = a.elig[bq] != 0;
   const int mshift = a.m[bq];
 
-  // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean
+  // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean.
+  // The fixed-m body takes its logits in base 2 straight from the MFMA: its query fragments
+  // are bf16(alpha q) (fp32 product, one rounding: the base-2 rescale of Q that the TPU path
+  // folds into Q's producer, [FM] Summary "Relayout optimization") and c_i = (alpha q_i) .
+  // k_mean.  The online body keeps q and scales its scores by alpha.
   bf16x8 qf[2][8];
   float cdot[2];
   const float* km = a.k_mean + (int64_t)bh * kD;
@@ -445,8 +456,16 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * hh);
-      __builtin_memcpy(&qf[n][kk], &w, 16);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      if (fixed) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x2 x = {__uint_as_float(u[i] << 16) * a.alpha, __uint_as_float(u[i] & 0xffff0000u) * a.alpha};
+          const bf16x2 y = __builtin_convertvector(x, bf16x2);
+          __builtin_memcpy(&u[i], &y, 4);
+        }
+      }
+      __builtin_memcpy(&qf[n][kk], u, 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         dot = __builtin_fmaf(__uint_as_float(u[i] << 16), km[16 * kk + 8 * hh + 2 * i], dot);
@@ -474,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   float shift[2];
   if (fixed) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + a.alpha * cdot[n];
+    for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + cdot[n];
     run_chunk<true>(a, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;

@@ -11,31 +11,42 @@ work behind one half of the MFMAs.  Here the register classes and the instructio
 are fixed by hand:
 
   AGPR  a[0:127]    O^T accumulators o[n][m]      (n: 32-query tile, m: 32-dim tile)
-        a[128:191]  resident query fragments q[n][kk]
-        a[192:255]  K fragments, double buffered by tile parity
+        a[128:191]  resident query fragments q[n][kk] (pre-scaled by alpha, see below)
+        a[192:223]  K fragments of the next tile
+        a[224:255]  V^T fragments of even tiles
   VGPR  v[0:63]     S^T scores, double buffered by tile parity (v[32:63] holds the odd tiles)
         v[64:95]    packed bf16 probabilities P, double buffered (v[64:79] even tiles)
-        v[96:159]   V^T fragments, double buffered (v[96:127] even tiles)
+        v[96:127]   16 copies each of -(m + c_i) for the two query tiles: the initial
+                    accumulator of the S MFMAs, so S arrives as the fixed-m exponent
+        v[128:159]  V^T fragments of odd tiles
         v160-161    row sums l[n];  v162-163  -(m + c_i) per query column
-        v180-187    temporaries of the row-sum unpacking
         v164-171    K fragment LDS addresses;  v172-175  V^T fragment LDS addresses
         v176-179    DMA lane offsets (K row 0/1, V row 0/1)
+        v180-187    temporaries of the row-sum unpacking
   SGPR  s[60:61] next K tile address, s[62:63] next V tile address, s[64:65] / s[66:67]
-        bytes between tiles, s68 this wave's LDS DMA base, s69 alpha, s70 group count
+        bytes between tiles, s68 this wave's LDS DMA base, s70 group count
+
+The query fragments hold bf16(alpha q) (alpha = softmax scale x log2 e, applied in fp32 and
+rounded once: the base-2 logit rescale of Q that the TPU path folds into Q's producer, in
+"feat(attention): fixed-m splash attention kernel with dynamic bounds and safety
+fallbacks", Summary, "Relayout optimization"), and c_i = (alpha q_i) . k_mean, so the exponent of the fixed-m body is
+K (alpha Q)^T - (m + c_i): the MFMA chain starts from -(m + c_i) and the VALU work per score
+is one exp2.
 
 One step handles tile t (its stage in the 8-deep LDS ring is static inside the unrolled
 group of 8 steps):
   wait for this wave's part of tile t+1, barrier; then 16 MFMAs O += V(t-1) P(t-1) and 16
-  MFMAs S(t+1) = K(t+1) Q^T, with the 144 VALU instructions that turn S(t) into P(t) and
-  the row sums spread over all 32, the K(t+1) fragment reads and the DMA of tile t+6 (into
-  the stage tile t-2 used) between the first PV MFMAs, and the 16 LDS transpose reads of
-  V(t) (used next step) in the first half of the S MFMAs.
+  MFMAs S(t+1) = K(t+1) Q^T - (m + c), with the 112 VALU instructions that turn S(t) into
+  P(t) and the row sums spread over all 32, the K(t+1) fragment reads and the DMA of tile
+  t+6 (into the stage tile t-2 used) between the first PV MFMAs, and the 16 LDS transpose
+  reads of V(t) (used next step) in the first half of the S MFMAs.
 
 Measured choices (shader-clock cycles per step, s_memtime-instrumented builds on gfx950):
 issuing the K reads and the DMA as a block after the barrier left the matrix cores idle
 (-7.5% when spread between the MFMAs); summing the bf16 pairs with v_dot2c_f32_bf16 costs
 ~9 cycles of matrix-core time per instruction, while unpacking each pair with a shift and a
-mask and adding in fp32 (four plain VALU ops) overlaps the MFMAs (-3.7%).
+mask and adding in fp32 (four plain VALU ops) overlaps the MFMAs (-3.7%); the per-score
+v_fma_f32 that applied alpha and the shift cost ~3 cycles each (-6.5% without it).
 
 Hazards the assembler does not resolve are covered by construction and checked here:
   * a VALU read of an MFMA result (S) waits >= 12 wait states after the producing MFMA
@@ -58,10 +69,10 @@ TILE_BYTES = 8192
 V_RING = STAGES * TILE_BYTES          # the V ring starts 64 KB into the shared buffer
 DMA_WAIT = (AHEAD - 2) * 4            # DMA instructions allowed in flight at a step start
 
-O_BASE, Q_BASE, K_BASE = 0, 128, 192
-S_BASE, P_BASE, V_BASE = 0, 64, 96
+O_BASE, Q_BASE, K_BASE, V0_ABASE = 0, 128, 192, 224
+S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
 LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
-S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_ALPHA, S_CNT = 60, 62, 64, 66, 68, 69, 70
+S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT = 60, 62, 64, 66, 68, 70
 TMP = 180                             # v180-v187: bf16 -> f32 unpacking temporaries
 
 
@@ -82,7 +93,9 @@ def q_reg(n, kk):
 
 
 def k_reg(buf, kk):
-    return areg(K_BASE + 32 * buf + 4 * kk, 4)
+    # single buffer: K(t+1) is read after step t's barrier, when the S MFMAs of step t-1
+    # (the last readers of K(t)) have long been issued
+    return areg(K_BASE + 4 * kk, 4)
 
 
 def s_first(buf, n):
@@ -93,8 +106,17 @@ def p_first(buf, n):
     return P_BASE + 16 * buf + 8 * n
 
 
-def v_first(buf, st, m):
-    return V_BASE + 32 * buf + 4 * (4 * st + m)
+def v_frag(buf, st, m, half=None):
+    """V^T fragment (st, m) of the tile parity `buf`: even tiles in AGPRs a[224:255], odd
+    tiles in VGPRs v[128:159]; `half` selects the 2-register half one transpose read fills."""
+    first = (V0_ABASE if buf == 0 else V1_VBASE) + 4 * (4 * st + m)
+    mk = areg if buf == 0 else vreg
+    return mk(first, 4) if half is None else mk(first + 2 * half, 2)
+
+
+def shift_reg(n):
+    """16 copies of -(m + c_i) for query tile n: the initial accumulator of the S MFMAs."""
+    return vreg(SHIFT_BASE + 16 * n, 16)
 
 
 def softmax_ops(buf):
@@ -103,10 +125,6 @@ def softmax_ops(buf):
     several slots apart.  Each op is (text, whether it reads the scores buffer)."""
     ops = []
     for g in range(4):
-        for n in range(2):
-            for r in range(4 * g, 4 * g + 4):
-                x = s_first(buf, n) + r
-                ops.append((f"v_fma_f32 v{x}, s{S_ALPHA}, v{x}, v{NSHIFT + n}", True))
         for n in range(2):
             for r in range(4 * g, 4 * g + 4):
                 x = s_first(buf, n) + r
@@ -127,7 +145,7 @@ def softmax_ops(buf):
                 ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n}", False))
             for n in range(2):
                 ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n + 1}", False))
-    assert len(ops) == 144
+    assert len(ops) == 112
     return ops
 
 
@@ -199,7 +217,7 @@ def step(e: Emitter, jj: int):
     for st in range(2):
         for m in range(4):
             for n in range(2):
-                vf = vreg(v_first(prv, st, m), 4)
+                vf = v_frag(prv, st, m)
                 p = vreg(p_first(prv, n) + 4 * st, 4)
                 e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
                 if extra:
@@ -214,13 +232,13 @@ def step(e: Emitter, jj: int):
     for kk in range(8):
         for n in range(2):
             s0 = s_first(prv, n)
-            src_c = "0" if kk == 0 else vreg(s0, 16)
+            src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
             e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(prv, kk)}, {q_reg(n, kk)}, {src_c}",
                    writes_sbuf=prv)
             if ti < len(tr):
                 for _ in range(2):
                     st, m, h = tr[ti]
-                    dst = vreg(v_first(cur, st, m) + 2 * h, 2)
+                    dst = v_frag(cur, st, m, h)
                     off = stage_t * TILE_BYTES + 4096 * st + 2048 * h
                     e.emit(f"ds_read_b64_tr_b16 {dst}, v{VOFF + m} offset:{off}")
                     ti += 1
@@ -230,6 +248,9 @@ def step(e: Emitter, jj: int):
 
 def generate() -> str:
     e = Emitter()
+    for n in range(2):
+        for i in range(16):
+            e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, v{NSHIFT + n}")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
     e.lines.append("L_fixedm_group_%=:")
@@ -256,7 +277,7 @@ def generate() -> str:
             outs.append(f'"+{{{vreg(p_first(0, n) + 4 * st, 4)}}}"(p[{n}][{st}])')
     for st in range(2):
         for m in range(4):
-            outs.append(f'"+{{{vreg(v_first(0, st, m), 4)}}}"(vf[{st}][{m}])')
+            outs.append(f'"+{{{v_frag(0, st, m)}}}"(vf[{st}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
              f'"+{{s{S_CNT}}}"(groups)']
@@ -269,10 +290,10 @@ def generate() -> str:
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
     ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
     ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
-            f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s{S_ALPHA}}}"(alpha)']
+            f'"{{s{S_LDS}}}"(lds_wave)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
-            + [f"v{i}" for i in range(V_BASE + 32, V_BASE + 64)] + [f"v{i}" for i in range(TMP, TMP + 8)]
-            + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
+            + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
+            + [f"v{i}" for i in range(TMP, TMP + 8)] + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
             + ["scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
@@ -289,7 +310,7 @@ __device__ __attribute__((always_inline)) inline void fixed_loop_asm(
     f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], f32x16 (&s)[2], bf16x8 (&p)[2][2], bf16x8 (&vf)[2][4],
     float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
     const uint32_t (&dma)[4], uint64_t kt, uint64_t vt, uint64_t ktile, uint64_t vtile, uint32_t lds_wave,
-    float alpha, uint32_t groups) {{
+    uint32_t groups) {{
   asm volatile(
 {body}
       : {join(outs)}
