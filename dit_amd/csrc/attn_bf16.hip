@@ -123,16 +123,19 @@ struct Ring {
 
 // Issues this wave's share (4 rows of K and 4 of V, 1 KB each) of tile t into LDS stage
 // `stage`.  Lane L of instruction i lands at row 4 (2 w + i) + L / 16, physical chunk
-// L % 16, and fetches the logical chunk the swizzle puts there.  Tiles that reach past the
-// chunk's end re-read its last row for the missing keys (masked later).
-// kFull: the caller guarantees the tile lies wholly inside the chunk.
-template <bool kFull = false>
+// L % 16, and fetches the logical chunk the swizzle puts there.  Tile t holds the 32 keys
+// from min(32 t, len - 32): the partial last tile is loaded as the chunk's last 32-key window
+// and tiles past the end repeat it, so every load is one in-bounds tile-wide window (the
+// rows that are not new keys are masked when the scores are formed).  A chunk shorter than
+// one tile clamps each row to the last key instead.
 __device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const Ring& g, int t, int stage) {
   lds_u8* kl = (lds_u8*)(smem + stage * kTileBytes);
   lds_u8* vl = (lds_u8*)(smem + kVRing + stage * kTileBytes);
-  if (kFull || (int64_t)(t + 1) * kKT <= g.len) {
-    const uint64_t kt = uniform_u64(g.kbase + (uint64_t)t * g.ktile);
-    const uint64_t vt = uniform_u64(g.vbase + (uint64_t)t * g.vtile);
+  if (g.len >= kKT) {
+    int64_t row0 = (int64_t)t * kKT;
+    if (row0 > g.len - kKT) row0 = g.len - kKT;
+    const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(row0 * g.k_ss * 2));
+    const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(row0 * g.v_ss * 2));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
@@ -143,7 +146,7 @@ __device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const R
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
-      int64_t key = (int64_t)t * kKT + g.row[i];
+      int64_t key = g.row[i];
       if (key >= g.len) key = g.len - 1;
       dma16_vaddr((const void*)(g.kbase + (uint64_t)(key * g.k_ss * 2) + 16 * g.ck[i]), kl + blk);
       dma16_vaddr((const void*)(g.vbase + (uint64_t)(key * g.v_ss * 2) + 16 * g.cv[i]), vl + blk);
@@ -151,12 +154,27 @@ __device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const R
   }
 }
 
+// Key index within the tile held by accumulator register r of this lane.
+__device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// Rows of tile t that hold keys not yet counted: [lo, hi) (see issue_tile).
+struct RowRange {
+  int lo, hi;
+};
+__device__ inline RowRange tile_rows(const Ring& g, int t) {
+  if (g.len < kKT) return {0, (int)g.len};
+  const int64_t n_full = g.len / kKT, rem = g.len - n_full * kKT;
+  if (t < n_full) return {0, kKT};
+  if (t == n_full && rem > 0) return {kKT - (int)rem, kKT};
+  return {kKT, kKT};
+}
+
 // S^T(tile) = K(tile) Q^T + init for one 32-key tile and two 32-query tiles: 16 MFMAs.  The
 // fixed-m body starts the chain from -(m + c_i) so S arrives as the exponent; the online
-// body starts from 0.
+// body starts from 0.  Rows of the tile outside `rows` start from -inf (p = 0).
 __device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const Ring& g, int stage,
                                                          const bf16x8 (&qf)[2][8], f32x16 (&s)[2],
-                                                         const float (&init)[2]) {
+                                                         const float (&init)[2], RowRange rows, int hh) {
   const uint8_t* ks = smem + stage * kTileBytes;
   bf16x8 kf[8];
 #pragma unroll
@@ -165,7 +183,10 @@ __device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, co
 #pragma unroll
   for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[n][r] = init[n];
+    for (int r = 0; r < 16; ++r) {
+      const int key = tile_key(r, hh);
+      c[n][r] = key >= rows.lo && key < rows.hi ? init[n] : -INFINITY;
+    }
   s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], c[0], 0, 0, 0);
   s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], c[1], 0, 0, 0);
 #pragma unroll
@@ -232,40 +253,32 @@ __device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int 
   return r;
 }
 
-// Key index within the tile held by accumulator register r of this lane.
-__device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
-
 // Fixed-m probabilities of one tile: S already holds the exponent alpha q.k - (m + c_i) (the
-// query fragments are pre-scaled by alpha and the MFMA chain starts from -(m + c_i)), so
-// p = 2^S: no max, no rescale.
-template <bool kPartial>
+// query fragments are pre-scaled by alpha and the MFMA chain starts from -(m + c_i), or
+// from -inf for masked rows), so p = 2^S: no max, no rescale.
 __device__ __attribute__((always_inline)) void softmax_fixed(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
-                                                             float (&lsum)[2], int valid, int hh) {
+                                                             float (&lsum)[2]) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     f32x16 e;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[n][r];
-      if (kPartial && tile_key(r, hh) >= valid) x = -INFINITY;
-      e[r] = __builtin_amdgcn_exp2f(x);
-    }
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[n][r]);
     p[n][0] = pack8_sum(e, 0, lsum[n]);
     p[n][1] = pack8_sum(e, 8, lsum[n]);
   }
 }
 
 // Online-softmax probabilities of one tile (the fallback body): raise the running max,
-// rescale the accumulator and the row sum, then exponentiate against the new max.
+// rescale the accumulator and the row sum, then exponentiate against the new max.  Masked
+// rows arrive as -inf scores (every tile this body visits has at least one real key).
 __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
                                                               float (&lsum)[2], float (&rmax)[2],
-                                                              f32x16 (&o)[2][4], float alpha, int valid,
-                                                              int hh) {
+                                                              f32x16 (&o)[2][4], float alpha) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tile_key(r, hh) < valid ? s[n][r] : -INFINITY);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float rn = fmaxf(rmax[n], alpha * mx);
     const float f = __builtin_amdgcn_exp2f(rmax[n] - rn);
@@ -275,10 +288,7 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
     for (int m = 0; m < 4; ++m) o[n][m] *= f;
     f32x16 e;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = tile_key(r, hh) < valid ? __builtin_fmaf(alpha, s[n][r], -rn) : -INFINITY;
-      e[r] = __builtin_amdgcn_exp2f(x);
-    }
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -rn));
     p[n][0] = pack8_sum(e, 0, lsum[n]);
     p[n][1] = pack8_sum(e, 8, lsum[n]);
   }
@@ -288,39 +298,25 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
 // one workgroup meet at the same barriers: wait for this wave's part of tile t+1, meet the
 // other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
 // loading tile t+kAhead into stage t-2.
-template <bool kFull = false>
 __device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ring& g, int t, int stage) {
   wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
   barrier();
-  issue_tile<kFull>(smem, g, t + kAhead, (stage + kAhead) % kStages);
+  issue_tile(smem, g, t + kAhead, (stage + kAhead) % kStages);
 }
 
-// Fixed-m step for a full middle tile t (1 <= t <= n_tiles - 2) whose ring stage is
-// `stage`.  Phase 1: the 16 MFMAs of O += V(t-1) P(t-1) run while the VALUs turn S(t)
-// into P(t); phase 2: the 16 MFMAs of S(t+1) = K(t+1) Q^T - (m + c) overwrite S.
-template <bool kFull = false>
-__device__ __attribute__((always_inline)) void fixed_mid(const uint8_t* smem, const Ring& g, int t, int stage,
-                                                         const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
-                                                         float (&lsum)[2], const float (&init)[2], int hh,
-                                                         f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
-                                                         bf16x8 (&p_cur)[2][2]) {
-  ring_step<kFull>(const_cast<uint8_t*>(smem), g, t, stage);
-  compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
-  softmax_fixed<false>(s, p_cur, lsum, kKT, hh);
-  compute_s(smem, g, (stage + 1) % kStages, qf, s, init);
-}
-
-// Last tile t = n_tiles - 1 >= 1 (possibly partial): O += V(t-1) P(t-1); P(t); O += V(t) P(t).
-__device__ __attribute__((always_inline)) void fixed_last(const uint8_t* smem, const Ring& g, int t, int stage,
-                                                          f32x16 (&o)[2][4], float (&lsum)[2], int hh,
-                                                          const f32x16 (&s)[2], bf16x8 (&p_prev)[2][2],
-                                                          bf16x8 (&p_cur)[2][2]) {
-  ring_step(const_cast<uint8_t*>(smem), g, t, stage);
-  compute_pv(smem, g, (stage + kStages - 1) % kStages, p_prev, o);
-  const int valid = (int)(g.len - (int64_t)t * kKT);
-  if (valid >= kKT) softmax_fixed<false>(s, p_cur, lsum, kKT, hh);
-  else softmax_fixed<true>(s, p_cur, lsum, valid, hh);
-  compute_pv(smem, g, stage, p_cur, o);
+// Steps of the fixed-m assembly loop for a chunk of n_tiles >= 2 tiles: fast groups while every
+// tile they prefetch and score is a full one, then tail groups through the last tile and
+// past it (the steps past the end see only masked keys).  The online body takes the same
+// number of ring steps so both bodies meet at the same barriers.
+struct FixedSchedule {
+  int fast, tail, steps;
+};
+__device__ inline FixedSchedule fixed_schedule(int64_t len) {
+  const int n_tiles = (int)((len + kKT - 1) / kKT), n_full = (int)(len / kKT);
+  if (n_tiles < 2) return {0, 0, 0};
+  const int fast = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
+  const int tail = (n_tiles - kStages * fast + kStages - 1) / kStages;
+  return {fast, tail, kStages * (fast + tail)};
 }
 
 template <bool kFixed>
@@ -360,6 +356,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
     }
   }
   const int n_tiles = (int)((cd.len + kKT - 1) / kKT);
+  const FixedSchedule sched = fixed_schedule(cd.len);
 #pragma unroll
   for (int t = 0; t < kAhead; ++t) issue_tile(const_cast<uint8_t*>(smem), g, t, t);
   wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
@@ -367,58 +364,52 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   if (kFixed) {
     const float nshift[2] = {-shift[0], -shift[1]};
     f32x16 s[2];
-    bf16x8 pA[2][2], pB[2][2];   // P(t) lives in pA for even t, pB for odd t
-    compute_s(smem, g, 0, qf, s, nshift);
+    bf16x8 p[2][2];
+    compute_s(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
     ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
+    softmax_fixed(s, p, lsum);
     if (n_tiles == 1) {
-      const int valid = (int)cd.len;
-      if (valid >= kKT) softmax_fixed<false>(s, pA, lsum, kKT, hh);
-      else softmax_fixed<true>(s, pA, lsum, valid, hh);
-      compute_pv(smem, g, 0, pA, o);
+      compute_pv(smem, g, 0, p, o);
     } else {
-      softmax_fixed<false>(s, pA, lsum, kKT, hh);
-      compute_s(smem, g, 1, qf, s, nshift);
-      // middle tiles 1 .. n_tiles-2: groups of kStages steps (the assembly loop) while every
-      // tile a group prefetches is a full one, then one step at a time
-      const int n_full = (int)(cd.len / kKT);
-      int t = 1;
-      const int groups = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
-      if (groups > 0) {
-        const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
-        uint32_t koff[8], voff[4];
+      // tiles 1 .. n_tiles-1 and the PV product of the last one: the assembly loop
+      compute_s(smem, g, 1, qf, s, nshift, tile_rows(g, 1), hh);
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
+      uint32_t koff[8], voff[4];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) koff[kk] = lds0 + g.koff[kk];
+      for (int kk = 0; kk < 8; ++kk) koff[kk] = lds0 + g.koff[kk];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
-        const uint32_t dma[4] = {g.kdma[0], g.kdma[1], g.vdma[0], g.vdma[1]};
-        const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * g.wave);
-        const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(1 + kAhead) * g.ktile);
-        const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(1 + kAhead) * g.vtile);
-        bf16x8 vf[2][4];
-        load_v(smem, g, 0, vf);   // V^T fragments of tile 0, consumed by the first step
-        fixed_loop_asm(o, qf, s, pA, vf, lsum, nshift, koff, voff, dma, kt, vt, uniform_u64(g.ktile),
-                       uniform_u64(g.vtile), lds_wave, (uint32_t)groups);
-        t += groups * kStages;
-      }
-      for (; t < n_tiles - 1; ++t) {
-        if (t & 1) fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, hh, s, pA, pB);
-        else fixed_mid(smem, g, t, t % kStages, qf, o, lsum, nshift, hh, s, pB, pA);
-      }
-      if (t & 1) fixed_last(smem, g, t, t % kStages, o, lsum, hh, s, pA, pB);
-      else fixed_last(smem, g, t, t % kStages, o, lsum, hh, s, pB, pA);
+      for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
+      const uint32_t dma[4] = {g.kdma[0], g.kdma[1], g.vdma[0], g.vdma[1]};
+      const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * g.wave);
+      // addresses of tile 1 + kAhead and of the chunk's last 32-key window (issue_tile's rule)
+      const int64_t last_row = g.len - kKT;
+      const int64_t row7 = (int64_t)(1 + kAhead) * kKT < last_row ? (int64_t)(1 + kAhead) * kKT : last_row;
+      const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(row7 * g.k_ss * 2));
+      const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(row7 * g.v_ss * 2));
+      const uint64_t k_last = uniform_u64(g.kbase + (uint64_t)(last_row * g.k_ss * 2));
+      const uint64_t v_last = uniform_u64(g.vbase + (uint64_t)(last_row * g.v_ss * 2));
+      const int n_full = (int)(g.len / kKT), rem = (int)(g.len - (int64_t)n_full * kKT);
+      bf16x8 vf[2][4];
+      load_v(smem, g, 0, vf);   // V^T fragments of tile 0, consumed by the first step
+      fixed_loop_asm(o, qf, s, p, vf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt, vt,
+                     uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last, (uint32_t)n_full,
+                     (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast, (uint32_t)sched.tail,
+                     (uint32_t)(kStages * sched.fast + 2));
     }
   } else {
+    const float zero[2] = {0.0f, 0.0f};
     for (int t = 0; t < n_tiles; ++t) {
       const int stage = t % kStages;
       ring_step(const_cast<uint8_t*>(smem), g, t, stage);
       f32x16 s[2];
       bf16x8 p[2][2];
-      const float zero[2] = {0.0f, 0.0f};
-      compute_s(smem, g, stage, qf, s, zero);
-      const int64_t rem = cd.len - (int64_t)t * kKT;
-      softmax_online(s, p, lsum, shift, o, a.alpha, rem < kKT ? (int)rem : kKT, hh);
+      compute_s(smem, g, stage, qf, s, zero, tile_rows(g, t), hh);
+      softmax_online(s, p, lsum, shift, o, a.alpha);
       compute_pv(smem, g, stage, p, o);
     }
+    // the fixed-m waves of this workgroup run sched.steps assembly steps after two prologue
+    // ring steps: take the same number of barriers (and keep loading the ring)
+    for (int t = n_tiles; t < sched.steps + 1; ++t) ring_step(const_cast<uint8_t*>(smem), g, t, t % kStages);
   }
   wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is released
   barrier();
@@ -436,8 +427,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   const int qlast = q0 < a.Sq ? q0 : a.Sq - 1;
   const int beta = qlast / a.q_block;
   const int64_t bq = (int64_t)bh * a.nqb + beta;
-  const bool fixed = a.elig[bq] != 0;
-  const int mshift = a.m[bq];
+  // The body is chosen per wave: make the choice visibly wave-uniform (a scalar branch), so
+  // no wave steps through the other body's code with an empty exec mask (that code holds
+  // barriers and assembly that keeps its state in fixed registers).
+  const bool fixed = __builtin_amdgcn_readfirstlane((int)a.elig[bq]) != 0;
+  const int mshift = __builtin_amdgcn_readfirstlane(a.m[bq]);
 
   // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean.
   // The fixed-m body takes its logits in base 2 straight from the MFMA: its query fragments

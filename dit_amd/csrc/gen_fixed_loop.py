@@ -72,7 +72,9 @@ DMA_WAIT = (AHEAD - 2) * 4            # DMA instructions allowed in flight at a 
 O_BASE, Q_BASE, K_BASE, V0_ABASE = 0, 128, 192, 224
 S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
 LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
-S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT = 60, 62, 64, 66, 68, 70
+S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
+S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
+KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
 TMP = 180                             # v180-v187: bf16 -> f32 unpacking temporaries
 
 
@@ -171,8 +173,10 @@ class Emitter:
         self.count += 1
 
 
-def step(e: Emitter, jj: int):
-    """Step jj of the unrolled group: tile t with t = 1 + jj (mod 8)."""
+def step(e: Emitter, jj: int, tail: bool):
+    """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).  A tail step clamps its
+    DMA to the chunk's last 32-key window and masks the keys of the next tile that are not
+    real, so steps past the chunk's end (and the partial last tile) run the same code."""
     t_mod = 1 + jj
     cur = t_mod % 2            # parity of t: S(t), P(t), V(t) buffers
     prv = 1 - cur              # parity of t-1 (= parity of t+1)
@@ -190,14 +194,23 @@ def step(e: Emitter, jj: int):
     # by at least one instruction, the wait state that hazard needs.
     kreads = [f"ds_read_b128 {k_reg(prv, kk)}, v{KOFF + kk} offset:{stage_next * TILE_BYTES}" for kk in range(8)]
     extra = []
+    if tail:
+        # tile t+6 may be the partial last tile or lie past the end: clamp its address to the
+        # start of the chunk's last 32-key window before the DMA reads it
+        clamp = []
+        for ptr, last in ((S_KT, S_KLAST), (S_VT, S_VLAST)):
+            clamp += [f"s_sub_u32 s{S_TMP}, s{last}, s{ptr}", f"s_subb_u32 s{S_TMP + 1}, s{last + 1}, s{ptr + 1}",
+                      f"s_cselect_b64 s[{ptr}:{ptr + 1}], s[{last}:{last + 1}], s[{ptr}:{ptr + 1}]"]
+        for ins in clamp:
+            e.emit(ins)
     for i in range(2):
         for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, S_KT),
                                     (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, S_VT)):
             extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", kreads.pop(0),
                           f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
     extra += [[kr] for kr in kreads]
-    extra.append([f"s_add_u32 s{S_KT}, s{S_KT}, s{S_KTILE}", f"s_addc_u32 s{S_KT + 1}, s{S_KT + 1}, s{S_KTILE + 1}"])
-    extra.append([f"s_add_u32 s{S_VT}, s{S_VT}, s{S_VTILE}", f"s_addc_u32 s{S_VT + 1}, s{S_VT + 1}, s{S_VTILE + 1}"])
+    for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE)):
+        extra.append([f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"])
 
     valu = softmax_ops(cur)
     vi = 0
@@ -213,7 +226,7 @@ def step(e: Emitter, jj: int):
             vi += 1
         slot += 1
 
-    # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first ten MFMAs
+    # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first MFMAs
     for st in range(2):
         for m in range(4):
             for n in range(2):
@@ -225,7 +238,23 @@ def step(e: Emitter, jj: int):
                         e.emit(ins)
                 valu3()
     assert not extra
-    # S(t+1) = K(t+1) Q^T, with the V(t) transpose reads in the first half
+    if tail:
+        # Initial accumulator of S(t+1): -(m + c_i) for the real keys of tile j = t+1, -inf for
+        # the others.  Real keys of tile j sit in rows >= lo: lo = 0 for a full tile, 32 - rem
+        # for the partial last tile (loaded as the chunk's last 32-key window), 32 past the end.
+        e.emit(f"s_cmp_eq_u32 s{S_J}, s{S_NFULL}")
+        e.emit(f"s_cselect_b32 s{S_LO}, s{S_LOPART}, 32")
+        e.emit(f"s_cmp_lt_u32 s{S_J}, s{S_NFULL}")
+        e.emit(f"s_cselect_b32 s{S_LO}, 0, s{S_LO}")
+        e.emit(f"s_add_u32 s{S_J}, s{S_J}, 1")
+        e.emit(f"v_sub_u32 v{MASK_X}, s{S_LO}, v{KB4}")         # lo - 4 (lane / 32)
+        for r in range(16):
+            key = 8 * (r >> 2) + (r & 3)                          # row of register r, lane half 0
+            e.emit(f"v_cmp_lt_i32_e32 vcc, {key}, v{MASK_X}")
+            for n in range(2):
+                e.emit(f"v_cndmask_b32_e32 v{SHIFT_BASE + 16 * n + r}, v{NSHIFT + n}, v{NEG_INF}, vcc")
+        e.emit("s_nop 1")
+    # S(t+1) = K(t+1) Q^T - (m + c), with the V(t) transpose reads in the first half
     e.emit("s_waitcnt lgkmcnt(0)")
     tr = [(st, m, h) for st in range(2) for m in range(4) for h in range(2)]
     ti = 0
@@ -251,16 +280,28 @@ def generate() -> str:
     for n in range(2):
         for i in range(16):
             e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, v{NSHIFT + n}")
+    e.emit(f"v_mov_b32 v{NEG_INF}, 0xff800000")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
+    e.emit(f"s_cmp_eq_u32 s{S_CNT}, 0")
+    e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
+    # fast groups: every tile they prefetch and every S tile they compute is a full one
     e.lines.append("L_fixedm_group_%=:")
     # the loop's back edge: the previous group's last S MFMAs may be a few instructions away
     e.s_written = {0: e.count - 1, 1: e.count - 1}
     for jj in range(STAGES):
-        step(e, jj)
+        step(e, jj, tail=False)
     e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
     e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_group_%=")
+    # tail groups: clamped DMA and masked keys, through the chunk's last tile and past it
+    e.lines.append("L_fixedm_tail_%=:")
+    e.s_written = {0: e.count - 1, 1: e.count - 1}
+    for jj in range(STAGES):
+        step(e, jj, tail=True)
+    e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
+    e.emit(f"s_cmp_lg_u32 s{S_TCNT}, 0")
+    e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
     e.emit("s_waitcnt lgkmcnt(0)")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
@@ -280,7 +321,7 @@ def generate() -> str:
             outs.append(f'"+{{{v_frag(0, st, m)}}}"(vf[{st}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
-             f'"+{{s{S_CNT}}}"(groups)']
+             f'"+{{s{S_CNT}}}"(groups)', f'"+{{s{S_TCNT}}}"(tail_groups)', f'"+{{s{S_J}}}"(next_tile)']
     ins = []
     for n in range(2):
         for kk in range(8):
@@ -289,28 +330,35 @@ def generate() -> str:
     ins += [f'"{{v{KOFF + kk}}}"(koff[{kk}])' for kk in range(8)]
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
     ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
+    ins += [f'"{{v{KB4}}}"(kb4)']
     ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
-            f'"{{s{S_LDS}}}"(lds_wave)']
+            f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s[{S_KLAST}:{S_KLAST + 1}]}}"(k_last)',
+            f'"{{s[{S_VLAST}:{S_VLAST + 1}]}}"(v_last)', f'"{{s{S_NFULL}}}"(n_full)', f'"{{s{S_LOPART}}}"(lo_part)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
-            + [f"v{i}" for i in range(TMP, TMP + 8)] + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
-            + ["scc", "memory"])
+            + [f"v{i}" for i in range(TMP, TMP + 8)] + [f"v{NEG_INF}", f"v{MASK_X}"]
+            + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
+            + [f"s{S_LO}", f"s{S_TMP}", f"s{S_TMP + 1}", "vcc", "scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
     def join(items):
         return ",\n        ".join(items)
 
     return f"""// Generated by gen_fixed_loop.py; do not edit by hand.
-// The steady-state fixed-m loop: `groups` groups of 8 pipelined 32-key steps, tiles
-// t0 .. t0 + 8 groups - 1 with t0 = 1 (mod 8).  On entry: s = S(t0) (odd-tile buffer), p =
-// P(t0 - 1), vf = the V^T fragments of tile t0 - 1, kt / vt = the addresses of tile t0 + 6,
-// tiles up to t0 + 5 issued and tile t0 in LDS.  On exit the same invariants hold for
-// t0 + 8 groups; every LDS read has completed.
+// The fixed-m loop of a chunk: `groups` fast groups then `tail_groups` (>= 1) tail groups of
+// 8 pipelined 32-key steps, tiles t0 .. t0 + 8 (groups + tail_groups) - 1 with t0 = 1.  On
+// entry: s = S(t0) (odd-tile buffer, masked like a tail step's), p = P(t0 - 1), vf = the
+// V^T fragments of tile t0 - 1, kt / vt = the addresses of tile t0 + 6 (clamped to the
+// chunk's last 32-key window), tiles up to t0 + 5 issued and tile t0 in LDS, next_tile =
+// t0 + 8 groups + 1 (the tile whose S the first tail step computes).  The steps past the
+// chunk's last tile see only masked keys (p = 0), so the last of them completes the PV
+// product of the last tile.  On exit every LDS read has completed.
 __device__ __attribute__((always_inline)) inline void fixed_loop_asm(
     f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], f32x16 (&s)[2], bf16x8 (&p)[2][2], bf16x8 (&vf)[2][4],
     float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
-    const uint32_t (&dma)[4], uint64_t kt, uint64_t vt, uint64_t ktile, uint64_t vtile, uint32_t lds_wave,
-    uint32_t groups) {{
+    const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt, uint64_t vt, uint64_t ktile, uint64_t vtile,
+    uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full, uint32_t lo_part, uint32_t groups,
+    uint32_t tail_groups, uint32_t next_tile) {{
   asm volatile(
 {body}
       : {join(outs)}

@@ -235,6 +235,32 @@ def test_assembly_loop_boundaries(F, chunks):
     _generic(F, 40 + len(chunks), "bf16", 1, 2, 128, 300, chunks, q_block=64, center="compute")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_no_reads_past_a_chunk(F, dtype):
+    """Every chunk is a view into a larger buffer whose rows past the chunk are NaN: a load
+    past a chunk's last key (or a misplaced last window) would put NaN into the output."""
+    import torch
+    say(f"edge: NaN past each chunk ({dtype})")
+    chunks = (737, 1000, 481, 33)               # last tiles of 1, 8, 1 and 1 keys; fast groups
+    D = 128
+    inp = WL.generic_inputs(45, dtype, 1, 2, D, 200, chunks, q_block=64)
+    q, ks, vs, _ = device_inputs(inp)
+    kp, vp = [], []
+    for k, v in zip(ks, vs):
+        pad = 64
+        kb = torch.full((1, k.shape[1] + pad, 2, D), float("nan"), device="cuda", dtype=k.dtype)
+        vb = torch.full_like(kb, float("nan"))
+        kb[:, :k.shape[1]] = k
+        vb[:, :v.shape[1]] = v
+        kp.append(kb[:, :k.shape[1]])
+        vp.append(vb[:, :v.shape[1]])
+    out, lse, desc, buf = F.forward(q, kp, vp, q_block=64, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(out.cpu().numpy(), ref, dtype)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL[dtype]
+
+
 def test_v_magnitude_forces_fallback(F):
     say("edge: |v| > 256")
     ob, _ = _generic(F, 35, "bf16", 1, 2, 128, 200, (150, 100), q_block=64,
