@@ -19,10 +19,11 @@ are fixed by hand:
         v[96:127]   16 copies each of -(m + c_i) for the two query tiles: the initial
                     accumulator of the S MFMAs, so S arrives as the fixed-m exponent
         v[128:159]  V^T fragments of odd tiles
-        v160-161    row sums l[n];  v162-163  -(m + c_i) per query column
+        v160-161    row sums l[n] (low bf16 halves);  v162-163  -(m + c_i) per query column
         v164-171    K fragment LDS addresses;  v172-175  V^T fragment LDS addresses
         v176-179    DMA lane offsets (K row 0/1, V row 0/1)
-        v180-187    temporaries of the row-sum unpacking
+        v180-185    temporaries of the row-sum unpacking;  v186-187  row sums of the high
+                    bf16 halves (folded into v160-161 when the block ends)
   SGPR  s[60:61] next K tile address, s[62:63] next V tile address, s[64:65] / s[66:67]
         bytes between tiles, s68 this wave's LDS DMA base, s70 group count
 
@@ -37,7 +38,7 @@ One step handles tile t (its stage in the 8-deep LDS ring is static inside the u
 group of 8 steps):
   wait for this wave's part of tile t+1, barrier; then 16 MFMAs O += V(t-1) P(t-1) and 16
   MFMAs S(t+1) = K(t+1) Q^T - (m + c), with the 112 VALU instructions that turn S(t) into
-  P(t) and the row sums spread over all 32, the K(t+1) fragment reads and the DMA of tile
+  P(t) and the row sums placed slot by slot (softmax_plan), the K(t+1) fragment reads and the DMA of tile
   t+6 (into the stage tile t-2 used) between the first PV MFMAs, and the 16 LDS transpose
   reads of V(t) (used next step) in the first half of the S MFMAs.
 
@@ -46,7 +47,11 @@ issuing the K reads and the DMA as a block after the barrier left the matrix cor
 (-7.5% when spread between the MFMAs); summing the bf16 pairs with v_dot2c_f32_bf16 costs
 ~9 cycles of matrix-core time per instruction, while unpacking each pair with a shift and a
 mask and adding in fp32 (four plain VALU ops) overlaps the MFMAs (-3.7%); the per-score
-v_fma_f32 that applied alpha and the shift cost ~3 cycles each (-6.5% without it).
+v_fma_f32 that applied alpha and the shift cost ~3 cycles each (-6.5% without it); one exp
+per MFMA slot with the plain ops a slot or more behind (softmax_plan) instead of groups of
+eight exps: -7.3% (1,485 -> 1,377 cycles a step).  Work-removal builds put the rest: without
+any VALU work a step takes ~1,220 cycles, without the exps ~1,310; moving the transpose reads
+next to the PV MFMAs or doubling up exps after the barrier costs 2-3%.
 
 Hazards the assembler does not resolve are covered by construction and checked here:
   * a VALU read of an MFMA result (S) waits >= 12 wait states after the producing MFMA
@@ -75,7 +80,9 @@ LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
 S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
 S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
 KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
-TMP = 180                             # v180-v187: bf16 -> f32 unpacking temporaries
+TMP = 180                             # v180-v185: bf16 -> f32 unpacking temporaries (3 pairs)
+N_TMP_PAIRS = 3
+LSUM_HI = 186                         # v186-v187: row sums of the high halves
 
 
 def areg(base, n=1):
@@ -121,34 +128,101 @@ def shift_reg(n):
     return vreg(SHIFT_BASE + 16 * n, 16)
 
 
-def softmax_ops(buf):
-    """The 144 VALU instructions turning S(t) (scores buffer `buf`) into P(t) and adding the
-    bf16-rounded probabilities to the row sums, ordered so that dependent instructions are
-    several slots apart.  Each op is (text, whether it reads the scores buffer)."""
-    ops = []
-    for g in range(4):
-        for n in range(2):
-            for r in range(4 * g, 4 * g + 4):
-                x = s_first(buf, n) + r
-                ops.append((f"v_exp_f32 v{x}, v{x}", True))
-        for n in range(2):
-            for i in (2 * g, 2 * g + 1):
-                x = s_first(buf, n) + 2 * i
-                ops.append((f"v_cvt_pk_bf16_f32 v{p_first(buf, n) + i}, v{x}, v{x + 1}", True))
-        # row sums of the bf16-rounded pairs: the low half as f32 is the pair shifted left by
-        # 16, the high half is the pair with its low 16 bits cleared; add low then high
-        for i in (2 * g, 2 * g + 1):
-            for n in range(2):
-                t = TMP + 4 * (i % 2) + 2 * n
-                w = p_first(buf, n) + i
-                ops.append((f"v_lshlrev_b32 v{t}, 16, v{w}", False))
-                ops.append((f"v_and_b32 v{t + 1}, 0xffff0000, v{w}", False))
-            for n in range(2):
-                ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n}", False))
-            for n in range(2):
-                ops.append((f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{TMP + 4 * (i % 2) + 2 * n + 1}", False))
-    assert len(ops) == 112
-    return ops
+# VALU slot plan of a step (one list entry per MFMA slot, 16 PV then 16 S slots):
+#  * exps: one per slot, two in S slot 4 and none in the last slot, so the last pair's
+#    convert and row-sum work still fits in the step;
+#  * budget of plain VALU ops beside the exp: small in the slots that also carry the DMA /
+#    K reads (PV slots 0-9) or the transpose reads (S slots 0-7), none beside two exps,
+#    larger elsewhere; the last slot takes what is left.
+EXP_QUOTA = [1] * 20 + [2] + [1] * 10 + [0]
+SIMPLE_CAP = [1, 1, 1, 1, 3, 3, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 2, 2, 2, 2, 0, 2, 2, 2, 4, 4, 4, 4, 4, 4, 4, 4]
+DEP_DIST = 2                          # a plain VALU op sits >= 2 instructions after its producer
+
+
+def softmax_plan(buf):
+    """The 112 VALU instructions that turn S(t) (scores buffer `buf`) into P(t) and the row
+    sums, placed into the 32 MFMA slots of a step.  Returns 32 lists of (text, whether the
+    instruction reads the scores buffer).
+
+    A v_exp_f32 holds the vector ALU for about half an MFMA, so at most one goes between two
+    MFMAs (bunching them starves the matrix cores: -7% cycles a step for this plan against
+    groups of exps).  Each bf16 pair (word) w of P takes 2 exps, then v_cvt_pk_bf16_f32, then
+    the unpacking of its two halves to fp32 (a shift and a mask) and two row-sum adds.  A
+    consumer of an exp goes in a later slot (a transcendental result needs a wait state
+    before a plain VALU op reads it); other consumers go >= DEP_DIST instructions after their
+    producer, and the low and high halves add into separate accumulators so that the adds of
+    one slot do not depend on each other."""
+    ops = []          # dicts: text, reads (scores buffer), deps, war, acc
+
+    def add(text, reads, deps=(), war=(), acc=None):
+        ops.append(dict(text=text, reads=reads, deps=list(deps), war=list(war), acc=acc))
+        return len(ops) - 1
+
+    exps, word_exps = [], []
+    for w in range(16):
+        n, i = w % 2, w // 2                     # word w: tile n, S registers 2i, 2i+1
+        x = s_first(buf, n) + 2 * i
+        pair = [add(f"v_exp_f32 v{r}, v{r}", True) for r in (x, x + 1)]
+        exps += pair
+        word_exps.append(pair)
+    plain, adds_of = [], {}
+    for w in range(16):
+        n, i = w % 2, w // 2
+        x = s_first(buf, n) + 2 * i
+        pw = p_first(buf, n) + i
+        t = TMP + 2 * (w % N_TMP_PAIRS)
+        war = adds_of.get(w - N_TMP_PAIRS, [])   # the temporaries' previous readers
+        cvt = add(f"v_cvt_pk_bf16_f32 v{pw}, v{x}, v{x + 1}", True, word_exps[w])
+        # the low half as f32 is the pair shifted left by 16, the high half is the pair
+        # with its low 16 bits cleared
+        lo = add(f"v_lshlrev_b32 v{t}, 16, v{pw}", False, [cvt], war)
+        hi = add(f"v_and_b32 v{t + 1}, 0xffff0000, v{pw}", False, [cvt], war)
+        a_lo = add(f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{t}", False, [lo], acc=LSUM + n)
+        a_hi = add(f"v_add_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{t + 1}", False, [hi], acc=LSUM_HI + n)
+        adds_of[w] = [a_lo, a_hi]
+        plain += [cvt, lo, hi, a_lo, a_hi]
+
+    pos = {}                                      # op -> (slot, index in the slot)
+    last_acc = {}
+    plan = [[] for _ in range(32)]
+    ei, pending = 0, list(plain)
+    for s in range(32):
+        for _ in range(EXP_QUOTA[s]):
+            pos[exps[ei]] = (s, len(plan[s]))
+            plan[s].append(exps[ei])
+            ei += 1
+        cap = SIMPLE_CAP[s] if s < 31 else len(pending)
+        dist = DEP_DIST if s < 31 else 1
+        took = 0
+        while took < cap:
+            pick = None
+            for k in pending:
+                o = ops[k]
+                ok = True
+                for d in o["deps"] + o["war"]:
+                    if d not in pos:
+                        ok = False
+                        break
+                    ds, di = pos[d]
+                    if ds == s and (ops[d]["text"].startswith("v_exp") or len(plan[s]) - di < dist):
+                        ok = False
+                        break
+                if ok and o["acc"] in last_acc:
+                    ls, li = last_acc[o["acc"]]
+                    ok = not (ls == s and len(plan[s]) - li < dist)
+                if ok:
+                    pick = k
+                    break
+            if pick is None:
+                break
+            pos[pick] = (s, len(plan[s]))
+            plan[s].append(pick)
+            pending.remove(pick)
+            took += 1
+            if ops[pick]["acc"] is not None:
+                last_acc[ops[pick]["acc"]] = pos[pick]
+    assert ei == 32 and not pending, "VALU plan does not fit the step"
+    return [[(ops[k]["text"], ops[k]["reads"]) for k in sl] for sl in plan]
 
 
 class Emitter:
@@ -212,18 +286,13 @@ def step(e: Emitter, jj: int, tail: bool):
     for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE)):
         extra.append([f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"])
 
-    valu = softmax_ops(cur)
-    vi = 0
-
+    plan = softmax_plan(cur)
     slot = 0
 
-    def valu3():
-        nonlocal vi, slot
-        want = (len(valu) * (slot + 1)) // 32
-        while vi < want:
-            text, reads = valu[vi]
+    def valu_slot():
+        nonlocal slot
+        for text, reads in plan[slot]:
             e.emit(text, reads_sbuf=cur if reads else None)
-            vi += 1
         slot += 1
 
     # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first MFMAs
@@ -236,7 +305,7 @@ def step(e: Emitter, jj: int, tail: bool):
                 if extra:
                     for ins in extra.pop(0):
                         e.emit(ins)
-                valu3()
+                valu_slot()
     assert not extra
     if tail:
         # Initial accumulator of S(t+1): -(m + c_i) for the real keys of tile j = t+1, -inf for
@@ -271,8 +340,8 @@ def step(e: Emitter, jj: int, tail: bool):
                     off = stage_t * TILE_BYTES + 4096 * st + 2048 * h
                     e.emit(f"ds_read_b64_tr_b16 {dst}, v{VOFF + m} offset:{off}")
                     ti += 1
-            valu3()
-    assert vi == len(valu) and ti == 16
+            valu_slot()
+    assert slot == 32 and ti == 16
 
 
 def generate() -> str:
@@ -281,6 +350,8 @@ def generate() -> str:
         for i in range(16):
             e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, v{NSHIFT + n}")
     e.emit(f"v_mov_b32 v{NEG_INF}, 0xff800000")
+    e.emit(f"v_mov_b32 v{LSUM_HI}, 0")
+    e.emit(f"v_mov_b32 v{LSUM_HI + 1}, 0")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
     e.emit(f"s_cmp_eq_u32 s{S_CNT}, 0")
@@ -302,6 +373,8 @@ def generate() -> str:
     e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
     e.emit(f"s_cmp_lg_u32 s{S_TCNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
+    e.emit(f"v_add_f32 v{LSUM}, v{LSUM}, v{LSUM_HI}")
+    e.emit(f"v_add_f32 v{LSUM + 1}, v{LSUM + 1}, v{LSUM_HI + 1}")
     e.emit("s_waitcnt lgkmcnt(0)")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
@@ -336,7 +409,8 @@ def generate() -> str:
             f'"{{s[{S_VLAST}:{S_VLAST + 1}]}}"(v_last)', f'"{{s{S_NFULL}}}"(n_full)', f'"{{s{S_LOPART}}}"(lo_part)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
-            + [f"v{i}" for i in range(TMP, TMP + 8)] + [f"v{NEG_INF}", f"v{MASK_X}"]
+            + [f"v{i}" for i in range(TMP, TMP + 2 * N_TMP_PAIRS)] + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
+            + [f"v{NEG_INF}", f"v{MASK_X}"]
             + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
             + [f"s{S_LO}", f"s{S_TMP}", f"s{S_TMP + 1}", "vcc", "scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
