@@ -156,7 +156,8 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out) {
   out->k_mean = off; off = align256(off + bh * (size_t)p.head_dim * 4);
   out->v_bad = off; off = align256(off + 4);
   out->scratch = off;
-  if (p.center == FIXEDM_CENTER_COMPUTE) off = align256(off + (size_t)kKmeanSlabs * bh * p.head_dim * 8);
+  if (p.center == FIXEDM_CENTER_COMPUTE)
+    off = align256(off + (size_t)kmean_slabs(p.batch, p.heads, p.sk_total) * bh * p.head_dim * 8);
   out->total = off;
   return true;
 }
@@ -170,8 +171,27 @@ bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out) {
   out->acc = off; off = align256(off + rows * (size_t)p.head_dim * 4);
   out->l = off; off = align256(off + rows * 4);
   out->r = off; off = align256(off + rows * 4);
+  out->acc_x = out->l_x = out->r_x = off;
+  if (p.dtype == FIXEDM_BF16) {
+    const int64_t tiles = p.batch * p.heads * out->n_qtiles;
+    const size_t xt = (size_t)(kMaxParts - 1) * (size_t)(tiles < kMaxSplitTail ? tiles : kMaxSplitTail);
+    out->acc_x = off; off = align256(off + xt * kQTile * (size_t)p.head_dim * 4);
+    out->l_x = off; off = align256(off + xt * kQTile * 4);
+    out->r_x = off; off = align256(off + xt * kQTile * 4);
+  }
   out->total = off;
   return true;
+}
+
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
 }
 
 }  // namespace fixedm
@@ -283,6 +303,7 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixe
   a.k_mean = reinterpret_cast<float*>(base + lay.k_mean);
   a.v_bad = reinterpret_cast<int32_t*>(base + lay.v_bad);
   a.kpart = reinterpret_cast<double*>(base + lay.scratch);
+  a.kslabs = kmean_slabs(p->batch, p->heads, p->sk_total);
   if (launch_bounds(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
   *out = d;
   return FIXEDM_OK;
@@ -334,6 +355,13 @@ fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, 
   a.acc = reinterpret_cast<float*>(wbase + wl.acc);
   a.l = reinterpret_cast<float*>(wbase + wl.l);
   a.r = reinterpret_cast<float*>(wbase + wl.r);
+  a.acc_x = reinterpret_cast<float*>(wbase + wl.acc_x);
+  a.l_x = reinterpret_cast<float*>(wbase + wl.l_x);
+  a.r_x = reinterpret_cast<float*>(wbase + wl.r_x);
+  const SplitPlan sp = p.dtype == FIXEDM_BF16 ? split_plan(p.batch * p.heads * wl.n_qtiles, device_cus())
+                                             : SplitPlan{(int32_t)(p.batch * p.heads * wl.n_qtiles), 1};
+  a.n_whole = sp.n_whole;
+  a.parts = sp.parts;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   int64_t visited = run->kv_visited;
@@ -385,6 +413,13 @@ fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t*
   a.B = (int32_t)p.batch; a.H = (int32_t)p.heads; a.D = (int32_t)p.head_dim;
   a.Sq = (int32_t)p.sq; a.n_qtiles = (int32_t)wl.n_qtiles; a.sq_pad = (int32_t)wl.sq_pad;
   a.reg_layout = p.dtype == FIXEDM_BF16 ? 1 : 0;
+  const SplitPlan sp = p.dtype == FIXEDM_BF16 ? split_plan(p.batch * p.heads * wl.n_qtiles, device_cus())
+                                             : SplitPlan{(int32_t)(p.batch * p.heads * wl.n_qtiles), 1};
+  a.n_whole = sp.n_whole;
+  a.parts = sp.parts;
+  a.acc_x = reinterpret_cast<const float*>(wbase + wl.acc_x);
+  a.l_x = reinterpret_cast<const float*>(wbase + wl.l_x);
+  a.r_x = reinterpret_cast<const float*>(wbase + wl.r_x);
   if (launch_finalize(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
   return FIXEDM_OK;
 }

@@ -320,11 +320,11 @@ __device__ inline FixedSchedule fixed_schedule(int64_t len) {
 }
 
 template <bool kFixed>
-__device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, const uint8_t* smem,
-                                                         const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
-                                                         float (&lsum)[2], float (&shift)[2], int b, int h) {
+__device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, const ChunkDesc& cd,
+                                                         const uint8_t* smem, const bf16x8 (&qf)[2][8],
+                                                         f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
+                                                         int b, int h) {
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
-  const ChunkDesc& cd = a.ch[0];
   Ring g;
   g.wave = tid >> 6;
   g.len = cd.len;
@@ -417,7 +417,24 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
 
 __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  const int tile = remap_tile(blockIdx.x, gridDim.x);
+  // Whole tiles first (XCD-remapped), then the parts of the split tail tiles: part p of a
+  // tail tile takes keys [lo_p, lo_{p+1}) of the chunk, lo_p = 32 * floor(len p / (32 parts)).
+  int tile, part = 0;
+  if ((int)blockIdx.x < a.n_whole) {
+    tile = remap_tile(blockIdx.x, a.n_whole);
+  } else {
+    const int u = blockIdx.x - a.n_whole;
+    tile = a.n_whole + u / a.parts;
+    part = u % a.parts;
+  }
+  ChunkDesc cd = a.ch[0];
+  if (a.parts > 1 && tile >= a.n_whole) {
+    const int64_t lo = cd.len * part / a.parts / kKT * kKT;
+    const int64_t hi = part + 1 == a.parts ? cd.len : cd.len * (part + 1) / a.parts / kKT * kKT;
+    cd.k = reinterpret_cast<const uint16_t*>(cd.k) + lo * cd.k_ss;
+    cd.v = reinterpret_cast<const uint16_t*>(cd.v) + lo * cd.v_ss;
+    cd.len = hi - lo;
+  }
   const int qt = tile % a.n_qtiles;
   const int bh = tile / a.n_qtiles;
   const int b = bh / a.H, h = bh % a.H;
@@ -488,31 +505,44 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   if (fixed) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + cdot[n];
-    run_chunk<true>(a, smem, qf, o, lsum, shift, b, h);
+    if (cd.len > 0) run_chunk<true>(a, cd, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;
-    run_chunk<false>(a, smem, qf, o, lsum, shift, b, h);
+    if (cd.len > 0) run_chunk<false>(a, cd, smem, qf, o, lsum, shift, b, h);
   }
 
   // ---- fold into the workspace: acc in register order (one 1 KB coalesced float4 store
-  // per (wave, n, m, j)), l and r per padded query row.  The first visit of a run writes;
-  // later visits add (fixed-m: pure addition) or rescale-merge (online softmax).
-  const int64_t tb = (int64_t)tile * (kQTile * kD);
+  // per (wave, n, m, j)), l and r per padded query row (parts 1.. of a split tile: their own
+  // slots).  The first visit of a run writes; later visits add (fixed-m: pure addition) or
+  // rescale-merge (online softmax; a part that has seen no key yet holds r = -inf, l = 0).
+  float* acc_t = a.acc;
+  float* l_t = a.l;
+  float* r_t = a.r;
+  int64_t tb = (int64_t)tile * (kQTile * kD);
+  int64_t row0 = (int64_t)bh * a.sq_pad + q0;
+  if (part > 0) {
+    const int64_t u = (int64_t)(tile - a.n_whole) * (a.parts - 1) + part - 1;
+    acc_t = a.acc_x;
+    l_t = a.l_x;
+    r_t = a.r_x;
+    tb = u * (kQTile * kD);
+    row0 = u * kQTile + wave * 64;
+  }
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const float other = __shfl_xor(lsum[n], 32, 64);
     const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
-    const int64_t rowi = (int64_t)bh * a.sq_pad + q0 + 32 * n + lq;
+    const int64_t rowi = row0 + 32 * n + lq;
     float lnew = ltot, rnew = shift[n], fw = 0.0f, fo = 1.0f;
     if (a.accumulate) {
-      const float lp = a.l[rowi], rp = a.r[rowi];
+      const float lp = l_t[rowi], rp = r_t[rowi];
       if (fixed) {
         lnew = lp + ltot;
         fw = 1.0f;
       } else {
         rnew = fmaxf(rp, shift[n]);
-        fw = __builtin_amdgcn_exp2f(rp - rnew);
-        fo = __builtin_amdgcn_exp2f(shift[n] - rnew);
+        fw = rp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(rp - rnew);
+        fo = shift[n] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(shift[n] - rnew);
         lnew = lp * fw + ltot * fo;
       }
     }
@@ -520,7 +550,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        f32x4* dst = reinterpret_cast<f32x4*>(a.acc + tb + ((((wave * 2 + n) * 4 + m) * 4 + jj) * 64 + lane) * 4);
+        f32x4* dst = reinterpret_cast<f32x4*>(acc_t + tb + ((((wave * 2 + n) * 4 + m) * 4 + jj) * 64 + lane) * 4);
         f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
         if (a.accumulate) {
           const f32x4 prev = *dst;
@@ -531,8 +561,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
       }
     }
     if (hh == 0) {
-      a.l[rowi] = lnew;
-      a.r[rowi] = rnew;
+      l_t[rowi] = lnew;
+      r_t[rowi] = rnew;
     }
   }
 }
@@ -540,7 +570,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  const int nb = a.B * a.H * a.n_qtiles;
+  const int tiles = a.B * a.H * a.n_qtiles;
+  const int nb = a.n_whole + (tiles - a.n_whole) * a.parts;
   attn_bf16_d128_kernel<<<nb, 256, 0, s>>>(a);
   return hipGetLastError();
 }

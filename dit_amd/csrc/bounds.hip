@@ -52,15 +52,6 @@ __device__ inline int find_chunk(const BoundsArgs& a, int64_t j) {
   return c;
 }
 
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    unsigned long long o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // Clears the reduction targets and fills k_mean for the NONE / SUPPLIED modes.
 __global__ void bounds_init_kernel(BoundsArgs a) {
   const int64_t nqb_all = (int64_t)a.B * a.H * a.nqb;
@@ -78,51 +69,40 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
   }
 }
 
-// Row j of the global key order (chunk by chunk) for this (b, h), in K or in V.
+// Partial key sums for the COMPUTE centring mode.  Workgroup (slab, b, head group): thread
+// (hl, c) owns dims 8c..8c+7 of head h0 + hl and adds the keys of the slab in key order.
+// A key's rows of the whole head group are adjacent in memory, so each key is one
+// contiguous read of the workgroup (10 KB for 40 heads of 128 bf16 dims).
 template <typename T>
-__device__ inline const T* key_row(const BoundsArgs& a, int b, int h, int64_t j, bool v) {
-  const ChunkDesc& cd = a.ch[find_chunk(a, j)];
-  return v ? reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + (j - cd.start) * cd.v_ss + h * cd.v_sh
-           : reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (j - cd.start) * cd.k_ss + h * cd.k_sh;
-}
-
-// Partial key sums for the COMPUTE centring mode: slab s of the global key range, one
-// (b, h) per blockIdx.y.  Thread (rg, c) sums keys rg, rg + nrg, ... of the slab for the
-// 8 dims of column chunk c; the row groups are then added in rg order.
-template <typename T>
-__global__ __launch_bounds__(256) void kmean_partial_kernel(BoundsArgs a) {
-  __shared__ double red[256][8];
-  const int nch = a.D / 8, nrg = 256 / nch;
-  const int rg = threadIdx.x / nch, c = threadIdx.x % nch;
-  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t s0 = a.N * blockIdx.x / kKmeanSlabs, s1 = a.N * (blockIdx.x + 1) / kKmeanSlabs;
+__global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
+  const int per = a.D / 8;
+  const int hl = threadIdx.x / per, c = threadIdx.x % per;
+  const int b = blockIdx.y, h = blockIdx.z * kBoundsHeads + hl;
+  if (h >= a.H) return;
+  const int64_t s0 = a.N * blockIdx.x / a.kslabs, s1 = a.N * (blockIdx.x + 1) / a.kslabs;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  // eight rows in flight per thread; they are added in increasing key order
-  for (int64_t j = s0 + rg; j < s1; j += 8 * nrg) {
+  int ci = 0;                                    // chunk of the current key (uniform)
+  for (int64_t j = s0; j < s1; j += 8) {
     float f[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t jj = j + (int64_t)u * nrg;
-      if (jj < s1) load8(key_row<T>(a, b, h, jj, false) + 8 * c, f[u]);
+      const int64_t jj = j + u;
+      if (jj < s1) {
+        while (ci + 1 < a.n_chunks && jj >= a.ch[ci + 1].start) ++ci;
+        const ChunkDesc& cd = a.ch[ci];
+        load8(reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (jj - cd.start) * cd.k_ss + h * cd.k_sh + 8 * c,
+              f[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j + (int64_t)u * nrg < s1)
+      if (j + u < s1)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[u][i];
   }
+  double* dst = a.kpart + ((int64_t)blockIdx.x * a.B * a.H + (int64_t)b * a.H + h) * a.D + 8 * c;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = acc[i];
-  __syncthreads();
-  if (threadIdx.x < nch) {
-    double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int g = 0; g < nrg; ++g)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = s[i] + red[g * nch + threadIdx.x][i];
-    double* dst = a.kpart + ((int64_t)blockIdx.x * a.B * a.H + bh) * a.D + 8 * threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = s[i];
-  }
+  for (int i = 0; i < 8; ++i) dst[i] = acc[i];
 }
 
 // k_mean[b,h,d] = fp32(sum over slabs in order / N).
@@ -131,7 +111,7 @@ __global__ void kmean_final_kernel(BoundsArgs a) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     double s = 0.0;
-    for (int sl = 0; sl < kKmeanSlabs; ++sl) s = s + a.kpart[(int64_t)sl * n + i];
+    for (int sl = 0; sl < a.kslabs; ++sl) s = s + a.kpart[(int64_t)sl * n + i];
     a.k_mean[i] = (float)(s / (double)a.N);
   }
 }
@@ -174,63 +154,115 @@ __device__ inline double row_sumsq(const RowRegs<T>& r, const float* c, int D) {
   return s;
 }
 
-// 256 keys of one (b, h) per workgroup: K2 = max over keys of sum_d (k_d - k_mean_d)^2
-// (fp64, d in order), and the V-magnitude check on the same keys' value rows.
+// fp64 sum over d in index order of x_d^2.
 template <typename T>
-__global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
-  __shared__ float km[128];
-  __shared__ unsigned long long wmax[4];
-  __shared__ int wbad[4];
-  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x;
-  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
-  if (tid < a.D) km[tid] = a.k_mean[(int64_t)bh * a.D + tid];
-  __syncthreads();
-  unsigned long long best = 0ull;
-  int bad = 0;
-  if (j < a.N) {
-    RowRegs<T> kr, vr;
-    kr.load(key_row<T>(a, b, h, j, false), a.D);
-    vr.load(key_row<T>(a, b, h, j, true), a.D);
-    best = (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km, a.D));
+__device__ inline double row_sumsq(const RowRegs<T>& r, int D) {
+  double s = 0.0;
 #pragma unroll
-    for (int d = 0; d < 128; ++d)
-      if (d < a.D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
+  for (int d = 0; d < 128; ++d) {
+    if (d < D) {
+      const double t = (double)r.elem(d);
+      s = s + t * t;
+    }
   }
-  best = wave_max_u64(best);
-  const int any_bad = __any(bad) ? 1 : 0;
-  const int w = tid >> 6;
-  if ((tid & 63) == 0) { wmax[w] = best; wbad[w] = any_bad; }
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long m = wmax[0];
-    int vb = wbad[0];
-    for (int i = 1; i < 4; ++i) { m = wmax[i] > m ? wmax[i] : m; vb |= wbad[i]; }
-    atomicMax(a.k2 + bh, m);
-    if (vb) atomicOr(a.v_bad, 1);
-  }
+  return s;
 }
 
-// One query row per thread: Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2.
-// Each wave's 64 rows lie in one q-block (q_block is a multiple of 64).
+// Row r of a norm workgroup's block: kBoundsKeys positions x the head group's heads, in
+// memory order (heads of one position adjacent).  One row per thread and pass, so a wave
+// reads 64 consecutive 256-byte rows: every cache line it touches is used whole.
+struct RowBlock {
+  int64_t p0;      // first position of the block
+  int h0, hg;      // head group: first head, heads
+  int rows;        // positions in the block x hg
+};
+
+__device__ inline RowBlock row_block(int64_t block, int64_t n_pos, int H) {
+  RowBlock rb;
+  rb.p0 = block * kBoundsKeys;
+  rb.h0 = blockIdx.z * kBoundsHeads;
+  rb.hg = H - rb.h0 < kBoundsHeads ? H - rb.h0 : kBoundsHeads;
+  const int64_t np = n_pos - rb.p0 < kBoundsKeys ? n_pos - rb.p0 : kBoundsKeys;
+  rb.rows = (int)np * rb.hg;
+  return rb;
+}
+
+// K2[b,h] = max over keys of sum_d (k_d - k_mean_d)^2 (fp64, d in order), and the
+// V-magnitude check on the same rows of V.  Workgroup (key block, b, head group); the head
+// group's k_mean sits in LDS with a padded row stride (lanes of a wave read different heads).
+template <typename T>
+__global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
+  __shared__ float km[kBoundsHeads * 129];
+  __shared__ unsigned long long hmax[kBoundsHeads];
+  const int b = blockIdx.y, tid = threadIdx.x, D = a.D, DP = D + 1;
+  const int h0 = blockIdx.z * kBoundsHeads;
+  const int hg = a.H - h0 < kBoundsHeads ? a.H - h0 : kBoundsHeads;
+  for (int i = tid; i < hg * D; i += 256)
+    km[(i / D) * DP + i % D] = a.k_mean[((int64_t)b * a.H + h0) * D + i];
+  for (int i = tid; i < hg; i += 256) hmax[i] = 0ull;
+  __syncthreads();
+  const int64_t n_blocks = (a.N + kBoundsKeys - 1) / kBoundsKeys;
+  int bad = 0;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    const RowBlock rb = row_block(blk, a.N, a.H);
+    for (int r = tid; r < rb.rows; r += 256) {
+      const int hl = r % rb.hg;
+      const int64_t j = rb.p0 + r / rb.hg;
+      const int h = h0 + hl;
+      const ChunkDesc& cd = a.ch[find_chunk(a, j)];
+      const int64_t jl = j - cd.start;
+      RowRegs<T> kr;
+      kr.load(reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + jl * cd.k_ss + h * cd.k_sh, D);
+      if (sizeof(T) == 2) {
+        RowRegs<T> vr;
+        vr.load(reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + jl * cd.v_ss + h * cd.v_sh, D);
+        atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km + hl * DP, D)));
+#pragma unroll
+        for (int d = 0; d < 128; ++d)
+          if (d < D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
+      } else {
+        atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km + hl * DP, D)));
+        RowRegs<T> vr;     // fp32 rows are 512 bytes: one row in registers at a time
+        vr.load(reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + jl * cd.v_ss + h * cd.v_sh, D);
+#pragma unroll
+        for (int d = 0; d < 128; ++d)
+          if (d < D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
+      }
+    }
+  }
+  const int any_bad = __any(bad) ? 1 : 0;
+  __syncthreads();
+  for (int i = tid; i < hg; i += 256)
+    if (hmax[i] != 0ull) atomicMax(a.k2 + (int64_t)b * a.H + h0 + i, hmax[i]);
+  if (any_bad && (tid & 63) == 0) atomicOr(a.v_bad, 1);
+}
+
+// Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2.  Workgroup (position
+// block, b, head group): its kBoundsKeys positions lie in one q-block (q_block is a
+// multiple of 64), so each head has one maximum per workgroup.
 template <typename T>
 __global__ __launch_bounds__(256) void qnorm_kernel(BoundsArgs a) {
-  __shared__ float zero[128];
-  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x;
-  if (tid < 128) zero[tid] = 0.0f;
-  __syncthreads();
-  const int64_t iw = (int64_t)blockIdx.x * 256 + (tid & ~63);   // the wave's first row
-  const int64_t i = (int64_t)blockIdx.x * 256 + tid;
-  if (iw >= a.Sq) return;
-  unsigned long long v = 0ull;
-  if (i < a.Sq) {
-    RowRegs<T> qr;
-    qr.load(reinterpret_cast<const T*>(a.q) + b * a.q_sb + i * a.q_ss + h * a.q_sh, a.D);
-    v = (unsigned long long)__double_as_longlong(row_sumsq<T>(qr, zero, a.D));
+  __shared__ unsigned long long hmax[kBoundsHeads];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int h0 = blockIdx.z * kBoundsHeads;
+  const int hg = a.H - h0 < kBoundsHeads ? a.H - h0 : kBoundsHeads;
+  const int64_t n_blocks = (a.Sq + kBoundsKeys - 1) / kBoundsKeys;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    if (tid < hg) hmax[tid] = 0ull;
+    __syncthreads();
+    const RowBlock rb = row_block(blk, a.Sq, a.H);
+    for (int r = tid; r < rb.rows; r += 256) {
+      const int hl = r % rb.hg;
+      const int64_t i = rb.p0 + r / rb.hg;
+      RowRegs<T> qr;
+      qr.load(reinterpret_cast<const T*>(a.q) + b * a.q_sb + i * a.q_ss + (h0 + hl) * a.q_sh, a.D);
+      atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(qr, a.D)));
+    }
+    __syncthreads();
+    const int64_t beta = rb.p0 / a.q_block;
+    if (tid < hg && hmax[tid] != 0ull) atomicMax(a.q2 + ((int64_t)b * a.H + h0 + tid) * a.nqb + beta, hmax[tid]);
+    __syncthreads();
   }
-  v = wave_max_u64(v);
-  if ((tid & 63) == 0) atomicMax(a.q2 + (int64_t)bh * a.nqb + iw / a.q_block, v);
 }
 
 // U = alpha64 * sqrt(Q2 * K2); m = ceil(U) - C; elig = v_ok && U <= gate && U finite.
@@ -255,14 +287,17 @@ __global__ void gate_kernel(BoundsArgs a) {
 
 template <typename T>
 void launch_typed(const BoundsArgs& a, hipStream_t s) {
-  const int bh = a.B * a.H;
+  const unsigned groups = (unsigned)((a.H + kBoundsHeads - 1) / kBoundsHeads);
   if (a.center == FIXEDM_CENTER_COMPUTE) {
-    kmean_partial_kernel<T><<<dim3(kKmeanSlabs, bh), 256, 0, s>>>(a);
-    const int64_t n = (int64_t)bh * a.D;
+    const int hpg = a.H < kBoundsHeads ? a.H : kBoundsHeads;
+    kmean_partial_kernel<T><<<dim3((unsigned)a.kslabs, (unsigned)a.B, groups), hpg * (a.D / 8), 0, s>>>(a);
+    const int64_t n = (int64_t)a.B * a.H * a.D;
     kmean_final_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
   }
-  knorm_vcheck_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), bh), 256, 0, s>>>(a);
-  qnorm_kernel<T><<<dim3((unsigned)((a.Sq + 255) / 256), bh), 256, 0, s>>>(a);
+  const int64_t kb = (a.N + kBoundsKeys - 1) / kBoundsKeys, qb = (a.Sq + kBoundsKeys - 1) / kBoundsKeys;
+  const int64_t cap = (int64_t)1 << 20;    // grid-stride loops beyond this many blocks
+  knorm_vcheck_kernel<T><<<dim3((unsigned)(kb < cap ? kb : cap), (unsigned)a.B, groups), 256, 0, s>>>(a);
+  qnorm_kernel<T><<<dim3((unsigned)(qb < cap ? qb : cap), (unsigned)a.B, groups), 256, 0, s>>>(a);
 }
 
 }  // namespace

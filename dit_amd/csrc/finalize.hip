@@ -53,12 +53,33 @@ __global__ void finalize_reg_kernel(FinalizeArgs a) {
   if (q >= a.Sq) return;
   const int d0 = 32 * m + 8 * jj + 4 * (lane >> 5);
   const int64_t rowi = (int64_t)bh * a.sq_pad + q;
-  const float l = a.l[rowi];
-  const float4 acc = reinterpret_cast<const float4*>(a.acc)[idx];
+  float l = a.l[rowi], r = a.r[rowi];
+  float4 acc = reinterpret_cast<const float4*>(a.acc)[idx];
+  if (a.parts > 1 && tile >= a.n_whole) {
+    // a split tail tile: merge its parts (same shift on fixed-m rows, so every factor is 1
+    // there and the merge is a plain sum; online rows rescale to the largest running max;
+    // a part that saw no key has r = -inf and l = 0)
+    const int64_t u0 = (tile - a.n_whole) * (a.parts - 1);
+    const int rin = wave * 64 + n * 32 + (lane & 31);
+    float rm = r;
+    for (int p = 1; p < a.parts; ++p) rm = fmaxf(rm, a.r_x[(u0 + p - 1) * kQTile + rin]);
+    const float f0 = r == rm ? 1.0f : (r == -INFINITY ? 0.0f : exp2f(r - rm));
+    acc = make_float4(acc.x * f0, acc.y * f0, acc.z * f0, acc.w * f0);
+    l = l * f0;
+    for (int p = 1; p < a.parts; ++p) {
+      const int64_t u = u0 + p - 1;
+      const float rp = a.r_x[u * kQTile + rin];
+      const float f = rp == rm ? 1.0f : (rp == -INFINITY ? 0.0f : exp2f(rp - rm));
+      const float4 x = reinterpret_cast<const float4*>(a.acc_x)[u * 8192 + rem];
+      acc = make_float4(acc.x + f * x.x, acc.y + f * x.y, acc.z + f * x.z, acc.w + f * x.w);
+      l = l + f * a.l_x[u * kQTile + rin];
+    }
+    r = rm;
+  }
   const float4 v = make_float4(__fdiv_rn(acc.x, l), __fdiv_rn(acc.y, l), __fdiv_rn(acc.z, l), __fdiv_rn(acc.w, l));
   store4(a, bh / a.H, q, bh % a.H, d0, v);
   if (a.lse != nullptr && m == 0 && jj == 0 && lane < 32)
-    a.lse[(int64_t)bh * a.Sq + q] = lse_of(a.r[rowi], l);
+    a.lse[(int64_t)bh * a.Sq + q] = lse_of(r, l);
 }
 
 // acc row-major: [bh][sq_pad][D].

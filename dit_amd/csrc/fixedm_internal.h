@@ -9,8 +9,44 @@ namespace fixedm {
 
 constexpr int kMaxChunksPerLaunch = 1;   // K/V chunks folded by one attention launch
 constexpr int kMaxBoundsChunks = 32;     // chunks one fixedm_bounds call accepts
-constexpr int kKmeanSlabs = 64;          // key slabs of the deterministic k_mean reduction
+constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (LDS staging)
+constexpr int kBoundsKeys = 32;          // key (or query) positions per norm workgroup
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
+constexpr int kMaxParts = 4;             // key-range parts of a split tail tile (bf16 kernel)
+constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
+
+// Grid-tail split of the bf16 attention launch.  The tiles fill whole rounds of one
+// workgroup per compute unit; the remaining `tail` tiles would leave most CUs idle for a
+// whole round, so each is cut into `parts` key ranges run by separate workgroups, whose
+// partial sums the finalize merges.  parts minimises the rounds the tail takes plus ~3% of
+// a tile per extra part (the query load and workspace fold each part repeats).  Depends on
+// the tile count and the CU count only, so every launch of a run and its finalize agree.
+struct SplitPlan {
+  int32_t n_whole, parts;
+};
+inline SplitPlan split_plan(int64_t tiles, int cus) {
+  SplitPlan sp{(int32_t)tiles, 1};
+  if (cus <= 0) return sp;
+  const int64_t tail = tiles % cus;
+  if (tail == 0 || tail > kMaxSplitTail) return sp;
+  double best = 1.0;
+  for (int p = 2; p <= kMaxParts; ++p) {
+    const double cost = (double)((tail * p + cus - 1) / cus) / p + 0.03 * (p - 1);
+    if (cost < best - 1e-9) { best = cost; sp.parts = p; }
+  }
+  if (sp.parts > 1) sp.n_whole = (int32_t)(tiles - tail);
+  return sp;
+}
+
+// Key slabs of the deterministic k_mean reduction: enough workgroups to fill the chip
+// (about 512 with B x head groups), at most one slab per 16 keys.
+inline int kmean_slabs(int64_t B, int64_t H, int64_t N) {
+  const int64_t groups = B * ((H + kBoundsHeads - 1) / kBoundsHeads);
+  int64_t s = (512 + groups - 1) / groups;
+  if (s > N / 16) s = N / 16;
+  if (s < 1) s = 1;
+  return (int)s;
+}
 
 struct ChunkDesc {
   const void* k;
@@ -27,10 +63,12 @@ struct BoundsLayout {
 };
 bool bounds_layout(const fixedm_problem& p, BoundsLayout* out);
 
-// Workspace: acc fp32, then row sum l and row shift r, per padded query row.
+// Workspace: acc fp32, then row sum l and row shift r, per padded query row; for the bf16
+// kernel also the same three for parts 1.. of split tail tiles ([kMaxParts - 1] per tile,
+// room for kMaxSplitTail tiles).
 struct WorkspaceLayout {
   int64_t n_qtiles, sq_pad;
-  size_t acc, l, r, total;
+  size_t acc, l, r, acc_x, l_x, r_x, total;
 };
 bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out);
 
@@ -54,7 +92,8 @@ struct BoundsArgs {
   unsigned long long* k2;
   float* k_mean;
   int32_t* v_bad;
-  double* kpart;            // [kKmeanSlabs][B*H][D] partial key sums
+  double* kpart;            // [kslabs][B*H][D] partial key sums
+  int32_t kslabs;
 };
 hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
 
@@ -75,6 +114,10 @@ struct AttnArgs {
   float* l;
   float* r;
   int32_t accumulate;  // 0: these keys open the run (initialise); 1: merge into workspace
+  int32_t n_whole, parts;      // split plan (bf16 kernel)
+  float* acc_x;                // parts 1.. of split tiles: [(tile - n_whole) * (parts - 1) + part - 1]
+  float* l_x;
+  float* r_x;
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
@@ -89,7 +132,13 @@ struct FinalizeArgs {
   float* lse;
   int32_t B, H, D, Sq, n_qtiles, sq_pad;
   int32_t reg_layout;  // 1: acc in the bf16 kernel's register order; 0: row-major [bh][q][d]
+  int32_t n_whole, parts;      // split plan of the bf16 launches (reg_layout only)
+  const float* acc_x;
+  const float* l_x;
+  const float* r_x;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+
+int device_cus();   // compute units of the current device (cached per device)
 
 }  // namespace fixedm
