@@ -69,25 +69,25 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
   }
 }
 
-// Partial key sums for the COMPUTE centring mode.  Workgroup (slab, b, head group): thread
-// (hl, c) owns dims 8c..8c+7 of head h0 + hl and adds the keys of the slab in key order.
-// A key's rows of the whole head group are adjacent in memory, so each key is one
-// contiguous read of the workgroup (10 KB for 40 heads of 128 bf16 dims).
+// Partial key sums for the COMPUTE centring mode.  Workgroup (w, b, head group) of a grid of
+// kslabs: thread (hl, c) owns dims 8c..8c+7 of head h0 + hl and adds, in key order, the keys
+// of blocks w, w + kslabs, w + 2 kslabs, ... (8 keys a block).  A key's rows of the head group
+// are adjacent in memory, so each key is one contiguous read of the workgroup, and the
+// workgroups in flight stream one contiguous window of keys.
 template <typename T>
 __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   const int per = a.D / 8;
   const int hl = threadIdx.x / per, c = threadIdx.x % per;
   const int b = blockIdx.y, h = blockIdx.z * kBoundsHeads + hl;
   if (h >= a.H) return;
-  const int64_t s0 = a.N * blockIdx.x / a.kslabs, s1 = a.N * (blockIdx.x + 1) / a.kslabs;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int ci = 0;                                    // chunk of the current key (uniform)
-  for (int64_t j = s0; j < s1; j += 8) {
+  for (int64_t j = (int64_t)blockIdx.x * 8; j < a.N; j += (int64_t)a.kslabs * 8) {
     float f[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t jj = j + u;
-      if (jj < s1) {
+      if (jj < a.N) {
         while (ci + 1 < a.n_chunks && jj >= a.ch[ci + 1].start) ++ci;
         const ChunkDesc& cd = a.ch[ci];
         load8(reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (jj - cd.start) * cd.k_ss + h * cd.k_sh + 8 * c,
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j + u < s1)
+      if (j + u < a.N)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[u][i];
   }
@@ -105,14 +105,31 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
 }
 
-// k_mean[b,h,d] = fp32(sum over slabs in order / N).
-__global__ void kmean_final_kernel(BoundsArgs a) {
+// k_mean[b,h,d] = fp32(sum of the partial sums / N): thread (g, e) of a 256-thread workgroup
+// adds partials g, g + 8, ... for element e; the 8 group sums are then added in g order.
+__global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
+  __shared__ double part[8][32];
   const int64_t n = (int64_t)a.B * a.H * a.D;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    double s = 0.0;
-    for (int sl = 0; sl < a.kslabs; ++sl) s = s + a.kpart[(int64_t)sl * n + i];
-    a.k_mean[i] = (float)(s / (double)a.N);
+  const int g = threadIdx.x >> 5, el = threadIdx.x & 31;
+  const int64_t i = (int64_t)blockIdx.x * 32 + el;
+  double s = 0.0;
+  if (i < n) {
+    int sl = g;
+    for (; sl + 56 < a.kslabs; sl += 64) {      // eight partials in flight, added in order
+      double x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = a.kpart[(int64_t)(sl + 8 * u) * n + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s = s + x[u];
+    }
+    for (; sl < a.kslabs; sl += 8) s = s + a.kpart[(int64_t)sl * n + i];
+  }
+  part[g][el] = s;
+  __syncthreads();
+  if (g == 0 && i < n) {
+    double t = part[0][el];
+    for (int k = 1; k < 8; ++k) t = t + part[k][el];
+    a.k_mean[i] = (float)(t / (double)a.N);
   }
 }
 
@@ -168,100 +185,160 @@ __device__ inline double row_sumsq(const RowRegs<T>& r, int D) {
   return s;
 }
 
-// Row r of a norm workgroup's block: kBoundsKeys positions x the head group's heads, in
-// memory order (heads of one position adjacent).  One row per thread and pass, so a wave
-// reads 64 consecutive 256-byte rows: every cache line it touches is used whole.
-struct RowBlock {
-  int64_t p0;      // first position of the block
-  int h0, hg;      // head group: first head, heads
-  int rows;        // positions in the block x hg
+// The norm kernels give each wave 64 consecutive rows (keys or query positions) of one
+// head.  The wave reads them with coalesced 16-byte loads (P = D sizeof(T) / 16 lanes per
+// row), stores them to its LDS area with the piece index XOR-swizzled by the row, and each
+// lane then reads back its own row (bank-conflict free both ways) and sums it in index order.
+template <typename T>
+struct NormGeom {
+  static constexpr int kMaxP = 128 * (int)sizeof(T) / 16;   // pieces per row at D = 128
+  static constexpr int kWaves = sizeof(T) == 2 ? 4 : 2;       // 64 KB of staging per workgroup
 };
 
-__device__ inline RowBlock row_block(int64_t block, int64_t n_pos, int H) {
-  RowBlock rb;
-  rb.p0 = block * kBoundsKeys;
-  rb.h0 = blockIdx.z * kBoundsHeads;
-  rb.hg = H - rb.h0 < kBoundsHeads ? H - rb.h0 : kBoundsHeads;
-  const int64_t np = n_pos - rb.p0 < kBoundsKeys ? n_pos - rb.p0 : kBoundsKeys;
-  rb.rows = (int)np * rb.hg;
-  return rb;
+// Row pointer of key j, head h, batch b, in K or V, for a key known to lie in chunks c0..c1
+// (a wave-uniform range: the chunk is selected without divergent indexing).
+template <typename T>
+__device__ inline const T* key_row(const BoundsArgs& a, int b, int h, int64_t j, int c0, int c1, bool v) {
+  const T* p = nullptr;
+  for (int c = c0; c <= c1; ++c) {
+    const ChunkDesc& cd = a.ch[c];
+    if (j >= cd.start)
+      p = v ? reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + (j - cd.start) * cd.v_ss + h * cd.v_sh
+            : reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (j - cd.start) * cd.k_ss + h * cd.k_sh;
+  }
+  return p;
 }
 
-// K2[b,h] = max over keys of sum_d (k_d - k_mean_d)^2 (fp64, d in order), and the
-// V-magnitude check on the same rows of V.  Workgroup (key block, b, head group); the head
-// group's k_mean sits in LDS with a padded row stride (lanes of a wave read different heads).
+// |x| <= 256 for every element of a 16-byte piece (NaN fails).
+__device__ inline bool piece_ok(uint4 w, const uint16_t*) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ok = ok && (u[i] & 0x7fffu) <= 0x4380u && ((u[i] >> 16) & 0x7fffu) <= 0x4380u;
+  return ok;
+}
+__device__ inline bool piece_ok(uint4 w, const float*) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ok = ok && (u[i] & 0x7fffffffu) <= 0x43800000u;
+  return ok;
+}
+
+__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Loads the P pieces lane `lane` owns of the wave's rows: piece lane mod P of rows
+// lane / P + i 64 / P.  Rows past nrows repeat row nrows - 1 (every load is in bounds and
+// unconditional; those rows are never summed).  row(r) gives a row's pointer.
+template <int P, typename RowFn>
+__device__ inline void load_pieces(uint4 (&v)[P], int nrows, int lane, RowFn row) {
+  const int pc = lane % P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    int r = lane / P + i * (64 / P);
+    r = r < nrows ? r : nrows - 1;
+    v[i] = reinterpret_cast<const uint4*>(row(r))[pc];
+  }
+}
+
+// Stores the pieces to the wave's LDS area (piece pc of row r at slot r P + (pc ^ (r mod P)))
+// and reads back row `lane` into out[0..P).
+template <int P>
+__device__ inline void transpose_rows(const uint4 (&v)[P], uint4* area, int lane, uint4* out) {
+  const int pc = lane % P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int r = lane / P + i * (64 / P);
+    area[r * P + (pc ^ (r % P))] = v[i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int q = 0; q < P; ++q) out[q] = area[lane * P + (q ^ (lane % P))];
+}
+
+// 256 keys of one (b, h) per workgroup, one key per thread: K2 = max over keys of
+// sum_d (k_d - k_mean_d)^2 (fp64, d in order; k_mean staged in LDS as fp64), and the
+// V-magnitude check on the same keys' value rows.  (A coalesced-load variant that
+// transposes rows through LDS measured slower: the per-row fp64 work, not the load
+// pattern, sets this kernel's pace.)
 template <typename T>
 __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
-  __shared__ float km[kBoundsHeads * 129];
-  __shared__ unsigned long long hmax[kBoundsHeads];
-  const int b = blockIdx.y, tid = threadIdx.x, D = a.D, DP = D + 1;
-  const int h0 = blockIdx.z * kBoundsHeads;
-  const int hg = a.H - h0 < kBoundsHeads ? a.H - h0 : kBoundsHeads;
-  for (int i = tid; i < hg * D; i += 256)
-    km[(i / D) * DP + i % D] = a.k_mean[((int64_t)b * a.H + h0) * D + i];
-  for (int i = tid; i < hg; i += 256) hmax[i] = 0ull;
+  __shared__ double km[128];
+  __shared__ unsigned long long wmax[4];
+  __shared__ int wbad[4];
+  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  if (tid < a.D) km[tid] = (double)a.k_mean[(int64_t)bh * a.D + tid];
   __syncthreads();
-  const int64_t n_blocks = (a.N + kBoundsKeys - 1) / kBoundsKeys;
+  unsigned long long best = 0ull;
   int bad = 0;
-  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-    const RowBlock rb = row_block(blk, a.N, a.H);
-    for (int r = tid; r < rb.rows; r += 256) {
-      const int hl = r % rb.hg;
-      const int64_t j = rb.p0 + r / rb.hg;
-      const int h = h0 + hl;
-      const ChunkDesc& cd = a.ch[find_chunk(a, j)];
-      const int64_t jl = j - cd.start;
-      RowRegs<T> kr;
-      kr.load(reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + jl * cd.k_ss + h * cd.k_sh, D);
-      if (sizeof(T) == 2) {
-        RowRegs<T> vr;
-        vr.load(reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + jl * cd.v_ss + h * cd.v_sh, D);
-        atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km + hl * DP, D)));
+  if (j < a.N) {
+    const int c = find_chunk(a, j);
+    RowRegs<T> kr, vr;
+    kr.load(key_row<T>(a, b, h, j, c, c, false), a.D);
+    vr.load(key_row<T>(a, b, h, j, c, c, true), a.D);
+    double s = 0.0;
 #pragma unroll
-        for (int d = 0; d < 128; ++d)
-          if (d < D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
-      } else {
-        atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(kr, km + hl * DP, D)));
-        RowRegs<T> vr;     // fp32 rows are 512 bytes: one row in registers at a time
-        vr.load(reinterpret_cast<const T*>(cd.v) + b * cd.v_sb + jl * cd.v_ss + h * cd.v_sh, D);
-#pragma unroll
-        for (int d = 0; d < 128; ++d)
-          if (d < D) bad |= !(fabsf(vr.elem(d)) <= 256.0f);
+    for (int d = 0; d < 128; ++d) {
+      if (d < a.D) {
+        const double t = (double)kr.elem(d) - km[d];
+        s = s + t * t;
       }
     }
+    best = (unsigned long long)__double_as_longlong(s);
+#pragma unroll
+    for (int i = 0; i < RowRegs<T>::kPieces; ++i)
+      if (i < a.D * (int)sizeof(T) / 16) bad |= !piece_ok(vr.p[i], (const T*)nullptr);
   }
+  best = wave_max_u64(best);
   const int any_bad = __any(bad) ? 1 : 0;
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) { wmax[w] = best; wbad[w] = any_bad; }
   __syncthreads();
-  for (int i = tid; i < hg; i += 256)
-    if (hmax[i] != 0ull) atomicMax(a.k2 + (int64_t)b * a.H + h0 + i, hmax[i]);
-  if (any_bad && (tid & 63) == 0) atomicOr(a.v_bad, 1);
+  if (tid == 0) {
+    unsigned long long m = wmax[0];
+    int vb = wbad[0];
+    for (int i = 1; i < 4; ++i) { m = wmax[i] > m ? wmax[i] : m; vb |= wbad[i]; }
+    atomicMax(a.k2 + bh, m);
+    if (vb) atomicOr(a.v_bad, 1);
+  }
 }
 
-// Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2.  Workgroup (position
-// block, b, head group): its kBoundsKeys positions lie in one q-block (q_block is a
-// multiple of 64), so each head has one maximum per workgroup.
-template <typename T>
-__global__ __launch_bounds__(256) void qnorm_kernel(BoundsArgs a) {
-  __shared__ unsigned long long hmax[kBoundsHeads];
-  const int b = blockIdx.y, tid = threadIdx.x;
-  const int h0 = blockIdx.z * kBoundsHeads;
-  const int hg = a.H - h0 < kBoundsHeads ? a.H - h0 : kBoundsHeads;
-  const int64_t n_blocks = (a.Sq + kBoundsKeys - 1) / kBoundsKeys;
-  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-    if (tid < hg) hmax[tid] = 0ull;
-    __syncthreads();
-    const RowBlock rb = row_block(blk, a.Sq, a.H);
-    for (int r = tid; r < rb.rows; r += 256) {
-      const int hl = r % rb.hg;
-      const int64_t i = rb.p0 + r / rb.hg;
-      RowRegs<T> qr;
-      qr.load(reinterpret_cast<const T*>(a.q) + b * a.q_sb + i * a.q_ss + (h0 + hl) * a.q_sh, a.D);
-      atomicMax(&hmax[hl], (unsigned long long)__double_as_longlong(row_sumsq<T>(qr, a.D)));
-    }
-    __syncthreads();
-    const int64_t beta = rb.p0 / a.q_block;
-    if (tid < hg && hmax[tid] != 0ull) atomicMax(a.q2 + ((int64_t)b * a.H + h0 + tid) * a.nqb + beta, hmax[tid]);
-    __syncthreads();
+// Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2: work item (block of 64
+// positions, head group), as in the K kernel; 64 positions lie in one q-block (q_block is
+// a multiple of 64).
+template <typename T, int P>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void qnorm_kernel(BoundsArgs a) {
+  constexpr int W = NormGeom<T>::kWaves, D = P * 16 / (int)sizeof(T);
+  __shared__ uint4 stage[W * 64 * P];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.y;
+  const int64_t n_hq = (a.H + W - 1) / W, n_pb = (a.Sq + 63) / 64;
+  uint4* area = stage + wave * 64 * P;
+  for (int64_t item = blockIdx.x; item < n_pb * n_hq; item += gridDim.x) {
+    const int h = (int)(item % n_hq) * W + wave;
+    const int64_t i0 = item / n_hq * 64;
+    if (h >= a.H) continue;
+    const int nrows = a.Sq - i0 < 64 ? (int)(a.Sq - i0) : 64;
+    const T* q0 = reinterpret_cast<const T*>(a.q) + b * a.q_sb + i0 * a.q_ss + h * a.q_sh;
+    uint4 qv[P];
+    load_pieces<P>(qv, nrows, lane, [&](int r) { return q0 + r * a.q_ss; });
+    RowRegs<T> qr;
+    transpose_rows<P>(qv, area, lane, qr.p);
+    const double ss = row_sumsq<T>(qr, D);
+    unsigned long long best = lane < nrows ? (unsigned long long)__double_as_longlong(ss) : 0ull;
+    best = wave_max_u64(best);
+    if (lane == 0) atomicMax(a.q2 + ((int64_t)b * a.H + h) * a.nqb + i0 / a.q_block, best);
   }
 }
 
@@ -292,12 +369,21 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
     const int hpg = a.H < kBoundsHeads ? a.H : kBoundsHeads;
     kmean_partial_kernel<T><<<dim3((unsigned)a.kslabs, (unsigned)a.B, groups), hpg * (a.D / 8), 0, s>>>(a);
     const int64_t n = (int64_t)a.B * a.H * a.D;
-    kmean_final_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+    kmean_final_kernel<<<(unsigned)((n + 31) / 32), 256, 0, s>>>(a);
   }
-  const int64_t kb = (a.N + kBoundsKeys - 1) / kBoundsKeys, qb = (a.Sq + kBoundsKeys - 1) / kBoundsKeys;
-  const int64_t cap = (int64_t)1 << 20;    // grid-stride loops beyond this many blocks
-  knorm_vcheck_kernel<T><<<dim3((unsigned)(kb < cap ? kb : cap), (unsigned)a.B, groups), 256, 0, s>>>(a);
-  qnorm_kernel<T><<<dim3((unsigned)(qb < cap ? qb : cap), (unsigned)a.B, groups), 256, 0, s>>>(a);
+  constexpr int W = NormGeom<T>::kWaves;
+  const int64_t n_hq = (a.H + W - 1) / W;
+  const int64_t qitems = (a.Sq + 63) / 64 * n_hq;
+  const int64_t cap = (int64_t)1 << 20;    // grid-stride loops beyond this many workgroups
+  const dim3 gq((unsigned)(qitems < cap ? qitems : cap), (unsigned)a.B);
+  knorm_vcheck_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), (unsigned)(a.B * a.H)), 256, 0, s>>>(a);
+  if constexpr (sizeof(T) == 4) {            // fp32: D = 64 (16 pieces a row) or 128 (32)
+    if (a.D == 128) {
+      qnorm_kernel<T, 32><<<gq, 64 * W, 0, s>>>(a);
+      return;
+    }
+  }
+  qnorm_kernel<T, 16><<<gq, 64 * W, 0, s>>>(a);   // bf16 D = 128, fp32 D = 64
 }
 
 }  // namespace

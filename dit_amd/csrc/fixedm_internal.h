@@ -10,7 +10,6 @@ namespace fixedm {
 constexpr int kMaxChunksPerLaunch = 1;   // K/V chunks folded by one attention launch
 constexpr int kMaxBoundsChunks = 32;     // chunks one fixedm_bounds call accepts
 constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (LDS staging)
-constexpr int kBoundsKeys = 32;          // key (or query) positions per norm workgroup
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
 constexpr int kMaxParts = 4;             // key-range parts of a split tail tile (bf16 kernel)
 constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
