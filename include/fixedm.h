@@ -131,7 +131,11 @@ size_t fixedm_bounds_bytes(const fixedm_problem* p);
 fixedm_status fixedm_bounds_layout(const fixedm_problem* p, fixedm_bounds_layout_t* out);
 
 /* Size of the accumulator workspace fixedm_attn_fwd/fixedm_finalize use (fp32 acc, row
- * sum l and row shift r for every padded query row), or 0 if the problem is invalid. */
+ * sum l and row shift r for every padded query row; for bf16 problems also the same three
+ * for the key-range parts of up to 255 split tail tiles), or 0 if the problem is invalid.
+ * How the bf16 kernel splits its last partial round of tiles depends on the problem and on
+ * the device's compute-unit count, so a run's fixedm_attn_fwd and fixedm_finalize calls
+ * must use the same device (they always do for one workspace in practice). */
 size_t fixedm_workspace_bytes(const fixedm_problem* p);
 
 /* Host-only constants of [FM] Summary for n >= 1 keys:
@@ -151,7 +155,7 @@ fixedm_status fixedm_constants(int64_t n, int32_t* log2_n, int32_t* C, int32_t* 
  * sum(chunk_len) must equal p->sk_total.  k_mean_in: device fp32 [B, H, D] contiguous,
  * required iff center == SUPPLIED.  bounds_dev: device buffer of fixedm_bounds_bytes(p)
  * bytes, 256-byte aligned.  On success *out describes the result (valid once the stream
- * reaches this point).  Enqueues 4-5 kernels; no host synchronisation. */
+ * reaches this point).  Enqueues 4-6 kernels; no host synchronisation. */
 fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q,
                             const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
                             const int64_t* chunk_len, int32_t n_chunks,
