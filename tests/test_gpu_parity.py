@@ -225,6 +225,17 @@ def test_mixed_bodies_with_assembly_loop(F):
     assert ob.elig.any() and not ob.elig.all()
 
 
+def test_split_grid_tail(F):
+    """37 heads x 8 query tiles = 296 tiles: on a 256-CU device the last 40 run as 4 key-range
+    parts each.  The first chunk (60 keys) leaves parts 0 and 1 of every split tile empty on
+    the visit that initialises the workspace, and a loud query block puts online-softmax waves
+    into split tiles (tail tiles belong to heads 32-36), so the finalize merges both kinds."""
+    say("edge: split grid tail")
+    ob, _ = _generic(F, 47, "bf16", 1, 37, 128, 2048, (60, 700, 1301), q_block=64,
+                     loud_rows=(35, 0, 64, 14.0))
+    assert ob.elig.any() and not ob.elig.all()
+
+
 @pytest.mark.parametrize("chunks", [
     (448, 480, 481),          # 14, 15 and 15 + 1 tiles: no assembly group, one group, one + partial
     (735, 0, 736, 1000),      # 22 and 23 full tiles (one / two groups) and an empty chunk
