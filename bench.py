@@ -1,12 +1,15 @@
 """Benchmark: fixed-m attention forward on one MI355X.
 
-One step = the whole hot path for one ring rank: fixedm_bounds, run init, one
-fixedm_attn_fwd per visiting K/V chunk (ring order 0, 3, 2, 1), fixedm_finalize to a bf16
-output.  Inputs are seeded synthetic tensors at the Wan2.2 720p rank-share shape (40 heads,
+One step = the whole hot path for one ring rank: fixedm_bounds, run init, then one
+fixedm_attn_fwd_final over the visiting K/V chunks in ring order 0, 3, 2, 1 (the chunks
+folded with the accumulators resident in registers, and the output written as bf16 by the
+same launch).  With --per-chunk a step is instead one fixedm_attn_fwd per chunk and a
+separate fixedm_finalize, as a ring rank receiving one chunk at a time would run it.
+Inputs are seeded synthetic tensors at the Wan2.2 720p rank-share shape (40 heads,
 head_dim 128, 18,900 resident queries, 75,600 keys in 4 chunks), resident in HBM before
 the timed region starts.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--per-chunk] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -115,6 +118,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-chunk", action="store_true",
+                    help="one fixedm_attn_fwd per ring chunk + fixedm_finalize instead of one "
+                         "fixedm_attn_fwd_final over all chunks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB fp32 read+write kernel (3 times): the reference "
@@ -164,13 +170,21 @@ def main():
     out_dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     out = torch.empty((wl.batch, wl.sq, wl.heads, wl.head_dim), dtype=out_dtype, device="cuda")
     stream = torch.cuda.current_stream()
-    n_attn = len(ks)
+    fused = not args.per_chunk
+    n_attn = 1 if fused else len(ks)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps * n_attn)]
 
     def step(timed_idx=None):
         desc, _ = F.bounds(p, q, ks, vs, k_mean=km, buf=buf, stream=stream)
         run = F.run_init(desc)
+        if fused:
+            if timed_idx is not None:
+                ev[timed_idx][0].record(stream)
+            F.attn_fwd_final(desc, run, q, ks, vs, ws, out, None, stream=stream)
+            if timed_idx is not None:
+                ev[timed_idx][1].record(stream)
+            return desc
         for c in range(n_attn):
             if timed_idx is not None:
                 ev[timed_idx * n_attn + c][0].record(stream)
@@ -227,7 +241,9 @@ def main():
             "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
             "sq": wl.sq, "sk": wl.sk, "chunks": list(wl.chunks), "ring_order": order,
             "q_block": wl.q_block, "centering": wl.center, "eligible_fraction": elig_frac,
-            "step": "bounds + 4 x attn_fwd (one per ring chunk) + finalize(bf16 out)",
+            "step": ("bounds + attn_fwd_final over the 4 ring chunks (bf16 out written by the "
+                     "attention launch)" if fused else
+                     "bounds + 4 x attn_fwd (one per ring chunk) + finalize(bf16 out)"),
         },
         "roofline": {
             "kernel": "attn_bf16_d128_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
@@ -235,6 +251,8 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
             "launch_ms": round(attn_avg, 4), "launches_per_step": n_attn,
             "flops_per_launch": per_launch_flops,
+            "timed_call": ("fixedm_attn_fwd_final: the attention launch plus the finalize of "
+                           "the split tail tiles" if fused else "fixedm_attn_fwd (one launch)"),
         },
     }
     if not args.no_cpu_baseline:

@@ -316,13 +316,19 @@ fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run) 
   run->token = bounds->token;
   run->kv_visited = 0;
   run->calls = 0;
-  run->reserved = 0;
+  run->finalized = 0;
   return FIXEDM_OK;
 }
 
-fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the attention entry points; fills *total with the keys of the call.
+fixedm_status check_attn_call(const fixedm_bounds_t* bounds, const fixedm_run_t* run, fixedm_tensor q,
                               const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
-                              const int64_t* chunk_len, int32_t n_chunks, void* workspace, void* stream) {
+                              const int64_t* chunk_len, int32_t n_chunks, const void* workspace,
+                              int64_t* total, bool allow_none = false) {
   fixedm_status st = check_descriptor(bounds);
   if (st != FIXEDM_OK) return st;
   if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
@@ -330,11 +336,30 @@ fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, 
   if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
   const fixedm_problem& p = bounds->p;
   if ((st = check_tensor(p, q)) != FIXEDM_OK) return st;
-  int64_t total = 0;
-  if ((st = check_chunks(p, k_chunks, v_chunks, chunk_len, n_chunks, &total)) != FIXEDM_OK) return st;
-  if (run->kv_visited < 0 || run->kv_visited + total > p.sk_total) return FIXEDM_ERR_STATE;
-  if (total == 0) return FIXEDM_OK;
+  *total = 0;
+  if (!(allow_none && n_chunks == 0) &&
+      (st = check_chunks(p, k_chunks, v_chunks, chunk_len, n_chunks, total)) != FIXEDM_OK)
+    return st;
+  if (run->finalized != 0) return FIXEDM_ERR_STATE;
+  if (run->kv_visited < 0 || run->kv_visited + *total > p.sk_total) return FIXEDM_ERR_STATE;
+  return FIXEDM_OK;
+}
 
+fixedm_status check_out_call(const fixedm_problem& p, fixedm_tensor out, int32_t out_dtype, const float* lse) {
+  if (out_dtype != FIXEDM_BF16 && out_dtype != FIXEDM_F32) return FIXEDM_ERR_UNSUPPORTED_DTYPE;
+  const fixedm_status st = check_out_tensor(p, out, out_dtype);
+  if (st != FIXEDM_OK) return st;
+  if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  return FIXEDM_OK;
+}
+
+SplitPlan plan_of(const fixedm_problem& p, const WorkspaceLayout& wl) {
+  const int64_t tiles = p.batch * p.heads * wl.n_qtiles;
+  return p.dtype == FIXEDM_BF16 ? split_plan(tiles, device_cus()) : SplitPlan{(int32_t)tiles, 1};
+}
+
+AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspace) {
+  const fixedm_problem& p = bounds->p;
   BoundsLayout lay;
   bounds_layout(p, &lay);
   WorkspaceLayout wl;
@@ -358,46 +383,14 @@ fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, 
   a.acc_x = reinterpret_cast<float*>(wbase + wl.acc_x);
   a.l_x = reinterpret_cast<float*>(wbase + wl.l_x);
   a.r_x = reinterpret_cast<float*>(wbase + wl.r_x);
-  const SplitPlan sp = p.dtype == FIXEDM_BF16 ? split_plan(p.batch * p.heads * wl.n_qtiles, device_cus())
-                                             : SplitPlan{(int32_t)(p.batch * p.heads * wl.n_qtiles), 1};
+  const SplitPlan sp = plan_of(p, wl);
   a.n_whole = sp.n_whole;
   a.parts = sp.parts;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  int64_t visited = run->kv_visited;
-  int32_t c = 0;
-  while (c < n_chunks) {
-    a.n_chunks = 0;
-    while (c < n_chunks && a.n_chunks < kMaxChunksPerLaunch) {
-      if (chunk_len[c] > 0) a.ch[a.n_chunks++] = make_chunk(k_chunks[c], v_chunks[c], chunk_len[c], 0);
-      ++c;
-    }
-    if (a.n_chunks == 0) break;
-    int64_t launched = 0;
-    for (int32_t i = 0; i < a.n_chunks; ++i) launched += a.ch[i].len;
-    a.accumulate = visited > 0 ? 1 : 0;
-    const hipError_t e = p.dtype == FIXEDM_BF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
-    if (e != hipSuccess) return FIXEDM_ERR_HIP;
-    visited += launched;
-  }
-  run->kv_visited = visited;
-  run->calls += 1;
-  return FIXEDM_OK;
+  return a;
 }
 
-fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run, const void* workspace,
-                              fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
-  fixedm_status st = check_descriptor(bounds);
-  if (st != FIXEDM_OK) return st;
-  if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
-  if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
-  if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
-  if (out_dtype != FIXEDM_BF16 && out_dtype != FIXEDM_F32) return FIXEDM_ERR_UNSUPPORTED_DTYPE;
-  const fixedm_problem& p = bounds->p;
-  if ((st = check_out_tensor(p, out, out_dtype)) != FIXEDM_OK) return st;
-  if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
-  if (run->kv_visited != p.sk_total) return FIXEDM_ERR_STATE;
-
+FinalizeArgs finalize_args(const fixedm_problem& p, const void* workspace, fixedm_tensor out, int32_t out_dtype,
+                           float* lse) {
   WorkspaceLayout wl;
   workspace_layout(p, &wl);
   const char* wbase = static_cast<const char*>(workspace);
@@ -413,13 +406,125 @@ fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t*
   a.B = (int32_t)p.batch; a.H = (int32_t)p.heads; a.D = (int32_t)p.head_dim;
   a.Sq = (int32_t)p.sq; a.n_qtiles = (int32_t)wl.n_qtiles; a.sq_pad = (int32_t)wl.sq_pad;
   a.reg_layout = p.dtype == FIXEDM_BF16 ? 1 : 0;
-  const SplitPlan sp = p.dtype == FIXEDM_BF16 ? split_plan(p.batch * p.heads * wl.n_qtiles, device_cus())
-                                             : SplitPlan{(int32_t)(p.batch * p.heads * wl.n_qtiles), 1};
+  const SplitPlan sp = plan_of(p, wl);
   a.n_whole = sp.n_whole;
   a.parts = sp.parts;
+  a.tile_begin = 0;
   a.acc_x = reinterpret_cast<const float*>(wbase + wl.acc_x);
   a.l_x = reinterpret_cast<const float*>(wbase + wl.l_x);
   a.r_x = reinterpret_cast<const float*>(wbase + wl.r_x);
+  return a;
+}
+
+// Enqueues the attention launches of one call: up to kMaxChunksPerLaunch non-empty chunks per
+// launch, each launch folding its chunks into registers and then into the workspace.  With
+// `fin` (bf16 only) the last launch completes the run and writes O itself (fin->... fields).
+fixedm_status enqueue_attn(AttnArgs a, const fixedm_problem& p, const fixedm_tensor* k_chunks,
+                           const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
+                           int64_t visited, const AttnArgs* fin, hipStream_t s) {
+  int32_t c = 0;
+  while (c < n_chunks) {
+    a.n_chunks = 0;
+    a.call_len = 0;
+    while (c < n_chunks && a.n_chunks < kMaxChunksPerLaunch) {
+      if (chunk_len[c] > 0) {
+        a.ch[a.n_chunks++] = make_chunk(k_chunks[c], v_chunks[c], chunk_len[c], a.call_len);
+        a.call_len += chunk_len[c];
+      }
+      ++c;
+    }
+    while (c < n_chunks && chunk_len[c] == 0) ++c;   // trailing empty chunks end the call here
+    if (a.n_chunks == 0) break;
+    a.accumulate = visited > 0 ? 1 : 0;
+    if (fin != nullptr && c == n_chunks) {
+      a.final_out = 1;
+      a.out_dtype = fin->out_dtype;
+      a.out = fin->out;
+      a.o_sb = fin->o_sb; a.o_ss = fin->o_ss; a.o_sh = fin->o_sh;
+      a.lse = fin->lse;
+    }
+    const hipError_t e = p.dtype == FIXEDM_BF16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    if (e != hipSuccess) return FIXEDM_ERR_HIP;
+    visited += a.call_len;
+  }
+  return FIXEDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
+                              const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
+                              const int64_t* chunk_len, int32_t n_chunks, void* workspace, void* stream) {
+  int64_t total = 0;
+  fixedm_status st = check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace, &total);
+  if (st != FIXEDM_OK) return st;
+  if (total == 0) return FIXEDM_OK;
+  const AttnArgs a = attn_args(bounds, q, workspace);
+  st = enqueue_attn(a, bounds->p, k_chunks, v_chunks, chunk_len, n_chunks, run->kv_visited, nullptr,
+                    static_cast<hipStream_t>(stream));
+  if (st != FIXEDM_OK) return st;
+  run->kv_visited += total;
+  run->calls += 1;
+  return FIXEDM_OK;
+}
+
+fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
+                                    const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
+                                    const int64_t* chunk_len, int32_t n_chunks, void* workspace,
+                                    fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
+  int64_t total = 0;
+  fixedm_status st =
+      check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace, &total, true);
+  if (st != FIXEDM_OK) return st;
+  const fixedm_problem& p = bounds->p;
+  if ((st = check_out_call(p, out, out_dtype, lse)) != FIXEDM_OK) return st;
+  if (run->kv_visited + total != p.sk_total) return FIXEDM_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const FinalizeArgs f = finalize_args(p, workspace, out, out_dtype, lse);
+  if (total == 0 || p.dtype != FIXEDM_BF16) {
+    // nothing left to fold, or the fp32 path: fold, then the finalize kernel
+    if (total > 0) {
+      const AttnArgs a = attn_args(bounds, q, workspace);
+      st = enqueue_attn(a, p, k_chunks, v_chunks, chunk_len, n_chunks, run->kv_visited, nullptr, s);
+      if (st != FIXEDM_OK) return st;
+    }
+    if (launch_finalize(f, s) != hipSuccess) return FIXEDM_ERR_HIP;
+  } else {
+    AttnArgs a = attn_args(bounds, q, workspace);
+    AttnArgs fin;
+    memset(&fin, 0, sizeof fin);
+    fin.out_dtype = out_dtype;
+    fin.out = const_cast<void*>(out.ptr);
+    fin.o_sb = out.stride_b; fin.o_ss = out.stride_s; fin.o_sh = out.stride_h;
+    fin.lse = lse;
+    st = enqueue_attn(a, p, k_chunks, v_chunks, chunk_len, n_chunks, run->kv_visited, &fin, s);
+    if (st != FIXEDM_OK) return st;
+    if (a.parts > 1) {
+      // the split tail tiles left their parts in the workspace: merge and write those tiles
+      FinalizeArgs ft = f;
+      ft.tile_begin = a.n_whole;
+      if (launch_finalize(ft, s) != hipSuccess) return FIXEDM_ERR_HIP;
+    }
+  }
+  run->kv_visited += total;
+  run->calls += 1;
+  run->finalized = 1;
+  return FIXEDM_OK;
+}
+
+fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run, const void* workspace,
+                              fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
+  fixedm_status st = check_descriptor(bounds);
+  if (st != FIXEDM_OK) return st;
+  if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
+  if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  const fixedm_problem& p = bounds->p;
+  if ((st = check_out_call(p, out, out_dtype, lse)) != FIXEDM_OK) return st;
+  if (run->kv_visited != p.sk_total || run->finalized != 0) return FIXEDM_ERR_STATE;
+  const FinalizeArgs a = finalize_args(p, workspace, out, out_dtype, lse);
   if (launch_finalize(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
   return FIXEDM_OK;
 }

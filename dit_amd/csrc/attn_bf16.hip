@@ -235,6 +235,41 @@ __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, c
 // The steady-state fixed-m loop, written out instruction by instruction (generated).
 #include "fixed_loop.inc"
 
+// O^T += V(tile)^T P(tile)^T for a chunk piece of a single tile in the fixed-m body, with the
+// accumulators held in AGPRs as the assembly loop holds them: in a chunk loop a compiled MFMA
+// on O would move the accumulators to architectural registers for the whole loop.  The
+// leading and trailing wait states cover the VALU-write -> MFMA-read and MFMA-write -> read
+// hazards the compiler cannot see across the block.
+__device__ __attribute__((always_inline)) inline void pv_tile_asm(f32x16 (&o)[2][4], const bf16x8 (&vf)[2][4],
+                                                                  const bf16x8 (&p)[2][2]) {
+  asm volatile(
+      "s_nop 4\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %4, %8, %18, %4\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %9, %16, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %5, %9, %18, %5\n"
+      "v_mfma_f32_32x32x16_bf16 %2, %10, %16, %2\n"
+      "v_mfma_f32_32x32x16_bf16 %6, %10, %18, %6\n"
+      "v_mfma_f32_32x32x16_bf16 %3, %11, %16, %3\n"
+      "v_mfma_f32_32x32x16_bf16 %7, %11, %18, %7\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %12, %17, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %4, %12, %19, %4\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %13, %17, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %5, %13, %19, %5\n"
+      "v_mfma_f32_32x32x16_bf16 %2, %14, %17, %2\n"
+      "v_mfma_f32_32x32x16_bf16 %6, %14, %19, %6\n"
+      "v_mfma_f32_32x32x16_bf16 %3, %15, %17, %3\n"
+      "v_mfma_f32_32x32x16_bf16 %7, %15, %19, %7\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 3\n"
+      : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+        "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3])
+      : "v"(vf[0][0]), "v"(vf[0][1]), "v"(vf[0][2]), "v"(vf[0][3]),
+        "v"(vf[1][0]), "v"(vf[1][1]), "v"(vf[1][2]), "v"(vf[1][3]),
+        "v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]));
+}
+
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
 // and adds the same rounded values to the row sum (low half then high half of each pair,
 // unpacked with integer ops), so numerator and denominator see identical weights.
@@ -324,7 +359,11 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
                                                          const uint8_t* smem, const bf16x8 (&qf)[2][8],
                                                          f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
                                                          int b, int h) {
-  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  // The lane's offsets are rebuilt for every chunk piece from an id the compiler cannot
+  // hoist: kept live across the assembly loop, which uses every register, they would spill.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, hh = lane >> 5;
   Ring g;
   g.wave = tid >> 6;
   g.len = cd.len;
@@ -369,7 +408,9 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
     ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
     softmax_fixed(s, p, lsum);
     if (n_tiles == 1) {
-      compute_pv(smem, g, 0, p, o);
+      bf16x8 vf[2][4];
+      load_v(smem, g, 0, vf);
+      pv_tile_asm(o, vf, p);
     } else {
       // tiles 1 .. n_tiles-1 and the PV product of the last one: the assembly loop
       compute_s(smem, g, 1, qf, s, nshift, tile_rows(g, 1), hh);
@@ -415,10 +456,32 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   barrier();
 }
 
+// Folds keys [klo, khi) of the launch's chunk sequence (the chunks concatenated in call
+// order) into the resident accumulators: one ring pass per chunk piece, the accumulators
+// and the online body's running max carried in registers from piece to piece.
+template <bool kFixed>
+__device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64_t klo, int64_t khi,
+                                                        const uint8_t* smem, const bf16x8 (&qf)[2][8],
+                                                        f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
+                                                        int b, int h) {
+#pragma unroll 1
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const int64_t c0 = a.ch[c].start, c1 = c0 + a.ch[c].len;
+    const int64_t s0 = klo > c0 ? klo : c0, s1 = khi < c1 ? khi : c1;
+    if (s1 <= s0) continue;
+    ChunkDesc cd = a.ch[c];
+    cd.k = reinterpret_cast<const uint16_t*>(cd.k) + (s0 - c0) * cd.k_ss;
+    cd.v = reinterpret_cast<const uint16_t*>(cd.v) + (s0 - c0) * cd.v_ss;
+    cd.len = s1 - s0;
+    run_chunk<kFixed>(a, cd, smem, qf, o, lsum, shift, b, h);
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   // Whole tiles first (XCD-remapped), then the parts of the split tail tiles: part p of a
-  // tail tile takes keys [lo_p, lo_{p+1}) of the chunk, lo_p = 32 * floor(len p / (32 parts)).
+  // tail tile takes keys [lo_p, lo_{p+1}) of the launch's chunk sequence,
+  // lo_p = 32 * floor(call_len p / (32 parts)); a whole tile takes all of them.
   int tile, part = 0;
   if ((int)blockIdx.x < a.n_whole) {
     tile = remap_tile(blockIdx.x, a.n_whole);
@@ -427,13 +490,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
     tile = a.n_whole + u / a.parts;
     part = u % a.parts;
   }
-  ChunkDesc cd = a.ch[0];
-  if (a.parts > 1 && tile >= a.n_whole) {
-    const int64_t lo = cd.len * part / a.parts / kKT * kKT;
-    const int64_t hi = part + 1 == a.parts ? cd.len : cd.len * (part + 1) / a.parts / kKT * kKT;
-    cd.k = reinterpret_cast<const uint16_t*>(cd.k) + lo * cd.k_ss;
-    cd.v = reinterpret_cast<const uint16_t*>(cd.v) + lo * cd.v_ss;
-    cd.len = hi - lo;
+  const bool split = a.parts > 1 && tile >= a.n_whole;
+  int64_t klo = 0, khi = a.call_len;
+  if (split) {
+    klo = a.call_len * part / a.parts / kKT * kKT;
+    khi = part + 1 == a.parts ? a.call_len : a.call_len * (part + 1) / a.parts / kKT * kKT;
   }
   const int qt = tile % a.n_qtiles;
   const int bh = tile / a.n_qtiles;
@@ -505,10 +566,66 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   if (fixed) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + cdot[n];
-    if (cd.len > 0) run_chunk<true>(a, cd, smem, qf, o, lsum, shift, b, h);
+    run_keys<true>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;
-    if (cd.len > 0) run_chunk<false>(a, cd, smem, qf, o, lsum, shift, b, h);
+    run_keys<false>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
+  }
+
+  if (a.final_out && !split) {
+    // The run ends with this launch: merge the workspace's earlier keys (if any), normalise
+    // once ([CM] "Accumulate, then normalize once") and write O, and lse, straight from the
+    // accumulator registers.  The arithmetic is the finalize kernel's: O = acc / l (IEEE
+    // division), bf16 by round-to-nearest-even, lse = ln 2 (r + log2 l).
+    const int64_t tb = (int64_t)tile * (kQTile * kD);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float other = __shfl_xor(lsum[n], 32, 64);
+      const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
+      const int64_t rowi = (int64_t)bh * a.sq_pad + q0 + 32 * n + lq;
+      float lnew = ltot, rnew = shift[n], fw = 0.0f, fo = 1.0f;
+      if (a.accumulate) {
+        const float lp = a.l[rowi], rp = a.r[rowi];
+        if (fixed) {
+          lnew = lp + ltot;
+          fw = 1.0f;
+        } else {
+          rnew = fmaxf(rp, shift[n]);
+          fw = rp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(rp - rnew);
+          fo = shift[n] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(shift[n] - rnew);
+          lnew = lp * fw + ltot * fo;
+        }
+      }
+      const int q = q0 + 32 * n + lq;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
+          if (a.accumulate) {
+            const f32x4 prev =
+                *reinterpret_cast<const f32x4*>(a.acc + tb + ((((wave * 2 + n) * 4 + m) * 4 + jj) * 64 + lane) * 4);
+            if (fixed) v = prev + v;
+            else v = prev * fw + v * fo;
+          }
+          if (q < a.Sq) {
+            const int64_t off = b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + 32 * m + 8 * jj + 4 * hh;
+            const float x0 = __fdiv_rn(v[0], lnew), x1 = __fdiv_rn(v[1], lnew);
+            const float x2 = __fdiv_rn(v[2], lnew), x3 = __fdiv_rn(v[3], lnew);
+            if (a.out_dtype == FIXEDM_F32) {
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{x0, x1, x2, x3};
+            } else {
+              uint2 w;
+              w.x = bf16_rne(x0) | (bf16_rne(x1) << 16);
+              w.y = bf16_rne(x2) | (bf16_rne(x3) << 16);
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w;
+            }
+          }
+        }
+      }
+      if (a.lse != nullptr && hh == 0 && q < a.Sq) a.lse[(int64_t)bh * a.Sq + q] = lse_of(rnew, lnew);
+    }
+    return;
   }
 
   // ---- fold into the workspace: acc in register order (one 1 KB coalesced float4 store

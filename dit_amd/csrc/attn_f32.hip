@@ -14,7 +14,8 @@
 // absolute error.  This path therefore forms each logit q.k and each exponent in fp64
 // (products of fp32 values are exact in fp64) and evaluates 2^e in fp64; the probability
 // is then rounded once to fp32 and, as the method prescribes, accumulated in fp32.
-// One wave per workgroup, one query row per lane; keys are staged through LDS 32 at a time.
+// One wave per workgroup, one query row per lane; keys are staged through LDS 32 at a time,
+// and the launch's chunks are folded one after the other into the same registers.
 #include <math.h>
 
 #include "fixedm_internal.h"
@@ -29,8 +30,8 @@ __device__ void run(const AttnArgs& a, float (&qv)[D], float (&acc)[D], float& l
                     int b, int h, float (*ks)[D], float (*vs)[D]) {
   const int lane = threadIdx.x;
   double shift = (double)r;
-  {
-    const ChunkDesc& cd = a.ch[0];
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const ChunkDesc& cd = a.ch[c];
     const float* kb = reinterpret_cast<const float*>(cd.k) + b * cd.k_sb + h * cd.k_sh;
     const float* vb = reinterpret_cast<const float*>(cd.v) + b * cd.v_sb + h * cd.v_sh;
     for (int64_t key0 = 0; key0 < cd.len; key0 += kKB) {

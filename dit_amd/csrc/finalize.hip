@@ -17,12 +17,6 @@
 namespace fixedm {
 namespace {
 
-__device__ inline uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ inline void store4(const FinalizeArgs& a, int b, int q, int h, int d0, float4 v) {
   if (a.out_dtype == FIXEDM_F32) {
     float* o = reinterpret_cast<float*>(a.out) + b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + d0;
@@ -36,14 +30,12 @@ __device__ inline void store4(const FinalizeArgs& a, int b, int q, int h, int d0
   }
 }
 
-__device__ inline float lse_of(float r, float l) {
-  return 0.69314718055994531f * (r + log2f(l));
-}
-
 // acc in the bf16 kernel's register order: [tile][wave 4][n 2][m 4][j 4][lane 64][4].
+// Tiles tile_begin.. are finalized (all of them, or only the split tail tiles after a
+// launch that wrote the whole tiles' output itself).
 __global__ void finalize_reg_kernel(FinalizeArgs a) {
   const int64_t total = (int64_t)a.B * a.H * a.n_qtiles * 8192;
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t idx = a.tile_begin * 8192 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int64_t tile = idx / 8192;
   const int rem = (int)(idx % 8192);
@@ -104,7 +96,8 @@ __global__ void finalize_row_kernel(FinalizeArgs a) {
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   if (a.reg_layout) {
-    const int64_t total = (int64_t)a.B * a.H * a.n_qtiles * 8192;
+    const int64_t total = ((int64_t)a.B * a.H * a.n_qtiles - a.tile_begin) * 8192;
+    if (total <= 0) return hipSuccess;
     finalize_reg_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
   } else {
     const int64_t total = (int64_t)a.B * a.H * a.Sq * (a.D / 4);

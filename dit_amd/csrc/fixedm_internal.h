@@ -7,7 +7,7 @@
 
 namespace fixedm {
 
-constexpr int kMaxChunksPerLaunch = 1;   // K/V chunks folded by one attention launch
+constexpr int kMaxChunksPerLaunch = 8;   // K/V chunks folded by one attention launch
 constexpr int kMaxBoundsChunks = 32;     // chunks one fixedm_bounds call accepts
 constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (LDS staging)
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
@@ -53,7 +53,8 @@ struct ChunkDesc {
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
   int64_t len;    // real keys in this chunk
-  int64_t start;  // global index of its first key (bounds kernels)
+  int64_t start;  // index of its first key: over all chunks (bounds kernels), or within the
+                  // launch's chunk sequence (attention kernels)
 };
 
 // Device buffer layout of the bounds descriptor (byte offsets, 256-byte aligned).
@@ -101,6 +102,7 @@ struct AttnArgs {
   int64_t q_sb, q_ss, q_sh;
   ChunkDesc ch[kMaxChunksPerLaunch];
   int32_t n_chunks;
+  int64_t call_len;    // keys of all chunks of this launch (their concatenation is split)
   int32_t B, H, D;
   int32_t Sq, n_qtiles, sq_pad;
   int32_t q_block, nqb;
@@ -117,6 +119,14 @@ struct AttnArgs {
   float* acc_x;                // parts 1.. of split tiles: [(tile - n_whole) * (parts - 1) + part - 1]
   float* l_x;
   float* r_x;
+  // Fused finalize (bf16 kernel): when set, this launch completes the run and the whole
+  // tiles write O = acc / l (and lse) straight from registers; split tiles still fold
+  // into the workspace for a finalize over those tiles only.
+  int32_t final_out;
+  int32_t out_dtype;
+  void* out;
+  int64_t o_sb, o_ss, o_sh;
+  float* lse;
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
@@ -132,6 +142,7 @@ struct FinalizeArgs {
   int32_t B, H, D, Sq, n_qtiles, sq_pad;
   int32_t reg_layout;  // 1: acc in the bf16 kernel's register order; 0: row-major [bh][q][d]
   int32_t n_whole, parts;      // split plan of the bf16 launches (reg_layout only)
+  int64_t tile_begin;          // reg_layout: first query tile finalized (the rest follow)
   const float* acc_x;
   const float* l_x;
   const float* r_x;
@@ -139,5 +150,18 @@ struct FinalizeArgs {
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 int device_cus();   // compute units of the current device (cached per device)
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN -> quiet NaN); the output cast of both the
+// finalize kernel and the fused finalize of the bf16 attention kernel.
+__device__ inline uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Natural-log log-sum-exp of a row from its base-2 shift r and its row sum l under r.
+__device__ inline float lse_of(float r, float l) {
+  return 0.69314718055994531f * (r + log2f(l));
+}
 
 }  // namespace fixedm

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfixedm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fixedm.h")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 BF16, F32 = 1, 2
 CENTER = {"none": 0, "supplied": 1, "compute": 2}
 STATUS = {
@@ -52,7 +52,7 @@ class BoundsDesc(ctypes.Structure):
 
 class RunState(ctypes.Structure):
     _fields_ = [("token", ctypes.c_uint64), ("kv_visited", ctypes.c_int64),
-                ("calls", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("calls", ctypes.c_int32), ("finalized", ctypes.c_int32)]
 
 
 class BoundsLayout(ctypes.Structure):
@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
     L.fixedm_attn_fwd.restype = ctypes.c_int
     L.fixedm_attn_fwd.argtypes = [P(BoundsDesc), P(RunState), Tensor, P(Tensor), P(Tensor),
                                   P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.fixedm_attn_fwd_final.restype = ctypes.c_int
+    L.fixedm_attn_fwd_final.argtypes = [P(BoundsDesc), P(RunState), Tensor, P(Tensor), P(Tensor),
+                                        P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, Tensor,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.fixedm_finalize.restype = ctypes.c_int
     L.fixedm_finalize.argtypes = [P(BoundsDesc), P(RunState), ctypes.c_void_p, Tensor,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
@@ -203,6 +207,17 @@ def attn_fwd(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, workspace, 
     _check(st, "fixedm_attn_fwd")
 
 
+def attn_fwd_final(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, workspace, out, lse=None,
+                   stream=None):
+    import torch
+    dt = {torch.bfloat16: BF16, torch.float32: F32}[out.dtype]
+    ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
+    st = lib().fixedm_attn_fwd_final(ctypes.byref(desc), ctypes.byref(run), tensor_desc(q), ks, vs,
+                                     lens, n, _ptr(workspace), tensor_desc(out), dt, _ptr(lse),
+                                     _stream(stream))
+    _check(st, "fixedm_attn_fwd_final")
+
+
 def finalize(desc: BoundsDesc, run: RunState, workspace, out, lse=None, stream=None):
     import torch
     dt = {torch.bfloat16: BF16, torch.float32: F32}[out.dtype]
@@ -241,9 +256,11 @@ def alloc_workspace(p: Problem, device):
 
 def forward(q, k_chunks, v_chunks, *, q_block=256, center="none", k_mean=None,
             softmax_scale=0.0, out_dtype=None, want_lse=False, chunks_per_call=1,
-            stream=None):
+            fused_final=False, stream=None):
     """The whole sequence for one rank: bounds, one fixedm_attn_fwd per ring step (each
-    with `chunks_per_call` chunks), finalize.  Returns (out, lse or None, desc, bounds buf)."""
+    with `chunks_per_call` chunks), finalize; with `fused_final` the last step is
+    fixedm_attn_fwd_final instead of fixedm_attn_fwd + fixedm_finalize.
+    Returns (out, lse or None, desc, bounds buf)."""
     import torch
     B, Sq, H, D = q.shape
     dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}[q.dtype]
@@ -252,10 +269,15 @@ def forward(q, k_chunks, v_chunks, *, q_block=256, center="none", k_mean=None,
     desc, buf = bounds(p, q, k_chunks, v_chunks, k_mean=k_mean, stream=stream)
     ws = alloc_workspace(p, q.device)
     run = run_init(desc)
-    for i in range(0, len(k_chunks), chunks_per_call):
-        attn_fwd(desc, run, q, k_chunks[i:i + chunks_per_call], v_chunks[i:i + chunks_per_call],
-                 ws, stream=stream)
     out = torch.empty((B, Sq, H, D), dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if want_lse else None
-    finalize(desc, run, ws, out, lse, stream=stream)
+    starts = list(range(0, len(k_chunks), chunks_per_call)) or [0]
+    for i in starts:
+        ks, vs = k_chunks[i:i + chunks_per_call], v_chunks[i:i + chunks_per_call]
+        if fused_final and i == starts[-1]:
+            attn_fwd_final(desc, run, q, ks, vs, ws, out, lse, stream=stream)
+        else:
+            attn_fwd(desc, run, q, ks, vs, ws, stream=stream)
+    if not fused_final:
+        finalize(desc, run, ws, out, lse, stream=stream)
     return out, lse, desc, buf

@@ -21,7 +21,9 @@
  *   fixedm_bounds      once per forward: norms, k_mean, U, m, eligibility;
  *   fixedm_run_init    once per forward: resets the host-side ring state;
  *   fixedm_attn_fwd    once per visiting K/V chunk (or once with several chunks);
- *   fixedm_finalize    once (or more): O = acc / l, optional log-sum-exp.
+ *   fixedm_finalize    once (or more): O = acc / l, optional log-sum-exp;
+ * or, for the last chunks of the run, fixedm_attn_fwd_final in place of the last
+ * fixedm_attn_fwd and fixedm_finalize (the final fold and the normalisation in one pass).
  *
  * Conventions shared by every entry point:
  *   - Tensors are described by fixedm_tensor: a device pointer plus element strides for
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FIXEDM_ABI_VERSION 1
+#define FIXEDM_ABI_VERSION 2
 
 typedef enum {
   FIXEDM_OK = 0,
@@ -111,8 +113,9 @@ typedef struct {
 typedef struct {
   uint64_t token;
   int64_t kv_visited;    /* keys folded in so far */
-  int32_t calls;         /* fixedm_attn_fwd calls so far */
-  int32_t reserved;
+  int32_t calls;         /* fixedm_attn_fwd / fixedm_attn_fwd_final calls so far */
+  int32_t finalized;     /* 1 after fixedm_attn_fwd_final: the run is complete and the
+                            workspace no longer holds its whole result */
 } fixedm_run_t;
 
 /* Byte offsets of the arrays fixedm_bounds writes into the descriptor's device buffer.
@@ -166,23 +169,43 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q,
 fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run);
 
 /* One or more ring steps ([CM] Overview ring figure, "The ring loop"): folds n_chunks
- * K/V chunks (in the given order) into the caller's workspace.  The first keys of a run
+ * K/V chunks (in the given order) into the caller's workspace.  Up to 8 chunks of one call
+ * are folded by one launch with the accumulators resident in registers across them.  The first keys of a run
  * initialise the workspace, later ones add to it: pure addition for eligible blocks,
  * the online-softmax rescale merge for the others.  q: [B, sq, H, D] (the same rows the
  * bounds were computed from); chunks as in fixedm_bounds.  workspace: device buffer of
  * fixedm_workspace_bytes() bytes, 256-byte aligned.  Errors: FIXEDM_ERR_BOUNDS_MISMATCH
  * if run->token does not match the descriptor, FIXEDM_ERR_STATE if the keys visited
- * would exceed sk_total.  Updates *run on success. */
+ * would exceed sk_total or the run was completed by fixedm_attn_fwd_final.  Updates *run
+ * on success. */
 fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run,
                               fixedm_tensor q, const fixedm_tensor* k_chunks,
                               const fixedm_tensor* v_chunks, const int64_t* chunk_len,
                               int32_t n_chunks, void* workspace, void* stream);
 
+/* The last ring step(s) of a run fused with the finalize ([CM] "Accumulate, then normalize
+ * once": the last step folds and normalises in one pass; "The ring loop").  Folds
+ * n_chunks K/V chunks like fixedm_attn_fwd, which must bring the run to sk_total keys
+ * (FIXEDM_ERR_STATE otherwise; n_chunks may be 0 with all keys already visited), and
+ * writes out and lse exactly as fixedm_finalize describes.  On the bf16 path the chunks of
+ * the call are folded with the accumulators resident in registers, and each query tile
+ * writes its output rows straight from them; only the split tail tiles (the key-range
+ * parts of the last partial round of tiles) pass through the workspace and a finalize
+ * over those tiles.  On the fp32 path it is fixedm_attn_fwd followed by fixedm_finalize.
+ * Arguments as in those two calls.  Sets run->finalized: a later fixedm_finalize or
+ * fixedm_attn_fwd on this run returns FIXEDM_ERR_STATE. */
+fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t* run,
+                                    fixedm_tensor q, const fixedm_tensor* k_chunks,
+                                    const fixedm_tensor* v_chunks, const int64_t* chunk_len,
+                                    int32_t n_chunks, void* workspace, fixedm_tensor out,
+                                    int32_t out_dtype, float* lse, void* stream);
+
 /* O = acc / l, cast to out_dtype (bf16 by round-to-nearest-even, or fp32), written to
  * out [B, sq, H, D]; if lse is non-NULL also lse[b, h, i] = ln2 * (r_i + log2 l_i), the
  * natural-log log-sum-exp of row i ([CM] Interface table, training output), as a
  * contiguous fp32 [B, H, sq] device array.  Requires run->kv_visited == sk_total
- * (FIXEDM_ERR_STATE otherwise).  Reads the workspace only, so it may be called again. */
+ * and a run not completed by fixedm_attn_fwd_final (FIXEDM_ERR_STATE otherwise).  Reads
+ * the workspace only, so it may be called again. */
 fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run,
                               const void* workspace, fixedm_tensor out, int32_t out_dtype,
                               float* lse, void* stream);

@@ -82,9 +82,10 @@ def test_invalid_problems(kw, code):
     assert e.value.status == code
 
 
-def test_bad_abi_version():
+@pytest.mark.parametrize("version", [1, F.ABI_VERSION + 1, 0])
+def test_bad_abi_version(version):
     p = _p()
-    p.abi_version = 2
+    p.abi_version = version
     assert F.bounds_bytes(p) == 0
 
 
@@ -133,5 +134,9 @@ def test_forged_descriptor_is_rejected(L):
                              lens, 1, 0x100000, None) == -4
     assert L.fixedm_finalize(ctypes.byref(d), ctypes.byref(run), 0x100000, T(0x20000, 0, 5120, 128),
                              1, None, None) == -4
+    assert L.fixedm_attn_fwd_final(ctypes.byref(d), ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc,
+                                   lens, 1, 0x100000, T(0x20000, 0, 5120, 128), 1, None, None) == -4
+    assert L.fixedm_attn_fwd_final(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
+                                   0x100000, T(0x20000, 0, 5120, 128), 1, None, None) == -1
     assert L.fixedm_attn_fwd(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
                              0x100000, None) == -1

@@ -3,8 +3,10 @@
 Bounds (k_mean, Q2, K2, U, m, eligibility) are compared bit for bit on every config; the
 output within the acceptance tolerances (_parity.TOL).  Configs 1, 2 and 5 are compared in
 full; configs 3 and 4 (the Wan 720p rank share and the ragged one) on sampled rows of every
-head, including the ragged last q-block, at the full sizes and in the launch configuration
-the benchmark times (bounds + one fixedm_attn_fwd per ring chunk + finalize)."""
+head, including the ragged last q-block, at the full sizes.  Config 3 runs both as a ring
+rank sees it (bounds + one fixedm_attn_fwd per ring chunk + finalize) and in the launch
+configuration the benchmark times (bounds + one fixedm_attn_fwd_final over the four chunks
+in ring order).  The fused and multi-chunk paths are also run on the edge cases."""
 import numpy as np
 import pytest
 
@@ -27,7 +29,7 @@ def F():
     return fixedm
 
 
-def _run(F, inp, *, q_block=None, order=None, out_dtype=None, want_lse=True):
+def _run(F, inp, *, q_block=None, order=None, out_dtype=None, want_lse=True, **fwd):
     import torch
     wl = inp.wl
     q, ks, vs, km = device_inputs(inp)
@@ -35,7 +37,7 @@ def _run(F, inp, *, q_block=None, order=None, out_dtype=None, want_lse=True):
         ks, vs = [ks[i] for i in order], [vs[i] for i in order]
     out, lse, desc, buf = F.forward(q, ks, vs, q_block=q_block or wl.q_block, center=wl.center,
                                     k_mean=km, out_dtype=out_dtype or torch.float32,
-                                    want_lse=want_lse)
+                                    want_lse=want_lse, **fwd)
     torch.cuda.synchronize()
     return out, lse, desc, buf, (q, ks, vs, km)
 
@@ -148,7 +150,7 @@ def test_config5_adversarial_fp32(F):
 
 # ------------------------------------------------------------------ edge cases --------
 def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_scale=1.0,
-             k_offset=0.0, v_poke=None, loud_rows=None):
+             k_offset=0.0, v_poke=None, loud_rows=None, **fwd):
     import torch
     inp = WL.generic_inputs(seed, dtype, B, H, D, Sq, chunks, q_block=q_block, center=center,
                             q_scale=q_scale, k_offset=k_offset)
@@ -168,7 +170,7 @@ def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_s
         inp.k_mean = None
     q, ks, vs, km = device_inputs(inp)
     out, lse, desc, buf = F.forward(q, ks, vs, q_block=q_block, center=center, k_mean=km,
-                                    out_dtype=torch.float32, want_lse=True)
+                                    out_dtype=torch.float32, want_lse=True, **fwd)
     torch.cuda.synchronize()
     ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=q_block, center=center,
                   k_mean=kmean, dtype=dtype)
@@ -348,3 +350,119 @@ def test_state_contracts(F):
     with pytest.raises(F.FixedmError) as e:
         F.run_init(desc)
     assert e.value.status == -4
+
+
+# ------------------------------------------------------------------ fused final step --
+# One fixedm_attn_fwd_final over every chunk: the accumulators stay in registers across the
+# chunks and the whole query tiles write O and lse themselves.
+FUSED = dict(chunks_per_call=8, fused_final=True)
+
+
+def test_config3_fused_sampled_rows(F, cfg3):
+    """The benchmark's launch configuration: bounds + fixedm_attn_fwd_final over the four ring
+    chunks in rank 0's order (0, 3, 2, 1)."""
+    say("config 3 output, fused final step over the 4 chunks")
+    inp = cfg3
+    out, lse, desc, buf, _ = _run(F, inp, order=(0, 3, 2, 1), **FUSED)
+    check_bounds(gpu_bounds_dict(desc, buf), _oracle_bounds(inp))
+    rows = _sample_rows(inp.wl.sq, 256)
+    ref, lse_ref = O.attention_rows(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1),
+                                    inp.wl.scale, rows)
+    got = out.cpu().numpy()
+    check_output(got[:, rows], ref, "bf16")
+    assert np.abs(lse.cpu().numpy()[:, :, rows] - lse_ref).max() <= LSE_TOL["bf16"]
+    assert np.isfinite(got).all()
+
+
+def test_config2_fused(F):
+    import torch
+    say("config 2, fused final step")
+    inp = WL.make_inputs(2)
+    out, lse, desc, buf, dev = _run(F, inp, **FUSED)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    got = out.cpu().numpy()
+    check_output(got, ref, "bf16")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
+    # the fused bf16 output is the round-to-nearest-even of the fused fp32 output
+    out16, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, out_dtype=torch.bfloat16, **FUSED)
+    bits = out16.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, bf16_rne_bits(got))
+    # per-chunk folds through the workspace: the same result up to fp32 summation order
+    unfused, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, out_dtype=torch.float32)
+    assert np.abs(unfused.cpu().numpy() - got).max() <= 1e-5
+
+
+@pytest.mark.parametrize("name,args,fwd", [
+    ("ragged, all chunks fused", (32, "bf16", 2, 3, 128, 300, (1, 63, 64, 65, 130)),
+     dict(center="compute", k_offset=2.0, **FUSED)),
+    ("ragged, last chunk fused onto folds", (32, "bf16", 2, 3, 128, 300, (1, 63, 64, 65, 130)),
+     dict(center="compute", k_offset=2.0, chunks_per_call=1, fused_final=True)),
+    ("mixed bodies, long chunks", (39, "bf16", 1, 2, 128, 256, (1000, 737)),
+     dict(loud_rows=(1, 128, 192, 14.0), **FUSED)),
+    ("split tail, all chunks fused", (47, "bf16", 1, 37, 128, 2048, (60, 700, 1301)),
+     dict(loud_rows=(35, 0, 64, 14.0), **FUSED)),
+    ("split tail, two per call", (47, "bf16", 1, 37, 128, 2048, (60, 700, 1301)),
+     dict(loud_rows=(35, 0, 64, 14.0), chunks_per_call=2, fused_final=True)),
+    ("loop boundaries and an empty chunk", (44, "bf16", 1, 2, 128, 300, (735, 0, 736, 1000)),
+     dict(center="compute", **FUSED)),
+    ("single key", (31, "bf16", 1, 2, 128, 1, (1,)), FUSED),
+    ("fp32 path", (32, "fp32", 2, 3, 64, 300, (1, 63, 64, 65, 130)),
+     dict(center="compute", k_offset=2.0, **FUSED)),
+])
+def test_fused_and_multichunk_edges(F, name, args, fwd):
+    say(f"fused: {name}")
+    _generic(F, *args, **fwd)
+
+
+def test_more_chunks_than_one_launch(F):
+    """11 chunks in one call: launches of 8 and 3 chunks; the fused call folds the first 8 into
+    the workspace and finishes with the last 3."""
+    import torch
+    say("fused: 11 chunks in one call")
+    chunks = (100, 37, 0, 250, 64, 1, 33, 500, 129, 70, 300)
+    for fwd in (dict(chunks_per_call=11), dict(chunks_per_call=11, fused_final=True)):
+        ob, out = _generic(F, 48, "bf16", 1, 3, 128, 333, chunks, center="compute", **fwd)
+        assert torch.isfinite(out).all()
+
+
+def test_fused_state_sentinel_and_determinism(F):
+    import torch
+    say("fused: state contracts, NaN sentinel, determinism")
+    inp = WL.generic_inputs(49, "bf16", 1, 5, 128, 700, (333, 444), q_block=64)
+    q, ks, vs, _ = device_inputs(inp)
+    p = F.make_problem("bf16", 1, 5, 128, 700, 777, 64)
+    outs = []
+    for _ in range(2):
+        desc, buf = F.bounds(p, q, ks, vs)
+        ws = F.alloc_workspace(p, q.device)
+        run = F.run_init(desc)
+        out = torch.full((1, 700, 5, 128), float("nan"), device="cuda")
+        lse = torch.full((1, 5, 700), float("nan"), device="cuda")
+        with pytest.raises(F.FixedmError) as e:
+            F.attn_fwd_final(desc, run, q, ks[:1], vs[:1], ws, out, lse)   # keys missing
+        assert e.value.status == -5
+        F.attn_fwd_final(desc, run, q, ks, vs, ws, out, lse)
+        assert run.finalized == 1 and run.kv_visited == 777
+        with pytest.raises(F.FixedmError) as e:
+            F.finalize(desc, run, ws, out)                                  # run already complete
+        assert e.value.status == -5
+        with pytest.raises(F.FixedmError) as e:
+            F.attn_fwd(desc, run, q, ks[:1], vs[:1], ws)
+        assert e.value.status == -5
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # all keys folded by fixedm_attn_fwd, then a fused call with no chunk: the finalize alone
+    desc, buf = F.bounds(p, q, ks, vs)
+    ws = F.alloc_workspace(p, q.device)
+    run = F.run_init(desc)
+    F.attn_fwd(desc, run, q, ks, vs, ws)
+    out2 = torch.full((1, 700, 5, 128), float("nan"), device="cuda")
+    F.attn_fwd_final(desc, run, q, [], [], ws, out2)
+    ref = torch.full_like(out2, float("nan"))
+    run2 = F.run_init(desc)
+    F.attn_fwd(desc, run2, q, ks, vs, ws)
+    F.finalize(desc, run2, ws, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref)
