@@ -236,10 +236,10 @@ __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, c
 #include "fixed_loop.inc"
 
 // O^T += V(tile)^T P(tile)^T for a chunk piece of a single tile in the fixed-m body, with the
-// accumulators held in AGPRs as the assembly loop holds them: in a chunk loop a compiled MFMA
-// on O would move the accumulators to architectural registers for the whole loop.  The
-// leading and trailing wait states cover the VALU-write -> MFMA-read and MFMA-write -> read
-// hazards the compiler cannot see across the block.
+// accumulators in the AGPRs the assembly loop keeps them in: in a chunk loop a compiled MFMA
+// on O would move the accumulators to other registers for the whole loop.  The leading and
+// trailing wait states cover the VALU-write -> MFMA-read and MFMA-write -> read hazards the
+// compiler cannot see across the block.
 __device__ __attribute__((always_inline)) inline void pv_tile_asm(f32x16 (&o)[2][4], const bf16x8 (&vf)[2][4],
                                                                   const bf16x8 (&p)[2][2]) {
   asm volatile(
@@ -263,11 +263,63 @@ __device__ __attribute__((always_inline)) inline void pv_tile_asm(f32x16 (&o)[2]
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 3\n"
-      : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-        "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3])
+      : "+{a[0:15]}"(o[0][0]), "+{a[16:31]}"(o[0][1]), "+{a[32:47]}"(o[0][2]), "+{a[48:63]}"(o[0][3]),
+        "+{a[64:79]}"(o[1][0]), "+{a[80:95]}"(o[1][1]), "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3])
       : "v"(vf[0][0]), "v"(vf[0][1]), "v"(vf[0][2]), "v"(vf[0][3]),
         "v"(vf[1][0]), "v"(vf[1][1]), "v"(vf[1][2]), "v"(vf[1][3]),
         "v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]));
+}
+
+// S^T(tile) = K(tile) (alpha Q)^T + init for the fixed-m body, the 16 MFMAs as one asm block
+// with the query fragments in the AGPRs the assembly loop reads them from: the query
+// fragments then keep one home through the chunk loop.  init (in s on entry) is -(m + c_i)
+// for the tile's real keys and -inf for the others.
+__device__ __attribute__((always_inline)) inline void s_tile_asm(f32x16 (&s)[2], const bf16x8 (&kf)[8],
+                                                                 const bf16x8 (&qf)[2][8]) {
+  asm volatile(
+      "s_nop 4\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %18, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %19, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %20, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %5, %21, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %6, %22, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %7, %15, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %23, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %8, %24, %1\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %9, %17, %0\n"
+      "v_mfma_f32_32x32x16_bf16 %1, %9, %25, %1\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 3\n"
+      : "+v"(s[0]), "+v"(s[1])
+      : "v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]), "v"(kf[7]),
+        "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
+        "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]), "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
+        "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]), "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
+        "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]));
+}
+
+__device__ __attribute__((always_inline)) void compute_s_fixed(const uint8_t* smem, const Ring& g, int stage,
+                                                               const bf16x8 (&qf)[2][8], f32x16 (&s)[2],
+                                                               const float (&init)[2], RowRange rows, int hh) {
+  const uint8_t* ks = smem + stage * kTileBytes;
+  bf16x8 kf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = tile_key(r, hh);
+      s[n][r] = key >= rows.lo && key < rows.hi ? init[n] : -INFINITY;
+    }
+  s_tile_asm(s, kf, qf);
 }
 
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
@@ -404,7 +456,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
     const float nshift[2] = {-shift[0], -shift[1]};
     f32x16 s[2];
     bf16x8 p[2][2];
-    compute_s(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
+    compute_s_fixed(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
     ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
     softmax_fixed(s, p, lsum);
     if (n_tiles == 1) {
@@ -413,7 +465,7 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       pv_tile_asm(o, vf, p);
     } else {
       // tiles 1 .. n_tiles-1 and the PV product of the last one: the assembly loop
-      compute_s(smem, g, 1, qf, s, nshift, tile_rows(g, 1), hh);
+      compute_s_fixed(smem, g, 1, qf, s, nshift, tile_rows(g, 1), hh);
       const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
       uint32_t koff[8], voff[4];
 #pragma unroll
@@ -456,6 +508,15 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   barrier();
 }
 
+// Pins the accumulators and the query fragments to the AGPRs the assembly blocks use, at a
+// point of the chunk loop: with these at the top and bottom of every iteration the values keep
+// one home through the loop instead of being copied (and spilled) around each asm block.
+__device__ __attribute__((always_inline)) inline void pin_state(f32x16 (&o)[2][4], bf16x8 (&qf)[2][8]) {
+  asm volatile(""
+               : "+{a[0:15]}"(o[0][0]), "+{a[16:31]}"(o[0][1]), "+{a[32:47]}"(o[0][2]), "+{a[48:63]}"(o[0][3]), "+{a[64:79]}"(o[1][0]), "+{a[80:95]}"(o[1][1]), "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3]),
+                 "+{a[128:131]}"(qf[0][0]), "+{a[132:135]}"(qf[0][1]), "+{a[136:139]}"(qf[0][2]), "+{a[140:143]}"(qf[0][3]), "+{a[144:147]}"(qf[0][4]), "+{a[148:151]}"(qf[0][5]), "+{a[152:155]}"(qf[0][6]), "+{a[156:159]}"(qf[0][7]), "+{a[160:163]}"(qf[1][0]), "+{a[164:167]}"(qf[1][1]), "+{a[168:171]}"(qf[1][2]), "+{a[172:175]}"(qf[1][3]), "+{a[176:179]}"(qf[1][4]), "+{a[180:183]}"(qf[1][5]), "+{a[184:187]}"(qf[1][6]), "+{a[188:191]}"(qf[1][7]));
+}
+
 // Folds keys [klo, khi) of the launch's chunk sequence (the chunks concatenated in call
 // order) into the resident accumulators: one ring pass per chunk piece, the accumulators
 // and the online body's running max carried in registers from piece to piece.
@@ -473,7 +534,9 @@ __device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64
     cd.k = reinterpret_cast<const uint16_t*>(cd.k) + (s0 - c0) * cd.k_ss;
     cd.v = reinterpret_cast<const uint16_t*>(cd.v) + (s0 - c0) * cd.v_ss;
     cd.len = s1 - s0;
+    if (kFixed) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
     run_chunk<kFixed>(a, cd, smem, qf, o, lsum, shift, b, h);
+    if (kFixed) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
   }
 }
 
