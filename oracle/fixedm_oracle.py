@@ -27,7 +27,10 @@ Readings taken where the pages leave a step open (listed again in the design doc):
   * q-blocks are consecutive runs of ``q_block`` real query rows; the last one is short;
   * sums over d run in index order; sums over keys run in chunk order, then position;
   * k_mean is fp32(sum_j k_j / N) with the sum and the division in fp64;
-  * non-finite U: ineligible and m = INT32_MAX.
+  * non-finite U: ineligible and m = INT32_MAX;
+  * per-row shifts (the per-query-row bound of [CM]): m_i = ceil(U_i) - C(N) with
+    U_i = alpha * sqrt(||q_i||^2 * K2); eligibility stays per q-block (every row of the
+    block must pass the same gate, i.e. the block's loudest row decides).
 
 Parity status: every public function below is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` (printed constants, closed forms, brute force, invariants).
@@ -104,6 +107,10 @@ class Bounds:
     elig: np.ndarray       # [B, H, nQB] bool
     v_ok: bool
     v_absmax: float
+    shift: str = "block"   # "block": one shift per (b, h, q-block); "row": one per query row
+    q2_row: np.ndarray | None = None   # [B, H, Sq] float64: sum_d q_id^2 (shift == "row")
+    u_row: np.ndarray | None = None    # [B, H, Sq] float64: alpha * sqrt(q2_row * k2)
+    m_row: np.ndarray | None = None    # [B, H, Sq] int64: ceil(u_row) - C
 
 
 def k_mean_of(k_chunks) -> np.ndarray:
@@ -130,8 +137,16 @@ def _rowsum_sq_in_order(x: np.ndarray) -> np.ndarray:
     return acc
 
 
+def _shift_of(u: np.ndarray, C: int) -> np.ndarray:
+    """m = ceil(u) - C as int64; INT32_MAX where u is not finite or m leaves int32."""
+    finite = np.isfinite(u)
+    m = np.full(u.shape, INT32_MAX, dtype=np.int64)
+    m[finite] = np.ceil(u[finite]).astype(np.int64) - C
+    return np.where((m > INT32_MAX) | (m < -INT32_MAX - 1), INT32_MAX, m)
+
+
 def bounds(q, k_chunks, v_chunks, *, scale: float, q_block: int, center: str = "none",
-           k_mean=None, dtype: str = "bf16") -> Bounds:
+           k_mean=None, dtype: str = "bf16", shift: str = "block") -> Bounds:
     """Per-(b, h, q-block) shift and eligibility ([FM] Summary equations).
 
     center: "none" (k_mean = 0), "supplied" (the given fp32 [B,H,D] mean) or "compute"
@@ -143,7 +158,16 @@ def bounds(q, k_chunks, v_chunks, *, scale: float, q_block: int, center: str = "
       elig = v_ok and dtype in {bf16, fp32} and U <= gate and U finite
     with v_ok = (max |v| <= 256), taken over the whole V ([FM] review thread on the
     V check; commit message, contract 2) and dtype safety from the same commit message.
+
+    shift="row" adds the per-query-row bound of [CM] "Picking a max that is safe without
+    measuring it" (the row's own norm times the largest key norm; Best practices, "Give each
+    query row its own bound") in the same base-2, integer-shift form:
+      U_i = alpha * sqrt(Q2_i * K2) with Q2_i = sum_d q_id^2,   m_i = ceil(U_i) - C(N).
+    Row i's shifted exponents then lie in [C - U_i - ceil(U_i), C], so the gate condition is
+    the same per row; the body is chosen per q-block, so eligibility stays the block's.
     """
+    if shift not in ("block", "row"):
+        raise ValueError(f"unknown shift granularity {shift!r}")
     q = np.asarray(q, dtype=np.float64)
     kc = [np.asarray(c, dtype=np.float64) for c in k_chunks]
     vc = [np.asarray(c, dtype=np.float64) for c in v_chunks]
@@ -192,11 +216,14 @@ def bounds(q, k_chunks, v_chunks, *, scale: float, q_block: int, center: str = "
     dtype_ok = dtype in ("bf16", "fp32")
 
     finite = np.isfinite(u)
-    m = np.full(u.shape, INT32_MAX, dtype=np.int64)
-    m[finite] = np.ceil(u[finite]).astype(np.int64) - C
-    m = np.where((m > INT32_MAX) | (m < -INT32_MAX - 1), INT32_MAX, m)
+    m = _shift_of(u, C)
     elig = finite & (u <= gate) & v_ok & dtype_ok
-    return Bounds(L, C, W, gate, n, kbar, q2, k2, u, m, elig, bool(v_ok), vabs)
+    bnd = Bounds(L, C, W, gate, n, kbar, q2, k2, u, m, elig, bool(v_ok), vabs, shift)
+    if shift == "row":
+        bnd.q2_row = np.ascontiguousarray(qn.transpose(0, 2, 1))          # [B, H, Sq]
+        bnd.u_row = alpha * np.sqrt(bnd.q2_row * k2[:, :, None])
+        bnd.m_row = _shift_of(bnd.u_row, C)
+    return bnd
 
 
 # --------------------------------------------------------------------------------------
@@ -280,25 +307,28 @@ def softmax_mass(q, k, scale: float, lse):
 # --------------------------------------------------------------------------------------
 # Emulations of the two accumulation bodies (self-checks of the method)
 # --------------------------------------------------------------------------------------
-def fixed_m_emulate(q, k_chunks, v_chunks, *, scale: float, k_mean, m: int, C: int,
+def fixed_m_emulate(q, k_chunks, v_chunks, *, scale: float, k_mean, m, C: int,
                     check_window: bool = True):
     """The eligible body for one (b, h, q-block) on one head ([FM] Summary; [CM] "A static
     bound makes the ring reduction pure addition", "Accumulate, then normalize once").
 
-    q [R, D]; chunks [Sc, D] in visit order; k_mean [D]; integer shift m.
+    q [R, D]; chunks [Sc, D] in visit order; k_mean [D]; integer shift m: one for the block,
+    or an array of R per-row shifts.
     Per key j: e_ij = alpha * q_i . (k_j - k_mean) - m;  p = 2^e;  acc += p v_j;  l += p.
     The chunks merge by pure addition (the first visit initialises), then O = acc / l.
     Returns (O, lse, e_min, e_max) with lse = ln2 * (m + alpha q_i.k_mean + log2 l)."""
     alpha = alpha_of(scale)
     qa = alpha * np.asarray(q, dtype=np.float64)
     kbar = np.asarray(k_mean, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    m_col = m[:, None] if m.ndim == 1 else m
     acc = None
     l = None
     e_min, e_max = math.inf, -math.inf
     for kc, vc in zip(k_chunks, v_chunks):
         kc = np.asarray(kc, dtype=np.float64)
         vc = np.asarray(vc, dtype=np.float64)
-        e = qa @ (kc - kbar).T - m
+        e = qa @ (kc - kbar).T - m_col
         if e.size:
             e_min = min(e_min, float(e.min()))
             e_max = max(e_max, float(e.max()))
@@ -363,9 +393,11 @@ def method_forward(q, k_chunks, v_chunks, bnd: Bounds, *, scale: float, q_block:
                 lo, hi = beta * q_block, min((beta + 1) * q_block, Sq)
                 qb = q[b, lo:hi, h, :]
                 if bnd.elig[b, h, beta]:
+                    shift = (bnd.m_row[b, h, lo:hi] if bnd.m_row is not None
+                             else int(bnd.m[b, h, beta]))
                     o, ls, e0, e1 = fixed_m_emulate(qb, kh, vh, scale=scale,
                                                     k_mean=bnd.k_mean[b, h],
-                                                    m=int(bnd.m[b, h, beta]), C=bnd.C)
+                                                    m=shift, C=bnd.C)
                     windows.append((b, h, beta, e0, e1))
                 else:
                     o, ls = online_softmax_emulate(qb, kh, vh, scale=scale, block=block)

@@ -157,6 +157,79 @@ def test_bounds_bruteforce(center):
         assert bool(b.elig[bb, h, beta]) == (u <= gate)
 
 
+@pytest.mark.parametrize("center", ["none", "compute"])
+def test_row_bounds_bruteforce(center):
+    """Per-row shifts ([CM] "Picking a max that is safe without measuring it": each query
+    row's own norm times the largest key norm) against pure-Python loops."""
+    inp = WL.generic_inputs(12, "bf16", 1, 2, 8, 19, (9, 5), q_block=8, center=center,
+                            k_offset=1.5 if center != "none" else 0.0)
+    q, kc, vc = inp.q, inp.k, inp.v
+    scale = 0.3
+    b = O.bounds(q, kc, vc, scale=scale, q_block=8, center=center, shift="row")
+    L, C, W, gate = O.constants(14)
+    for h in range(2):
+        k2 = b.k2[0, h]
+        for i in range(19):
+            s = 0.0
+            for d in range(8):
+                s += float(q[0, i, h, d]) ** 2
+            u = float(np.float32(scale)) * 1.4426950408889634 * math.sqrt(s * k2)
+            assert b.q2_row[0, h, i] == s
+            assert b.u_row[0, h, i] == u
+            assert b.m_row[0, h, i] == math.ceil(u) - C
+
+
+@pytest.mark.parametrize("q_block", [64, 128, 256])
+def test_row_shift_max_over_block_is_block_shift(q_block):
+    """ceil, sqrt and products are monotone, so the block's bound is its loudest row's bound:
+    max over a block's rows of U_i and m_i equal the block's U and m exactly, and the
+    eligibility (decided per block) is the same in both modes."""
+    inp = WL.generic_inputs(13, "bf16", 2, 3, 32, 300, (130, 77), q_block=q_block,
+                            center="compute", k_offset=2.0, q_scale=1.7)
+    q = inp.q.astype(np.float64)
+    q[:, 40:50, 1] *= 9.0                   # a few loud rows in one head
+    blk = O.bounds(q, inp.k, inp.v, scale=0.2, q_block=q_block, center="compute")
+    row = O.bounds(q, inp.k, inp.v, scale=0.2, q_block=q_block, center="compute", shift="row")
+    assert np.array_equal(blk.m, row.m) and np.array_equal(blk.elig, row.elig)
+    for beta in range(blk.m.shape[2]):
+        lo, hi = beta * q_block, min((beta + 1) * q_block, 300)
+        assert np.array_equal(row.u_row[:, :, lo:hi].max(axis=2), blk.u[:, :, beta])
+        assert np.array_equal(row.m_row[:, :, lo:hi].max(axis=2), blk.m[:, :, beta])
+    assert (row.m_row <= np.repeat(blk.m, q_block, axis=2)[:, :, :300]).all()
+
+
+def test_row_shift_closed_form_and_headroom():
+    """Rows along one direction with norms n_i against keys +-e0 (max norm 1, no centring):
+    U_i = alpha n_i, m_i = ceil(alpha n_i) - C, and each row's largest shifted exponent
+    alpha n_i - m_i lies in (C - 1, C]; under the block shift the quiet rows sit
+    ceil(U_max) - ceil(U_i) further down (the overshoot [CM] Best practices warns about)."""
+    D, norms = 4, [0.5, 3.25, 17.0, 60.5]
+    scale = 0.125
+    alpha = float(np.float32(scale)) * 1.4426950408889634
+    q = np.zeros((1, len(norms), 1, D))
+    for i, n in enumerate(norms):
+        q[0, i, 0, 0] = n
+    k = np.zeros((1, 2, 1, D))
+    k[0, 0, 0, 0], k[0, 1, 0, 0] = 1.0, -1.0
+    v = np.ones((1, 2, 1, D))
+    row = O.bounds(q, [k], [v], scale=scale, q_block=64, shift="row", dtype="fp32")
+    L, C, W, gate = O.constants(2)
+    assert row.C == C
+    for i, n in enumerate(norms):
+        assert row.m_row[0, 0, i] == math.ceil(alpha * n) - C
+    o, lse, windows = O.method_forward(q, [k], [v], row, scale=scale, q_block=64)
+    _, _, e0, e1 = O.fixed_m_emulate(q[0, :, 0], [k[0, :, 0]], [v[0, :, 0]], scale=scale,
+                                     k_mean=np.zeros(D), m=row.m_row[0, 0], C=C)
+    assert C - 1 < e1 <= C
+    for i, n in enumerate(norms):
+        e_top = alpha * n - row.m_row[0, 0, i]
+        assert C - 1 < e_top <= C
+        e_blk = alpha * n - row.m[0, 0, 0]
+        assert e_blk == pytest.approx(e_top - (row.m[0, 0, 0] - row.m_row[0, 0, i]))
+    ref, lse_ref = O.attention(q, k, v, scale)
+    assert np.max(np.abs(o - ref)) < 1e-12 and np.max(np.abs(lse - lse_ref)) < 1e-12
+
+
 def test_v_bound_inclusive_and_nan():
     q = np.ones((1, 4, 1, 4))
     k = [np.ones((1, 5, 1, 4))]
@@ -301,6 +374,32 @@ def test_method_forward_mixed_bodies_and_centring():
     assert b.elig[0, :2].all() and not b.elig[0, 2].any()
     o, lse, windows = O.method_forward(q, inp.k, inp.v, b, scale=scale, q_block=64, block=16)
     ref, lse_ref = O.attention(q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), scale)
+    assert np.max(np.abs(o - ref)) < 1e-11 and np.max(np.abs(lse - lse_ref)) < 1e-11
+
+
+@pytest.mark.parametrize("q_block", [64, 256])
+def test_method_forward_row_shift(q_block):
+    """The whole method with per-row shifts equals softmax attention, and every eligible
+    row's shifted exponents stay inside [-125, C], on the tiny config and on offset keys with
+    centring and a loud head that falls back."""
+    inp = WL.make_inputs(1)
+    wl = inp.wl
+    b = O.bounds(inp.q, inp.k, inp.v, scale=wl.scale, q_block=q_block, shift="row")
+    o, lse, windows = O.method_forward(inp.q, inp.k, inp.v, b, scale=wl.scale, q_block=q_block)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), wl.scale)
+    assert np.max(np.abs(o - ref)) < 1e-12 and np.max(np.abs(lse - lse_ref)) < 1e-12
+    assert len(windows) == b.elig.sum() > 0
+    for (_, _, _, e0, e1) in windows:
+        assert e0 >= -125 and e1 <= b.C
+    inp = WL.generic_inputs(21, "fp32", 1, 3, 16, 70, (40, 33), q_block=64, k_offset=3.0)
+    q = inp.q.astype(np.float64)
+    q[:, :, 2] *= 60.0
+    q[:, 5:9, 0] *= 4.0
+    b = O.bounds(q, inp.k, inp.v, scale=0.25, q_block=64, center="compute", dtype="fp32", shift="row")
+    assert b.elig[0, :2].all() and not b.elig[0, 2].any()
+    assert len(set(b.m_row[0, 0].tolist())) > 1
+    o, lse, _ = O.method_forward(q, inp.k, inp.v, b, scale=0.25, q_block=64, block=16)
+    ref, lse_ref = O.attention(q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), 0.25)
     assert np.max(np.abs(o - ref)) < 1e-11 and np.max(np.abs(lse - lse_ref)) < 1e-11
 
 
