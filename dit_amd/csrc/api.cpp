@@ -35,6 +35,7 @@ fixedm_status check_problem(const fixedm_problem* p) {
     return FIXEDM_ERR_INVALID_ARGUMENT;
   if (p->center < FIXEDM_CENTER_NONE || p->center > FIXEDM_CENTER_COMPUTE)
     return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (p->shift != FIXEDM_SHIFT_BLOCK && p->shift != FIXEDM_SHIFT_ROW) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (!(p->softmax_scale >= 0.0f) || !isfinite(p->softmax_scale)) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (p->dtype == FIXEDM_BF16 && p->head_dim != 128) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   if (p->dtype == FIXEDM_F32 && p->head_dim != 64 && p->head_dim != 128) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
@@ -110,6 +111,7 @@ uint64_t descriptor_token(const fixedm_bounds_t& b) {
   h = fnv1a(h, &p.q_block, sizeof p.q_block);
   h = fnv1a(h, &p.softmax_scale, sizeof p.softmax_scale);
   h = fnv1a(h, &p.center, sizeof p.center);
+  h = fnv1a(h, &p.shift, sizeof p.shift);
   h = fnv1a(h, &b.log2_n, sizeof b.log2_n);
   h = fnv1a(h, &b.C, sizeof b.C);
   h = fnv1a(h, &b.W, sizeof b.W);
@@ -155,6 +157,10 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out) {
   out->k2 = off; off = align256(off + bh * 8);
   out->k_mean = off; off = align256(off + bh * (size_t)p.head_dim * 4);
   out->v_bad = off; off = align256(off + 4);
+  const size_t rows = p.shift == FIXEDM_SHIFT_ROW ? bh * (size_t)p.sq : 0;
+  out->m_row = off; off = align256(off + rows * 4);
+  out->q2_row = off; off = align256(off + rows * 8);
+  out->u_row = off; off = align256(off + rows * 8);
   out->scratch = off;
   if (p.center == FIXEDM_CENTER_COMPUTE)
     off = align256(off + (size_t)kmean_slabs(p.batch, p.heads, p.sk_total) * bh * p.head_dim * 8);
@@ -236,7 +242,8 @@ fixedm_status fixedm_bounds_layout(const fixedm_problem* p, fixedm_bounds_layout
   BoundsLayout l;
   bounds_layout(*p, &l);
   out->m = l.m; out->elig = l.elig; out->u = l.u; out->q2 = l.q2; out->k2 = l.k2;
-  out->k_mean = l.k_mean; out->v_bad = l.v_bad; out->scratch = l.scratch; out->total = l.total;
+  out->k_mean = l.k_mean; out->v_bad = l.v_bad; out->m_row = l.m_row; out->q2_row = l.q2_row;
+  out->u_row = l.u_row; out->scratch = l.scratch; out->total = l.total;
   return FIXEDM_OK;
 }
 
@@ -304,6 +311,11 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixe
   a.v_bad = reinterpret_cast<int32_t*>(base + lay.v_bad);
   a.kpart = reinterpret_cast<double*>(base + lay.scratch);
   a.kslabs = kmean_slabs(p->batch, p->heads, p->sk_total);
+  if (p->shift == FIXEDM_SHIFT_ROW) {
+    a.m_row = reinterpret_cast<int32_t*>(base + lay.m_row);
+    a.q2_row = reinterpret_cast<double*>(base + lay.q2_row);
+    a.u_row = reinterpret_cast<double*>(base + lay.u_row);
+  }
   if (launch_bounds(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
   *out = d;
   return FIXEDM_OK;
@@ -373,6 +385,7 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.Sq = (int32_t)p.sq; a.n_qtiles = (int32_t)wl.n_qtiles; a.sq_pad = (int32_t)wl.sq_pad;
   a.q_block = (int32_t)p.q_block; a.nqb = (int32_t)bounds->n_qblocks;
   a.m = reinterpret_cast<const int32_t*>(bbase + lay.m);
+  a.m_row = p.shift == FIXEDM_SHIFT_ROW ? reinterpret_cast<const int32_t*>(bbase + lay.m_row) : nullptr;
   a.elig = reinterpret_cast<const uint8_t*>(bbase + lay.elig);
   a.k_mean = reinterpret_cast<const float*>(bbase + lay.k_mean);
   a.alpha = bounds->alpha;

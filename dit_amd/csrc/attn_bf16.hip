@@ -627,8 +627,16 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   float lsum[2] = {0.0f, 0.0f};
   float shift[2];
   if (fixed) {
+    // the fixed shift: the q-block's m, or (per-row shifts) each query row's own m
 #pragma unroll
-    for (int n = 0; n < 2; ++n) shift[n] = (float)mshift + cdot[n];
+    for (int n = 0; n < 2; ++n) {
+      int mm = mshift;
+      if (a.m_row != nullptr) {
+        const int row = q0 + 32 * n + lq < a.Sq ? q0 + 32 * n + lq : a.Sq - 1;
+        mm = a.m_row[(int64_t)bh * a.Sq + row];
+      }
+      shift[n] = (float)mm + cdot[n];
+    }
     run_keys<true>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;

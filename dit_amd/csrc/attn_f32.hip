@@ -100,7 +100,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
   float l = 0.0f, r;
   if (fixed) {
-    r = (float)((double)a.m[bq] + a.alpha64 * dot);
+    const int32_t mm = a.m_row != nullptr ? a.m_row[(int64_t)bh * a.Sq + rowc] : a.m[bq];
+    r = (float)((double)mm + a.alpha64 * dot);
     run<D, true>(a, qv, acc, l, r, b, h, ks, vs);
   } else {
     r = -INFINITY;

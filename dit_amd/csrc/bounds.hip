@@ -336,6 +336,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void qnorm_kernel(Boun
     RowRegs<T> qr;
     transpose_rows<P>(qv, area, lane, qr.p);
     const double ss = row_sumsq<T>(qr, D);
+    if (a.q2_row != nullptr && lane < nrows) a.q2_row[((int64_t)b * a.H + h) * a.Sq + i0 + lane] = ss;
     unsigned long long best = lane < nrows ? (unsigned long long)__double_as_longlong(ss) : 0ull;
     best = wave_max_u64(best);
     if (lane == 0) atomicMax(a.q2 + ((int64_t)b * a.H + h) * a.nqb + i0 / a.q_block, best);
@@ -360,6 +361,24 @@ __global__ void gate_kernel(BoundsArgs a) {
   a.u[i] = u;
   a.m[i] = m;
   a.elig[i] = (uint8_t)((*a.v_bad == 0) && finite && (u <= (double)a.gate));
+}
+
+// Per-row shifts: U_i = alpha64 * sqrt(Q2_i * K2); m_i = ceil(U_i) - C (the block formula on
+// one row's norm; INT32_MAX when U_i is not finite or m_i leaves int32).
+__global__ void gate_row_kernel(BoundsArgs a) {
+  const int64_t n = (int64_t)a.B * a.H * a.Sq;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t bh = i / a.Sq;
+  const double k2 = __longlong_as_double((long long)a.k2[bh]);
+  const double u = __dmul_rn(a.alpha64, __dsqrt_rn(__dmul_rn(a.q2_row[i], k2)));
+  int32_t m = INT32_MAX;
+  if (isfinite(u)) {
+    const double mc = ceil(u) - (double)a.C;
+    if (mc >= -2147483648.0 && mc <= 2147483647.0) m = (int32_t)mc;
+  }
+  a.u_row[i] = u;
+  a.m_row[i] = m;
 }
 
 template <typename T>
@@ -397,6 +416,10 @@ hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s) {
   if (a.dtype == FIXEDM_BF16) launch_typed<uint16_t>(a, s);
   else launch_typed<float>(a, s);
   gate_kernel<<<(unsigned)((nqb_all + 255) / 256), 256, 0, s>>>(a);
+  if (a.m_row != nullptr) {
+    const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+    gate_row_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

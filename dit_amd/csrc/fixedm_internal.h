@@ -59,7 +59,7 @@ struct ChunkDesc {
 
 // Device buffer layout of the bounds descriptor (byte offsets, 256-byte aligned).
 struct BoundsLayout {
-  size_t m, elig, u, q2, k2, k_mean, v_bad, scratch, total;
+  size_t m, elig, u, q2, k2, k_mean, v_bad, m_row, q2_row, u_row, scratch, total;
 };
 bool bounds_layout(const fixedm_problem& p, BoundsLayout* out);
 
@@ -94,6 +94,10 @@ struct BoundsArgs {
   int32_t* v_bad;
   double* kpart;            // [kslabs][B*H][D] partial key sums
   int32_t kslabs;
+  // per-row shifts (shift == FIXEDM_SHIFT_ROW; null otherwise): [B, H, Sq]
+  int32_t* m_row;
+  double* q2_row;
+  double* u_row;
 };
 hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
 
@@ -107,6 +111,7 @@ struct AttnArgs {
   int32_t Sq, n_qtiles, sq_pad;
   int32_t q_block, nqb;
   const int32_t* m;
+  const int32_t* m_row;   // per-row shifts [B, H, Sq], or null for one shift per q-block
   const uint8_t* elig;
   const float* k_mean;
   float alpha;       // fp32(scale * log2 e)

@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fixedm.h")
 ABI_VERSION = 2
 BF16, F32 = 1, 2
 CENTER = {"none": 0, "supplied": 1, "compute": 2}
+SHIFT = {"block": 0, "row": 1}
 STATUS = {
     0: "FIXEDM_OK", -1: "FIXEDM_ERR_INVALID_ARGUMENT", -2: "FIXEDM_ERR_UNSUPPORTED_DTYPE",
     -3: "FIXEDM_ERR_UNSUPPORTED_SHAPE", -4: "FIXEDM_ERR_BOUNDS_MISMATCH", -5: "FIXEDM_ERR_STATE",
@@ -40,7 +41,8 @@ class Problem(ctypes.Structure):
                 ("batch", ctypes.c_int64), ("heads", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("sq", ctypes.c_int64),
                 ("sk_total", ctypes.c_int64), ("q_block", ctypes.c_int64),
-                ("softmax_scale", ctypes.c_float), ("center", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("center", ctypes.c_int32),
+                ("shift", ctypes.c_int32)]
 
 
 class BoundsDesc(ctypes.Structure):
@@ -57,7 +59,8 @@ class RunState(ctypes.Structure):
 
 class BoundsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("m", "elig", "u", "q2", "k2", "k_mean", "v_bad", "scratch", "total")]
+                ("m", "elig", "u", "q2", "k2", "k_mean", "v_bad", "m_row", "q2_row", "u_row",
+                 "scratch", "total")]
 
 
 _lib = None
@@ -123,11 +126,12 @@ def constants(n: int):
 
 
 def make_problem(dtype, batch, heads, head_dim, sq, sk_total, q_block=256, softmax_scale=0.0,
-                 center="none") -> Problem:
+                 center="none", shift="block") -> Problem:
     dt = {"bf16": BF16, "fp32": F32}.get(dtype, dtype)
     c = CENTER.get(center, center)
+    sh = SHIFT.get(shift, shift)
     return Problem(ABI_VERSION, dt, batch, heads, head_dim, sq, sk_total, q_block,
-                   softmax_scale, c)
+                   softmax_scale, c, sh)
 
 
 def bounds_bytes(p: Problem) -> int:
@@ -237,7 +241,16 @@ def read_bounds(desc: BoundsDesc, buf) -> dict:
         width = torch.tensor([], dtype=dtype).element_size()
         return buf[off:off + n * width].view(dtype)
 
+    rows = {}
+    if p.shift == SHIFT["row"]:
+        n = bh * p.sq
+        rows = {
+            "m_row": view(lay.m_row, n, torch.int32).view(p.batch, p.heads, p.sq),
+            "q2_row": view(lay.q2_row, n, torch.float64).view(p.batch, p.heads, p.sq),
+            "u_row": view(lay.u_row, n, torch.float64).view(p.batch, p.heads, p.sq),
+        }
     return {
+        **rows,
         "m": view(lay.m, bh * nqb, torch.int32).view(p.batch, p.heads, nqb),
         "elig": view(lay.elig, bh * nqb, torch.uint8).view(p.batch, p.heads, nqb),
         "u": view(lay.u, bh * nqb, torch.float64).view(p.batch, p.heads, nqb),
@@ -256,7 +269,7 @@ def alloc_workspace(p: Problem, device):
 
 def forward(q, k_chunks, v_chunks, *, q_block=256, center="none", k_mean=None,
             softmax_scale=0.0, out_dtype=None, want_lse=False, chunks_per_call=1,
-            fused_final=False, stream=None):
+            fused_final=False, shift="block", stream=None):
     """The whole sequence for one rank: bounds, one fixedm_attn_fwd per ring step (each
     with `chunks_per_call` chunks), finalize; with `fused_final` the last step is
     fixedm_attn_fwd_final instead of fixedm_attn_fwd + fixedm_finalize.
@@ -265,7 +278,7 @@ def forward(q, k_chunks, v_chunks, *, q_block=256, center="none", k_mean=None,
     B, Sq, H, D = q.shape
     dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}[q.dtype]
     N = sum(int(k.shape[1]) for k in k_chunks)
-    p = make_problem(dtype, B, H, D, Sq, N, q_block, softmax_scale, center)
+    p = make_problem(dtype, B, H, D, Sq, N, q_block, softmax_scale, center, shift)
     desc, buf = bounds(p, q, k_chunks, v_chunks, k_mean=k_mean, stream=stream)
     ws = alloc_workspace(p, q.device)
     run = run_init(desc)

@@ -74,6 +74,14 @@ typedef enum {
   FIXEDM_CENTER_COMPUTE = 2   /* mean of the real keys of all chunks, fp64 sum, fp32 result */
 } fixedm_center;
 
+/* Granularity of the fixed shift m.  BLOCK: one m per (batch, head, q-block) ([FM]
+ * Summary).  ROW: one m per query row from that row's own norm, the per-query-row bound of
+ * [CM] "Picking a max that is safe without measuring it" (Best practices: "Give each query
+ * row its own bound"), in the same base-2 integer form m_i = ceil(U_i) - C(N).  In both
+ * modes eligibility is decided per q-block: the body is chosen per block, and a block
+ * passes when its loudest row does. */
+typedef enum { FIXEDM_SHIFT_BLOCK = 0, FIXEDM_SHIFT_ROW = 1 } fixedm_shift;
+
 typedef struct {
   const void* ptr;  /* device pointer to element [0, 0, 0, 0] */
   int64_t stride_b; /* element strides; the head_dim axis has stride 1 */
@@ -92,6 +100,7 @@ typedef struct {
   int64_t q_block;       /* rows per shift/eligibility block: positive multiple of 64 */
   float softmax_scale;   /* s; 0 selects fp32(1/sqrt(D)) ([CM] Interface table) */
   int32_t center;        /* fixedm_center */
+  int32_t shift;         /* fixedm_shift */
 } fixedm_problem;
 
 /* Filled by fixedm_bounds; the caller owns it and must not modify it afterwards. */
@@ -122,9 +131,12 @@ typedef struct {
  * m: int32 [B, H, nQB]; elig: uint8 [B, H, nQB] (1 = fixed-m body); u: fp64 [B, H, nQB];
  * q2: fp64 [B, H, nQB] (max of sum_d q^2 over the block's real rows); k2: fp64 [B, H]
  * (max of sum_d (k - k_mean)^2 over all keys); k_mean: fp32 [B, H, D]; v_bad: int32
- * (count of V elements with !(|v| <= 256); v_ok = (v_bad == 0)). */
+ * (nonzero when some V element has !(|v| <= 256); v_ok = (v_bad == 0)).  With
+ * shift == FIXEDM_SHIFT_ROW also m_row: int32 [B, H, sq] (m_i = ceil(u_i) - C), q2_row:
+ * fp64 [B, H, sq] (sum_d q_id^2) and u_row: fp64 [B, H, sq] (alpha64 * sqrt(q2_i * k2));
+ * in BLOCK mode these three arrays are empty (their offsets equal the next one's). */
 typedef struct {
-  size_t m, elig, u, q2, k2, k_mean, v_bad, scratch, total;
+  size_t m, elig, u, q2, k2, k_mean, v_bad, m_row, q2_row, u_row, scratch, total;
 } fixedm_bounds_layout_t;
 
 /* Size of the device buffer fixedm_bounds needs, or 0 if the problem is invalid. */
@@ -153,7 +165,9 @@ fixedm_status fixedm_constants(int64_t n, int32_t* log2_n, int32_t* C, int32_t* 
  *   q2[b,h,beta] = max over the block's real rows of sum_d q_d^2        (fp64);
  *   k2[b,h]      = max over all keys of all chunks of sum_d (k_d - k_mean_d)^2 (fp64);
  *   u  = alpha64 * sqrt(q2 * k2), alpha64 = fp64(s) * log2(e);  m = ceil(u) - C;
- *   elig = (no |v| > 256 anywhere in V) && u <= gate && u finite.
+ *   elig = (no |v| > 256 anywhere in V) && u <= gate && u finite;
+ *   shift == ROW: per query row also u_i = alpha64 * sqrt(q2_i * k2), m_i = ceil(u_i) - C,
+ *   and the attention calls shift row i by m_i (eligibility stays the block's).
  * q: [B, sq, H, D]; k_chunks/v_chunks: n_chunks tensors of [B, chunk_len[c], H, D];
  * sum(chunk_len) must equal p->sk_total.  k_mean_in: device fp32 [B, H, D] contiguous,
  * required iff center == SUPPLIED.  bounds_dev: device buffer of fixedm_bounds_bytes(p)

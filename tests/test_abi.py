@@ -55,6 +55,11 @@ def test_sizes_of_valid_problems():
     ws = F.workspace_bytes(p)
     assert ws >= rows * (128 + 2) * 4 and ws % 256 == 0
     assert F.bounds_bytes(_p(dtype="fp32", head_dim=64, center="none")) > 0
+    assert (lay.m_row, lay.q2_row, lay.u_row) == (lay.scratch,) * 3      # block mode: empty
+    r = F.bounds_layout(_p(shift="row"))
+    assert r.q2_row - r.m_row >= 40 * 18900 * 4 and r.u_row - r.q2_row >= 40 * 18900 * 8
+    assert r.scratch - r.u_row >= 40 * 18900 * 8 and all(o % 256 == 0 for o in (r.m_row, r.q2_row, r.u_row))
+    assert F.workspace_bytes(_p(shift="row")) == ws
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -69,6 +74,8 @@ def test_sizes_of_valid_problems():
     (dict(sq=-1), -1),
     (dict(sk_total=0), -1),
     (dict(center=5), -1),
+    (dict(shift=2), -1),
+    (dict(shift=-1), -1),
     (dict(softmax_scale=-0.1), -1),
     (dict(softmax_scale=float("nan")), -1),
     (dict(batch=2, heads=40000), -3),
