@@ -17,8 +17,8 @@
 //     query rows resident in VGPRs as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16).
 //   * In the 32x32 accumulator layout each lane owns ONE query column and 16 keys, so the
 //     fixed-m exponent e = alpha*S - (m + c_i) is one FMA with a per-lane constant, the
-//     row sum is a per-lane running fp32 sum (of the same bf16-rounded probabilities the
-//     PV product consumes), and the exp2'd scores, packed to bf16, are
+//     row sum is a per-lane running fp32 sum of the fp32 probabilities, and the exp2'd
+//     scores, packed to bf16, are
 //     already the B operand of O^T += V^T P^T with no transpose (the K-stationary layout of
 //     [CM]).  The matching key order on the V^T operand comes from the gfx950 LDS transpose
 //     read ds_read_b64_tr_b16.
@@ -323,17 +323,14 @@ __device__ __attribute__((always_inline)) void compute_s_fixed(const uint8_t* sm
 }
 
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
-// and adds the same rounded values to the row sum (low half then high half of each pair,
-// unpacked with integer ops), so numerator and denominator see identical weights.
+// and adds the fp32 probabilities to the row sum, key by key.
 __device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int base, float& lsum) {
   bf16x2 w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     w[i] = __builtin_convertvector((f32x2){e[base + 2 * i], e[base + 2 * i + 1]}, bf16x2);
-    uint32_t u;
-    __builtin_memcpy(&u, &w[i], 4);
-    lsum += __uint_as_float(u << 16);
-    lsum += __uint_as_float(u & 0xffff0000u);
+    lsum += e[base + 2 * i];
+    lsum += e[base + 2 * i + 1];
   }
   bf16x8 r;
   __builtin_memcpy(&r, w, 16);

@@ -22,8 +22,8 @@ are fixed by hand:
         v160-161    row sums l[n] (low bf16 halves);  v162-163  -(m + c_i) per query column
         v164-171    K fragment LDS addresses;  v172-175  V^T fragment LDS addresses
         v176-179    DMA lane offsets (K row 0/1, V row 0/1)
-        v180-185    temporaries of the row-sum unpacking;  v186-187  row sums of the high
-                    bf16 halves (folded into v160-161 when the block ends)
+        v186-187    row sums of the high keys of each pair (folded into v160-161 when the
+                    block ends)
   SGPR  s[60:61] next K tile address, s[62:63] next V tile address, s[64:65] / s[66:67]
         bytes between tiles, s68 this wave's LDS DMA base, s70 group count
 
@@ -37,7 +37,7 @@ is one exp2.
 One step handles tile t (its stage in the 8-deep LDS ring is static inside the unrolled
 group of 8 steps):
   wait for this wave's part of tile t+1, barrier; then 16 MFMAs O += V(t-1) P(t-1) and 16
-  MFMAs S(t+1) = K(t+1) Q^T - (m + c), with the 112 VALU instructions that turn S(t) into
+  MFMAs S(t+1) = K(t+1) Q^T - (m + c), with the 80 VALU instructions that turn S(t) into
   P(t) and the row sums placed slot by slot (softmax_plan), the K(t+1) fragment reads and the DMA of tile
   t+6 (into the stage tile t-2 used) between the first PV MFMAs, and the 16 LDS transpose
   reads of V(t) (used next step) in the first half of the S MFMAs.
@@ -45,8 +45,10 @@ group of 8 steps):
 Measured choices (shader-clock cycles per step, s_memtime-instrumented builds on gfx950):
 issuing the K reads and the DMA as a block after the barrier left the matrix cores idle
 (-7.5% when spread between the MFMAs); summing the bf16 pairs with v_dot2c_f32_bf16 costs
-~9 cycles of matrix-core time per instruction, while unpacking each pair with a shift and a
-mask and adding in fp32 (four plain VALU ops) overlaps the MFMAs (-3.7%); the per-score
+~9 cycles of matrix-core time per instruction; adding the fp32 probabilities to the row sums
+(two plain ops a pair) beats unpacking the bf16 pairs (four) only when every reader of an exp
+sits two or more MFMA slots after it (a transcendental result arrives late: one slot behind
+measured 1.6% slower than the unpacking, two slots behind 1.5% faster); the per-score
 v_fma_f32 that applied alpha and the shift cost ~3 cycles each (-6.5% without it); one exp
 per MFMA slot with the plain ops a slot or more behind (softmax_plan) instead of groups of
 eight exps: -7.3% (1,485 -> 1,377 cycles a step).  Work-removal builds put the rest: without
@@ -80,8 +82,6 @@ LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
 S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
 S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
 KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
-TMP = 180                             # v180-v185: bf16 -> f32 unpacking temporaries (3 pairs)
-N_TMP_PAIRS = 3
 LSUM_HI = 186                         # v186-v187: row sums of the high halves
 
 
@@ -137,21 +137,21 @@ def shift_reg(n):
 EXP_QUOTA = [1] * 20 + [2] + [1] * 10 + [0]
 SIMPLE_CAP = [1, 1, 1, 1, 3, 3, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 2, 2, 2, 2, 0, 2, 2, 2, 4, 4, 4, 4, 4, 4, 4, 4]
 DEP_DIST = 2                          # a plain VALU op sits >= 2 instructions after its producer
+EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it reads
 
 
 def softmax_plan(buf):
-    """The 112 VALU instructions that turn S(t) (scores buffer `buf`) into P(t) and the row
+    """The 80 VALU instructions that turn S(t) (scores buffer `buf`) into P(t) and the row
     sums, placed into the 32 MFMA slots of a step.  Returns 32 lists of (text, whether the
     instruction reads the scores buffer).
 
     A v_exp_f32 holds the vector ALU for about half an MFMA, so at most one goes between two
     MFMAs (bunching them starves the matrix cores: -7% cycles a step for this plan against
-    groups of exps).  Each bf16 pair (word) w of P takes 2 exps, then v_cvt_pk_bf16_f32, then
-    the unpacking of its two halves to fp32 (a shift and a mask) and two row-sum adds.  A
-    consumer of an exp goes in a later slot (a transcendental result needs a wait state
-    before a plain VALU op reads it); other consumers go >= DEP_DIST instructions after their
-    producer, and the low and high halves add into separate accumulators so that the adds of
-    one slot do not depend on each other."""
+    groups of exps).  Each bf16 pair (word) w of P takes 2 exps, then v_cvt_pk_bf16_f32 and
+    two row-sum adds of the fp32 exps.  A consumer of an exp goes EXP_GAP or more slots later
+    (the last slot takes what is left, one slot behind); other consumers go >= DEP_DIST
+    instructions after their producer, and the low and high keys of a pair add into separate
+    accumulators so that the adds of one slot do not depend on each other."""
     ops = []          # dicts: text, reads (scores buffer), deps, war, acc
 
     def add(text, reads, deps=(), war=(), acc=None):
@@ -165,22 +165,16 @@ def softmax_plan(buf):
         pair = [add(f"v_exp_f32 v{r}, v{r}", True) for r in (x, x + 1)]
         exps += pair
         word_exps.append(pair)
-    plain, adds_of = [], {}
+    plain = []
     for w in range(16):
         n, i = w % 2, w // 2
         x = s_first(buf, n) + 2 * i
         pw = p_first(buf, n) + i
-        t = TMP + 2 * (w % N_TMP_PAIRS)
-        war = adds_of.get(w - N_TMP_PAIRS, [])   # the temporaries' previous readers
         cvt = add(f"v_cvt_pk_bf16_f32 v{pw}, v{x}, v{x + 1}", True, word_exps[w])
-        # the low half as f32 is the pair shifted left by 16, the high half is the pair
-        # with its low 16 bits cleared
-        lo = add(f"v_lshlrev_b32 v{t}, 16, v{pw}", False, [cvt], war)
-        hi = add(f"v_and_b32 v{t + 1}, 0xffff0000, v{pw}", False, [cvt], war)
-        a_lo = add(f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{t}", False, [lo], acc=LSUM + n)
-        a_hi = add(f"v_add_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{t + 1}", False, [hi], acc=LSUM_HI + n)
-        adds_of[w] = [a_lo, a_hi]
-        plain += [cvt, lo, hi, a_lo, a_hi]
+        a_lo = add(f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{x}", True, [word_exps[w][0]], acc=LSUM + n)
+        a_hi = add(f"v_add_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{x + 1}", True, [word_exps[w][1]],
+                   acc=LSUM_HI + n)
+        plain += [cvt, a_lo, a_hi]
 
     pos = {}                                      # op -> (slot, index in the slot)
     last_acc = {}
@@ -204,7 +198,10 @@ def softmax_plan(buf):
                         ok = False
                         break
                     ds, di = pos[d]
-                    if ds == s and (ops[d]["text"].startswith("v_exp") or len(plan[s]) - di < dist):
+                    if ops[d]["text"].startswith("v_exp") and s - ds < (EXP_GAP if s < 31 else 1):
+                        ok = False
+                        break
+                    if ds == s and len(plan[s]) - di < dist:
                         ok = False
                         break
                 if ok and o["acc"] in last_acc:
@@ -409,7 +406,7 @@ def generate() -> str:
             f'"{{s[{S_VLAST}:{S_VLAST + 1}]}}"(v_last)', f'"{{s{S_NFULL}}}"(n_full)', f'"{{s{S_LOPART}}}"(lo_part)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
-            + [f"v{i}" for i in range(TMP, TMP + 2 * N_TMP_PAIRS)] + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
+            + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
             + [f"v{NEG_INF}", f"v{MASK_X}"]
             + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
             + [f"s{S_LO}", f"s{S_TMP}", f"s{S_TMP + 1}", "vcc", "scc", "memory"])

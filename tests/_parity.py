@@ -11,12 +11,12 @@ import numpy as np
 import oracle as O
 
 TOL = {"bf16": {"max": 1e-2, "mean": 1e-3}, "fp32": {"max": 1e-5, "mean": 1e-5}}
-# lse = ln2 (r + log2 l).  On the bf16 path two roundings (each relative <= 2^-8) reach lse:
-# the logits come from bf16(alpha q), and l sums the bf16-rounded probabilities the PV
-# product uses.  Over thousands of keys of Wan-like rows their effects average out far below
-# the worst case; 2.5e-3 is the tolerance set on those rows (measured errors ~1e-3).  Rows
-# far louder than that are checked against lse_bound_bf16, the worst case of the same
-# arithmetic.  The fp32 path forms logits and probabilities in fp64 and fp32.
+# lse = ln2 (r + log2 l).  On the bf16 path l sums fp32 probabilities, and the logits come
+# from bf16(alpha q) (one rounding, relative <= 2^-8 per element).  Over thousands of keys of
+# Wan-like rows the rounding's effect averages out far below the worst case; 2.5e-3 is the
+# tolerance set on those rows (measured errors ~1e-3).  Rows far louder than that are
+# checked against lse_bound_bf16, the worst case of the same arithmetic.  The fp32 path forms
+# logits and probabilities in fp64 and fp32.
 LSE_TOL = {"bf16": 2.5e-3, "fp32": 1e-5}
 
 
@@ -86,9 +86,9 @@ def check_output(got, ref, dtype: str, what: str = "O"):
 def lse_bound_bf16(q, k_all, scale: float) -> np.ndarray:
     """Worst-case lse error of the bf16 path per row, [B, H, Sq]: the fixed-m body forms
     logits from bf16(alpha q) (one round-to-nearest-even, relative error <= 2^-8 per element),
-    so a base-2 logit moves by at most 2^-8 sum_d |alpha q_d k_d|; the row sum adds
-    bf16-rounded probabilities (relative <= 2^-8 each), moving ln l by at most ln(1 + 2^-8).
-    Used for rows far louder than the Wan-like ones LSE_TOL was set on."""
+    so a base-2 logit moves by at most 2^-8 sum_d |alpha q_d k_d| and lse by ln 2 times that;
+    ln(1 + 2^-8) more covers the fp32 summation of l and the online body's bf16 path with
+    ample margin.  Used for rows far louder than the Wan-like ones LSE_TOL was set on."""
     alpha = float(np.float32(scale)) * O.LOG2E
     qa = np.abs(alpha * np.asarray(q, np.float64))
     ka = np.abs(np.asarray(k_all, np.float64))
