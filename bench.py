@@ -174,9 +174,15 @@ def main():
     n_attn = 1 if fused else len(ks)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps * n_attn)]
+    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
 
     def step(timed_idx=None):
+        if timed_idx is not None:
+            ev_b[timed_idx][0].record(stream)
         desc, _ = F.bounds(p, q, ks, vs, k_mean=km, buf=buf, stream=stream)
+        if timed_idx is not None:
+            ev_b[timed_idx][1].record(stream)
         run = F.run_init(desc)
         if fused:
             if timed_idx is not None:
@@ -211,6 +217,13 @@ def main():
     ms_per_step = total_ms / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in ev]
     attn_avg = sum(attn_ms) / len(attn_ms)
+    bounds_avg = sum(a.elapsed_time(b) for a, b in ev_b) / len(ev_b)
+    # the bounds pass reads Q once, K twice when the key mean is computed (the mean, then the
+    # centred norms), else once, and V once
+    esz = 2 if wl.dtype == "bf16" else 4
+    kv_bytes = wl.batch * wl.sk * wl.heads * wl.head_dim * esz
+    q_bytes = wl.batch * wl.sq * wl.heads * wl.head_dim * esz
+    bounds_bytes = q_bytes + kv_bytes * (3 if wl.center == "compute" else 2)
 
     flops = wl.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -254,6 +267,12 @@ def main():
             "timed_call": ("fixedm_attn_fwd_final: the attention launch plus the finalize of "
                            "the split tail tiles" if fused else "fixedm_attn_fwd (one launch)"),
         },
+    }
+    result["bounds"] = {
+        "ms": round(bounds_avg, 4), "algorithmic_bytes": bounds_bytes,
+        "GB/s": round(bounds_bytes / (bounds_avg * 1e-3) / 1e9, 1), "bound": "hbm",
+        "frac_of_hbm_peak": round(bounds_bytes / (bounds_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "terms": "Q + K (key mean) + K (centred norms) + V (magnitude check), one read each",
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (bounded sample)")
