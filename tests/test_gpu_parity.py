@@ -532,3 +532,56 @@ def test_row_shift_edges(F, name, args, kw):
     say(f"per-row shift: {name}")
     for fwd in (dict(chunks_per_call=1), FUSED):
         _generic(F, *args, shift="row", **kw, **fwd)
+
+
+# ------------------------------------------------------------------ degenerate inputs -
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_nonfinite_query_takes_fallback(F, dtype):
+    """An infinite query element makes its block's bound non-finite: the block is ineligible
+    with m = INT32_MAX (bit-exact), takes the online body, and its poisoned row comes out
+    non-finite as softmax's does; every other row matches the oracle."""
+    import torch
+    say(f"degenerate: inf in a query ({dtype})")
+    D = 128 if dtype == "bf16" else 64
+    inp = WL.generic_inputs(51, dtype, 1, 2, D, 200, (150, 170), q_block=64)
+    qf = inp.q.copy()
+    qf[0, 5, 1, 7] = np.inf
+    inp.q_store = WL.bf16_bits_from_f32(qf) if dtype == "bf16" else qf
+    q, ks, vs, _ = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, out_dtype=torch.float32, want_lse=True, **FUSED)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=64, dtype=dtype)
+    assert not ob.elig[0, 1, 0] and ob.m[0, 1, 0] == O.INT32_MAX and ob.elig[0, 0].all()
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, _ = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    got = out.cpu().numpy()
+    assert not np.isfinite(ref[0, 5, 1]).any() and not np.isfinite(got[0, 5, 1]).any()
+    keep = np.ones(got.shape[:3], bool)
+    keep[0, 5, 1] = False
+    check_output(got[keep], ref[keep], dtype, "O (other rows)")
+
+
+@pytest.mark.parametrize("shift", ["block", "row"])
+def test_zero_query_rows_give_the_mean_of_v(F, shift):
+    """Query rows that are all zero: U = 0, m = -C, every key's exponent is exactly C, so the
+    block stays eligible and its rows equal the mean of V (the textbook special case)."""
+    import torch
+    say(f"degenerate: zero query rows (shift={shift})")
+    inp = WL.generic_inputs(52, "bf16", 1, 2, 128, 256, (300, 211), q_block=64, center="compute",
+                            k_offset=2.0)
+    qf = inp.q.copy()
+    qf[0, 64:128, 0] = 0.0
+    inp.q_store = WL.bf16_bits_from_f32(qf)
+    q, ks, vs, _ = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, center="compute", out_dtype=torch.float32,
+                                    want_lse=True, shift=shift, **FUSED)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=64, center="compute", shift=shift)
+    assert ob.elig.all() and ob.u[0, 0, 1] == 0.0 and ob.m[0, 0, 1] == -ob.C
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    mean_v = np.concatenate(inp.v, 1)[0, :, 0].astype(np.float64).mean(axis=0)
+    got = out.cpu().numpy()
+    assert np.abs(got[0, 64:128, 0] - mean_v[None, :]).max() <= 1e-5
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(got, ref, "bf16")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
