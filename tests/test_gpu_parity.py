@@ -585,3 +585,14 @@ def test_zero_query_rows_give_the_mean_of_v(F, shift):
     ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
     check_output(got, ref, "bf16")
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
+
+
+def test_combined_options(F):
+    """Batch 2, five heads, q_block 192 (three waves' rows per block, blocks straddling
+    workgroups), supplied centring on offset keys, per-row shifts, an empty and a one-key
+    chunk, a loud block that falls back, all chunks in one fused call."""
+    say("combined: B=2 H=5 q_block=192 supplied row-shift fused")
+    ob, _ = _generic(F, 53, "bf16", 2, 5, 128, 700, (333, 0, 1200, 1, 47), q_block=192,
+                     center="supplied", k_offset=3.0, loud_rows=(3, 192, 384, 14.0), shift="row",
+                     **FUSED)
+    assert ob.elig.any() and not ob.elig[:, 3, 1].any()
