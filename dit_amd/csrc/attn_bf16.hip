@@ -451,18 +451,17 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   barrier();
   if (kFixed) {
     const float nshift[2] = {-shift[0], -shift[1]};
-    f32x16 s[2];
-    bf16x8 p[2][2];
-    compute_s_fixed(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
-    ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
-    softmax_fixed(s, p, lsum);
     if (n_tiles == 1) {
+      f32x16 s[2];
+      bf16x8 p[2][2];
+      compute_s_fixed(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
+      ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
+      softmax_fixed(s, p, lsum);
       bf16x8 vf[2][4];
       load_v(smem, g, 0, vf);
       pv_tile_asm(o, vf, p);
     } else {
-      // tiles 1 .. n_tiles-1 and the PV product of the last one: the assembly loop
-      compute_s_fixed(smem, g, 1, qf, s, nshift, tile_rows(g, 1), hh);
+      // the whole pass from tile 0 on runs in the assembly block (priming step, then the loop)
       const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
       uint32_t koff[8], voff[4];
 #pragma unroll
@@ -471,17 +470,21 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
       const uint32_t dma[4] = {g.kdma[0], g.kdma[1], g.vdma[0], g.vdma[1]};
       const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * g.wave);
-      // addresses of tile 1 + kAhead and of the chunk's last 32-key window (issue_tile's rule)
+      // addresses of tiles kAhead and 1 + kAhead and of the chunk's last 32-key window
+      // (issue_tile's rule: tile t starts at min(32 t, len - 32))
       const int64_t last_row = g.len - kKT;
+      const int64_t row6 = (int64_t)kAhead * kKT < last_row ? (int64_t)kAhead * kKT : last_row;
       const int64_t row7 = (int64_t)(1 + kAhead) * kKT < last_row ? (int64_t)(1 + kAhead) * kKT : last_row;
+      const uint64_t kt6 = uniform_u64(g.kbase + (uint64_t)(row6 * g.k_ss * 2));
+      const uint64_t vt6 = uniform_u64(g.vbase + (uint64_t)(row6 * g.v_ss * 2));
       const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(row7 * g.k_ss * 2));
       const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(row7 * g.v_ss * 2));
       const uint64_t k_last = uniform_u64(g.kbase + (uint64_t)(last_row * g.k_ss * 2));
       const uint64_t v_last = uniform_u64(g.vbase + (uint64_t)(last_row * g.v_ss * 2));
       const int n_full = (int)(g.len / kKT), rem = (int)(g.len - (int64_t)n_full * kKT);
-      bf16x8 vf[2][4];
-      load_v(smem, g, 0, vf);   // V^T fragments of tile 0, consumed by the first step
-      fixed_loop_asm(o, qf, s, p, vf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt, vt,
+      // tile 1 is whole, or (33..63 keys) the partial last tile whose real keys start at 32 - rem
+      const uint32_t lo1 = n_full >= 2 ? 0u : (uint32_t)(kKT - rem);
+      fixed_loop_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
                      uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last, (uint32_t)n_full,
                      (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast, (uint32_t)sched.tail,
                      (uint32_t)(kStages * sched.fast + 2));

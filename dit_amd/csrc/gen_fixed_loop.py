@@ -81,6 +81,7 @@ S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
 LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
 S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
 S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
+S_KT6, S_VT6, S_LO1 = 82, 84, 86      # tile 6's addresses (the priming step's DMA); tile 1's first real row
 KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
 LSUM_HI = 186                         # v186-v187: row sums of the high halves
 
@@ -244,11 +245,15 @@ class Emitter:
         self.count += 1
 
 
-def step(e: Emitter, jj: int, tail: bool):
+def step(e: Emitter, jj: int, tail: bool, first: bool = False):
     """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).  A tail step clamps its
     DMA to the chunk's last 32-key window and masks the keys of the next tile that are not
-    real, so steps past the chunk's end (and the partial last tile) run the same code."""
-    t_mod = 1 + jj
+    real, so steps past the chunk's end (and the partial last tile) run the same code.
+
+    first: the priming step t = 0 of a chunk (S(0) already issued): no PV product (there is
+    no tile -1), the DMA of tile 6 from s[S_KT6], S(1) masked from row s[S_LO1] on (tile 1
+    is the partial last tile when the chunk has 33..63 keys)."""
+    t_mod = 0 if first else 1 + jj
     cur = t_mod % 2            # parity of t: S(t), P(t), V(t) buffers
     prv = 1 - cur              # parity of t-1 (= parity of t+1)
     stage_t = t_mod % STAGES
@@ -265,6 +270,11 @@ def step(e: Emitter, jj: int, tail: bool):
     # by at least one instruction, the wait state that hazard needs.
     kreads = [f"ds_read_b128 {k_reg(prv, kk)}, v{KOFF + kk} offset:{stage_next * TILE_BYTES}" for kk in range(8)]
     extra = []
+    if first:
+        # the S(0) MFMAs issued just before read the K fragment registers the K(1) reads
+        # overwrite: let them take their operands first
+        e.emit("s_nop 7")
+        e.emit("s_nop 7")
     if tail:
         # tile t+6 may be the partial last tile or lie past the end: clamp its address to the
         # start of the chunk's last 32-key window before the DMA reads it
@@ -274,14 +284,16 @@ def step(e: Emitter, jj: int, tail: bool):
                       f"s_cselect_b64 s[{ptr}:{ptr + 1}], s[{last}:{last + 1}], s[{ptr}:{ptr + 1}]"]
         for ins in clamp:
             e.emit(ins)
+    kt_reg, vt_reg = (S_KT6, S_VT6) if first else (S_KT, S_VT)
     for i in range(2):
-        for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, S_KT),
-                                    (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, S_VT)):
+        for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, kt_reg),
+                                    (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, vt_reg)):
             extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", kreads.pop(0),
                           f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
     extra += [[kr] for kr in kreads]
-    for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE)):
-        extra.append([f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"])
+    if not first:     # the loop's next DMA address (the priming step's tile-6 registers are dead after it)
+        for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE)):
+            extra.append([f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"])
 
     plan = softmax_plan(cur)
     slot = 0
@@ -292,27 +304,32 @@ def step(e: Emitter, jj: int, tail: bool):
             e.emit(text, reads_sbuf=cur if reads else None)
         slot += 1
 
-    # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first MFMAs
+    # O^T += V(t-1)^T P(t-1)^T, with the K reads and the DMA after the first MFMAs (the
+    # priming step has no PV product: its slots hold only the other work)
     for st in range(2):
         for m in range(4):
             for n in range(2):
                 vf = v_frag(prv, st, m)
                 p = vreg(p_first(prv, n) + 4 * st, 4)
-                e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
+                if not first:
+                    e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
                 if extra:
                     for ins in extra.pop(0):
                         e.emit(ins)
                 valu_slot()
     assert not extra
-    if tail:
+    if tail or first:
         # Initial accumulator of S(t+1): -(m + c_i) for the real keys of tile j = t+1, -inf for
         # the others.  Real keys of tile j sit in rows >= lo: lo = 0 for a full tile, 32 - rem
         # for the partial last tile (loaded as the chunk's last 32-key window), 32 past the end.
-        e.emit(f"s_cmp_eq_u32 s{S_J}, s{S_NFULL}")
-        e.emit(f"s_cselect_b32 s{S_LO}, s{S_LOPART}, 32")
-        e.emit(f"s_cmp_lt_u32 s{S_J}, s{S_NFULL}")
-        e.emit(f"s_cselect_b32 s{S_LO}, 0, s{S_LO}")
-        e.emit(f"s_add_u32 s{S_J}, s{S_J}, 1")
+        if first:
+            e.emit(f"s_mov_b32 s{S_LO}, s{S_LO1}")
+        else:
+            e.emit(f"s_cmp_eq_u32 s{S_J}, s{S_NFULL}")
+            e.emit(f"s_cselect_b32 s{S_LO}, s{S_LOPART}, 32")
+            e.emit(f"s_cmp_lt_u32 s{S_J}, s{S_NFULL}")
+            e.emit(f"s_cselect_b32 s{S_LO}, 0, s{S_LO}")
+            e.emit(f"s_add_u32 s{S_J}, s{S_J}, 1")
         e.emit(f"v_sub_u32 v{MASK_X}, s{S_LO}, v{KB4}")         # lo - 4 (lane / 32)
         for r in range(16):
             key = 8 * (r >> 2) + (r & 3)                          # row of register r, lane half 0
@@ -351,6 +368,18 @@ def generate() -> str:
     e.emit(f"v_mov_b32 v{LSUM_HI + 1}, 0")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
+    # Priming: S(0) from stage 0 (tile 0 is whole whenever this block runs), then step t = 0
+    # (P(0), the row sums of tile 0, S(1), V(0)'s fragments, the DMA of tile 6).
+    for kk in range(8):
+        e.emit(f"ds_read_b128 {k_reg(0, kk)}, v{KOFF + kk} offset:0")
+    e.emit("s_waitcnt lgkmcnt(0)")
+    for kk in range(8):
+        for n in range(2):
+            s0 = s_first(0, n)
+            src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
+            e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(0, kk)}, {q_reg(n, kk)}, {src_c}",
+                   writes_sbuf=0)
+    step(e, 0, tail=False, first=True)
     e.emit(f"s_cmp_eq_u32 s{S_CNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
     # fast groups: every tile they prefetch and every S tile they compute is a full one
@@ -381,14 +410,6 @@ def generate() -> str:
     for n in range(2):
         for m in range(4):
             outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
-    for n in range(2):
-        outs.append(f'"+{{{vreg(s_first(1, n), 16)}}}"(s[{n}])')
-    for n in range(2):
-        for st in range(2):
-            outs.append(f'"+{{{vreg(p_first(0, n) + 4 * st, 4)}}}"(p[{n}][{st}])')
-    for st in range(2):
-        for m in range(4):
-            outs.append(f'"+{{{v_frag(0, st, m)}}}"(vf[{st}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
              f'"+{{s{S_CNT}}}"(groups)', f'"+{{s{S_TCNT}}}"(tail_groups)', f'"+{{s{S_J}}}"(next_tile)']
@@ -401,14 +422,15 @@ def generate() -> str:
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
     ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
     ins += [f'"{{v{KB4}}}"(kb4)']
+    ins += [f'"{{s[{S_KT6}:{S_KT6 + 1}]}}"(kt6)', f'"{{s[{S_VT6}:{S_VT6 + 1}]}}"(vt6)', f'"{{s{S_LO1}}}"(lo1)']
     ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
             f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s[{S_KLAST}:{S_KLAST + 1}]}}"(k_last)',
             f'"{{s[{S_VLAST}:{S_VLAST + 1}]}}"(v_last)', f'"{{s{S_NFULL}}}"(n_full)', f'"{{s{S_LOPART}}}"(lo_part)']
-    clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 32)] + [f"v{i}" for i in range(P_BASE + 16, P_BASE + 32)]
+    clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 64)] + [f"v{i}" for i in range(P_BASE, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
             + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
             + [f"v{NEG_INF}", f"v{MASK_X}"]
-            + [f"a{i}" for i in range(K_BASE, K_BASE + 32)]
+            + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
             + [f"s{S_LO}", f"s{S_TMP}", f"s{S_TMP + 1}", "vcc", "scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
@@ -416,20 +438,21 @@ def generate() -> str:
         return ",\n        ".join(items)
 
     return f"""// Generated by gen_fixed_loop.py; do not edit by hand.
-// The fixed-m loop of a chunk: `groups` fast groups then `tail_groups` (>= 1) tail groups of
-// 8 pipelined 32-key steps, tiles t0 .. t0 + 8 (groups + tail_groups) - 1 with t0 = 1.  On
-// entry: s = S(t0) (odd-tile buffer, masked like a tail step's), p = P(t0 - 1), vf = the
-// V^T fragments of tile t0 - 1, kt / vt = the addresses of tile t0 + 6 (clamped to the
-// chunk's last 32-key window), tiles up to t0 + 5 issued and tile t0 in LDS, next_tile =
-// t0 + 8 groups + 1 (the tile whose S the first tail step computes).  The steps past the
-// chunk's last tile see only masked keys (p = 0), so the last of them completes the PV
-// product of the last tile.  On exit every LDS read has completed.
+// The fixed-m pass over a chunk of >= 2 tiles: the priming step (S(0), then step t = 0: P(0),
+// S(1), V(0)'s fragments, the DMA of tile 6), `groups` fast groups, then `tail_groups` (>= 1)
+// tail groups of 8 pipelined 32-key steps, tiles t0 .. t0 + 8 (groups + tail_groups) - 1 with
+// t0 = 1.  On entry: tiles 0 .. 5 issued and tile 0 in LDS (waited and met at a barrier),
+// kt6 / vt6 = the addresses of tile 6 and kt / vt those of tile 7 (each clamped to the
+// chunk's last 32-key window), lo1 = tile 1's first real row, next_tile = 8 groups + 2 (the
+// tile whose S the first tail step computes).  The steps past the chunk's last tile see only
+// masked keys (p = 0), so the last of them completes the PV product of the last tile.  On
+// exit every LDS read has completed.
 __device__ __attribute__((always_inline)) inline void fixed_loop_asm(
-    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], f32x16 (&s)[2], bf16x8 (&p)[2][2], bf16x8 (&vf)[2][4],
+    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8],
     float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
-    const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt, uint64_t vt, uint64_t ktile, uint64_t vtile,
-    uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full, uint32_t lo_part, uint32_t groups,
-    uint32_t tail_groups, uint32_t next_tile) {{
+    const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt6, uint64_t vt6, uint32_t lo1, uint64_t kt, uint64_t vt,
+    uint64_t ktile, uint64_t vtile, uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full,
+    uint32_t lo_part, uint32_t groups, uint32_t tail_groups, uint32_t next_tile) {{
   asm volatile(
 {body}
       : {join(outs)}
