@@ -1,0 +1,89 @@
+"""The generated assembly loop of the bf16 kernel: the committed fixed_loop.inc is exactly
+what gen_fixed_loop.py writes, and the structural rules its docstring states hold (CPU only)."""
+import os
+import re
+import sys
+
+import pytest
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "dit_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def gen():
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_fixed_loop
+    finally:
+        sys.path.remove(CSRC)
+    return gen_fixed_loop
+
+
+def _body(text):
+    return re.findall(r'^\s*"([^"\\]*)\\n"', text, flags=re.M)
+
+
+def test_committed_loop_matches_generator(gen):
+    with open(os.path.join(CSRC, "fixed_loop.inc")) as f:
+        assert f.read() == gen.generate()
+
+
+def test_every_step_places_all_exps_and_row_sums(gen):
+    for buf in (0, 1):
+        plan = gen.softmax_plan(buf)
+        assert len(plan) == 32
+        texts = [t for slot in plan for t, _ in slot]
+        assert sum(t.startswith("v_exp_f32") for t in texts) == 32
+        assert sum(t.startswith("v_cvt_pk_bf16_f32") for t in texts) == 16
+        assert sum(t.startswith("v_add_f32") for t in texts) == 32
+        # every score register is exponentiated exactly once
+        regs = sorted(int(re.match(r"v_exp_f32 v(\d+)", t).group(1)) for t in texts if t.startswith("v_exp"))
+        first = gen.s_first(buf, 0)
+        assert regs == list(range(first, first + 32))
+
+
+def test_exp_readers_sit_behind_their_exp(gen):
+    """A reader of an exp result sits EXP_GAP or more MFMA slots after it (one slot in the
+    step's last slot), never in the same slot."""
+    for buf in (0, 1):
+        plan = gen.softmax_plan(buf)
+        exp_slot = {}
+        for s, slot in enumerate(plan):
+            for t, _ in slot:
+                m = re.match(r"v_exp_f32 v(\d+)", t)
+                if m:
+                    exp_slot[int(m.group(1))] = s
+        for s, slot in enumerate(plan):
+            for t, _ in slot:
+                if t.startswith("v_exp"):
+                    continue
+                for r in (int(x) for x in re.findall(r"v(\d+)", t.split(" ", 1)[1])[1:]):
+                    if r in exp_slot:
+                        gap = s - exp_slot[r]
+                        assert gap >= (gen.EXP_GAP if s < 31 else 1), (t, gap)
+
+
+def test_mfma_results_are_waited_for(gen):
+    """Every VALU read of a score register comes >= 16 wait states (an instruction is one, s_nop N is N+1)
+    after the MFMA that last wrote that score buffer; at a label the tracking restarts as if an MFMA
+    had just written both buffers, as the generator assumes."""
+    lines = _body(gen.generate())
+    written = {}
+    count = 0
+    s_regs = {0: set(range(gen.s_first(0, 0), gen.s_first(0, 0) + 32)),
+              1: set(range(gen.s_first(1, 0), gen.s_first(1, 0) + 32))}
+    for ln in lines:
+        if ln.endswith(":"):            # a label: the generator restarts its tracking conservatively
+            written = {b: count - 1 for b in (0, 1)}
+            continue
+        if ln.startswith("v_mfma") and re.match(r"v_mfma\S* v\[(\d+):", ln):
+            lo = int(re.match(r"v_mfma\S* v\[(\d+):", ln).group(1))
+            for b, regs in s_regs.items():
+                if lo in regs:
+                    written[b] = count
+        elif ln.startswith(("v_exp", "v_cvt_pk", "v_add_f32")):
+            for r in (int(x) for x in re.findall(r"v(\d+)", ln)[1:]):
+                for b, regs in s_regs.items():
+                    if r in regs and b in written:
+                        assert count - written[b] - 1 >= 16, ln
+        count += int(ln.split()[1]) + 1 if ln.startswith("s_nop") else 1
