@@ -74,9 +74,17 @@ def err_stats(got: np.ndarray, ref: np.ndarray):
     return float(d.max()), float(d.mean())
 
 
+def error_quantiles(got, ref, qs=(0.5, 0.9, 0.99, 0.999, 1.0)) -> dict:
+    """Distribution of |got - ref| (element-wise, fp64): the given quantiles."""
+    d = np.abs(np.asarray(got, np.float64) - ref).ravel()
+    return {q: float(np.quantile(d, q)) for q in qs}
+
+
 def check_output(got, ref, dtype: str, what: str = "O"):
     mx, mn = err_stats(got, ref)
     say(f"  {what}: max|d|={mx:.3e} mean|d|={mn:.3e} (tol {TOL[dtype]})")
+    eq = error_quantiles(got, ref)
+    say("  |d| quantiles: " + "  ".join(f"p{100 * q:g}={v:.2e}" for q, v in eq.items()))
     assert np.isfinite(got).all(), f"{what} has non-finite values"
     assert mx <= TOL[dtype]["max"], f"{what} max abs error {mx}"
     assert mn <= TOL[dtype]["mean"], f"{what} mean abs error {mn}"
