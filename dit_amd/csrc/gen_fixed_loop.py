@@ -140,6 +140,9 @@ SIMPLE_CAP = [1, 1, 1, 1, 3, 3, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 2, 2, 2, 2, 0, 2, 
 DEP_DIST = 2                          # a plain VALU op sits >= 2 instructions after its producer
 EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it reads
 BARRIER_AFTER = 2                     # PV MFMAs issued before a step's vmcnt wait and barrier
+V_TR_PER_SLOT, V_TR_FIRST = 2, 0      # V^T transpose reads per S MFMA slot, from this slot on
+                                      # (one per slot over all 16, or two per slot in the second
+                                      # half, measured 0.5-0.6% slower)
 
 
 def softmax_plan(buf):
@@ -360,8 +363,8 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False):
             src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
             e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(prv, kk)}, {q_reg(n, kk)}, {src_c}",
                    writes_sbuf=prv)
-            if ti < len(tr):
-                for _ in range(2):
+            if ti < len(tr) and 2 * kk + n >= V_TR_FIRST:
+                for _ in range(V_TR_PER_SLOT):
                     st, m, h = tr[ti]
                     dst = v_frag(cur, st, m, h)
                     off = stage_t * TILE_BYTES + 4096 * st + 2048 * h
