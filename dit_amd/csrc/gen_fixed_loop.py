@@ -140,6 +140,8 @@ SIMPLE_CAP = [1, 1, 1, 1, 3, 3, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 2, 2, 2, 2, 0, 2, 
 DEP_DIST = 2                          # a plain VALU op sits >= 2 instructions after its producer
 EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it reads
 BARRIER_AFTER = 2                     # PV MFMAs issued before a step's vmcnt wait and barrier
+DMA_WITH_KREAD = True                 # a K fragment read between each M0 write and its DMA
+                                      # (DMAs first with s_nop 0, K reads after: same speed)
 V_TR_PER_SLOT, V_TR_FIRST = 2, 0      # V^T transpose reads per S MFMA slot, from this slot on
                                       # (one per slot over all 16, or two per slot in the second
                                       # half, measured 0.5-0.6% slower)
@@ -299,7 +301,8 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False):
     for i in range(2):
         for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, kt_reg),
                                     (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, vt_reg)):
-            extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", kreads.pop(0),
+            between = kreads.pop(0) if DMA_WITH_KREAD else "s_nop 0"
+            extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", between,
                           f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
     extra += [[kr] for kr in kreads]
     if not first:     # the loop's next DMA address (the priming step's tile-6 registers are dead after it)
