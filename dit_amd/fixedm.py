@@ -180,6 +180,43 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# The C ABI takes device buffers as bare pointers (their sizes are the caller's contract);
+# the binding checks sizes and shapes against the problem before any call, so a PyTorch
+# caller gets an exception instead of a launch that reads or writes past a buffer.
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_bytes(t, nbytes: int, what: str):
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes; the problem needs {nbytes}")
+
+
+def _need_shape(t, shape, what: str):
+    if t is None or tuple(t.shape) != tuple(shape):
+        got = None if t is None else tuple(t.shape)
+        raise ValueError(f"{what} has shape {got}; the problem needs {tuple(shape)}")
+
+
+def _check_qkv(p: Problem, q, k_chunks, v_chunks):
+    _need_shape(q, (p.batch, p.sq, p.heads, p.head_dim), "q")
+    for i, (k, v) in enumerate(zip(k_chunks, v_chunks)):
+        want = (p.batch, int(k.shape[1]), p.heads, p.head_dim)
+        _need_shape(k, want, f"k_chunks[{i}]")
+        _need_shape(v, want, f"v_chunks[{i}]")
+
+
+def _check_out(p: Problem, out, lse):
+    import torch
+    _need_shape(out, (p.batch, p.sq, p.heads, p.head_dim), "out")
+    if lse is not None:
+        _need_shape(lse, (p.batch, p.heads, p.sq), "lse")
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor")
+
+
 # ----------------------------------------------------------------------- device calls
 def bounds(p: Problem, q, k_chunks, v_chunks, k_mean=None, buf=None, stream=None):
     """fixedm_bounds: returns (BoundsDesc, device buffer).  buf: optional uint8 CUDA tensor
@@ -190,6 +227,10 @@ def bounds(p: Problem, q, k_chunks, v_chunks, k_mean=None, buf=None, stream=None
         raise FixedmError(-1, "fixedm_bounds_bytes")
     if buf is None:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _need_bytes(buf, nbytes, "bounds buffer")
+    _check_qkv(p, q, k_chunks, v_chunks)
+    if p.center == CENTER["supplied"]:
+        _need_shape(k_mean, (p.batch, p.heads, p.head_dim), "k_mean")
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     desc = BoundsDesc()
     st = lib().fixedm_bounds(ctypes.byref(p), tensor_desc(q), ks, vs, lens, n, _ptr(k_mean),
@@ -205,6 +246,8 @@ def run_init(desc: BoundsDesc) -> RunState:
 
 
 def attn_fwd(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, workspace, stream=None):
+    _check_qkv(desc.p, q, k_chunks, v_chunks)
+    _need_bytes(workspace, workspace_bytes(desc.p), "workspace")
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     st = lib().fixedm_attn_fwd(ctypes.byref(desc), ctypes.byref(run), tensor_desc(q), ks, vs,
                                lens, n, _ptr(workspace), _stream(stream))
@@ -215,6 +258,9 @@ def attn_fwd_final(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, works
                    stream=None):
     import torch
     dt = {torch.bfloat16: BF16, torch.float32: F32}[out.dtype]
+    _check_qkv(desc.p, q, k_chunks, v_chunks)
+    _need_bytes(workspace, workspace_bytes(desc.p), "workspace")
+    _check_out(desc.p, out, lse)
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     st = lib().fixedm_attn_fwd_final(ctypes.byref(desc), ctypes.byref(run), tensor_desc(q), ks, vs,
                                      lens, n, _ptr(workspace), tensor_desc(out), dt, _ptr(lse),
@@ -225,6 +271,8 @@ def attn_fwd_final(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, works
 def finalize(desc: BoundsDesc, run: RunState, workspace, out, lse=None, stream=None):
     import torch
     dt = {torch.bfloat16: BF16, torch.float32: F32}[out.dtype]
+    _need_bytes(workspace, workspace_bytes(desc.p), "workspace")
+    _check_out(desc.p, out, lse)
     st = lib().fixedm_finalize(ctypes.byref(desc), ctypes.byref(run), _ptr(workspace),
                                tensor_desc(out), dt, _ptr(lse), _stream(stream))
     _check(st, "fixedm_finalize")

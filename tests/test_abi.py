@@ -147,3 +147,35 @@ def test_forged_descriptor_is_rejected(L):
                                    0x100000, T(0x20000, 0, 5120, 128), 1, None, None) == -1
     assert L.fixedm_attn_fwd(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
                              0x100000, None) == -1
+
+
+def test_binding_checks_sizes_and_shapes():
+    """The C ABI takes bare device pointers; the binding rejects buffers smaller than the
+    problem needs and tensors of the wrong shape before any call (CPU tensors suffice)."""
+    import torch
+    p = _p(sq=100, sk_total=1000)
+    q = torch.empty((1, 100, 40, 128), dtype=torch.bfloat16)
+    k = [torch.empty((1, 1000, 40, 128), dtype=torch.bfloat16)]
+    with pytest.raises(ValueError, match="bounds buffer"):
+        F.bounds(p, q, k, k, buf=torch.empty(16, dtype=torch.uint8))
+    buf = torch.empty(F.bounds_bytes(p), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q has shape"):
+        F.bounds(p, q[:, :50], k, k, buf=buf)
+    with pytest.raises(ValueError, match=r"k_chunks\[0\]"):
+        F.bounds(p, q, [k[0][:, :, :20]], k, buf=buf)
+    ps = _p(sq=100, sk_total=1000, center="supplied")
+    with pytest.raises(ValueError, match="k_mean"):
+        F.bounds(ps, q, k, k, k_mean=torch.empty(40, 128), buf=torch.empty(F.bounds_bytes(ps), dtype=torch.uint8))
+    d = F.BoundsDesc()
+    d.p = p
+    run = F.RunState()
+    with pytest.raises(ValueError, match="workspace"):
+        F.attn_fwd(d, run, q, k, k, torch.empty(8, dtype=torch.uint8))
+    ws = torch.empty(F.workspace_bytes(p), dtype=torch.uint8)
+    out = torch.empty((1, 100, 40, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out has shape"):
+        F.finalize(d, run, ws, out[:, :10])
+    with pytest.raises(ValueError, match="lse"):
+        F.finalize(d, run, ws, out, lse=torch.empty((1, 40, 100), dtype=torch.float64))
+    with pytest.raises(ValueError, match="workspace"):
+        F.attn_fwd_final(d, run, q, k, k, torch.empty(8, dtype=torch.uint8), out)
