@@ -255,10 +255,12 @@ size_t fixedm_workspace_bytes(const fixedm_problem* p) {
 
 fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
                             const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
-                            const float* k_mean_in, void* bounds_dev, fixedm_bounds_t* out, void* stream) {
+                            const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
+                            fixedm_bounds_t* out, void* stream) {
   fixedm_status st = check_problem(p);
   if (st != FIXEDM_OK) return st;
   if (out == nullptr || bounds_dev == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (bounds_dev_bytes < fixedm_bounds_bytes(p)) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)bounds_dev & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
   if ((st = check_tensor(*p, q)) != FIXEDM_OK) return st;
   if (n_chunks > kMaxBoundsChunks) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
@@ -340,10 +342,11 @@ namespace {
 fixedm_status check_attn_call(const fixedm_bounds_t* bounds, const fixedm_run_t* run, fixedm_tensor q,
                               const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
                               const int64_t* chunk_len, int32_t n_chunks, const void* workspace,
-                              int64_t* total, bool allow_none = false) {
+                              size_t workspace_bytes, int64_t* total, bool allow_none = false) {
   fixedm_status st = check_descriptor(bounds);
   if (st != FIXEDM_OK) return st;
   if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fixedm_workspace_bytes(&bounds->p)) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
   if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
   const fixedm_problem& p = bounds->p;
@@ -469,9 +472,11 @@ extern "C" {
 
 fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
                               const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
-                              const int64_t* chunk_len, int32_t n_chunks, void* workspace, void* stream) {
+                              const int64_t* chunk_len, int32_t n_chunks, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   int64_t total = 0;
-  fixedm_status st = check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace, &total);
+  fixedm_status st = check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace,
+                                     workspace_bytes, &total);
   if (st != FIXEDM_OK) return st;
   if (total == 0) return FIXEDM_OK;
   const AttnArgs a = attn_args(bounds, q, workspace);
@@ -486,10 +491,11 @@ fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run, 
 fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t* run, fixedm_tensor q,
                                     const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
                                     const int64_t* chunk_len, int32_t n_chunks, void* workspace,
-                                    fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
+                                    size_t workspace_bytes, fixedm_tensor out, int32_t out_dtype, float* lse,
+                                    void* stream) {
   int64_t total = 0;
-  fixedm_status st =
-      check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace, &total, true);
+  fixedm_status st = check_attn_call(bounds, run, q, k_chunks, v_chunks, chunk_len, n_chunks, workspace,
+                                     workspace_bytes, &total, true);
   if (st != FIXEDM_OK) return st;
   const fixedm_problem& p = bounds->p;
   if ((st = check_out_call(p, out, out_dtype, lse)) != FIXEDM_OK) return st;
@@ -528,10 +534,12 @@ fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t*
 }
 
 fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run, const void* workspace,
-                              fixedm_tensor out, int32_t out_dtype, float* lse, void* stream) {
+                              size_t workspace_bytes, fixedm_tensor out, int32_t out_dtype, float* lse,
+                              void* stream) {
   fixedm_status st = check_descriptor(bounds);
   if (st != FIXEDM_OK) return st;
   if (run == nullptr || workspace == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fixedm_workspace_bytes(&bounds->p)) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (run->token != bounds->token) return FIXEDM_ERR_BOUNDS_MISMATCH;
   if (((uintptr_t)workspace & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
   const fixedm_problem& p = bounds->p;

@@ -87,19 +87,20 @@ def lib() -> ctypes.CDLL:
     L.fixedm_workspace_bytes.argtypes = [P(Problem)]
     L.fixedm_bounds.restype = ctypes.c_int
     L.fixedm_bounds.argtypes = [P(Problem), Tensor, P(Tensor), P(Tensor), P(ctypes.c_int64),
-                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, P(BoundsDesc),
-                                ctypes.c_void_p]
+                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                P(BoundsDesc), ctypes.c_void_p]
     L.fixedm_run_init.restype = ctypes.c_int
     L.fixedm_run_init.argtypes = [P(BoundsDesc), P(RunState)]
     L.fixedm_attn_fwd.restype = ctypes.c_int
     L.fixedm_attn_fwd.argtypes = [P(BoundsDesc), P(RunState), Tensor, P(Tensor), P(Tensor),
-                                  P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+                                  P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
     L.fixedm_attn_fwd_final.restype = ctypes.c_int
     L.fixedm_attn_fwd_final.argtypes = [P(BoundsDesc), P(RunState), Tensor, P(Tensor), P(Tensor),
-                                        P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, Tensor,
-                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+                                        P(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                        Tensor, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.fixedm_finalize.restype = ctypes.c_int
-    L.fixedm_finalize.argtypes = [P(BoundsDesc), P(RunState), ctypes.c_void_p, Tensor,
+    L.fixedm_finalize.argtypes = [P(BoundsDesc), P(RunState), ctypes.c_void_p, ctypes.c_size_t, Tensor,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     _lib = L
     return L
@@ -234,7 +235,7 @@ def bounds(p: Problem, q, k_chunks, v_chunks, k_mean=None, buf=None, stream=None
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     desc = BoundsDesc()
     st = lib().fixedm_bounds(ctypes.byref(p), tensor_desc(q), ks, vs, lens, n, _ptr(k_mean),
-                             _ptr(buf), ctypes.byref(desc), _stream(stream))
+                             _ptr(buf), _nbytes(buf), ctypes.byref(desc), _stream(stream))
     _check(st, "fixedm_bounds")
     return desc, buf
 
@@ -250,7 +251,7 @@ def attn_fwd(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, workspace, 
     _need_bytes(workspace, workspace_bytes(desc.p), "workspace")
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     st = lib().fixedm_attn_fwd(ctypes.byref(desc), ctypes.byref(run), tensor_desc(q), ks, vs,
-                               lens, n, _ptr(workspace), _stream(stream))
+                               lens, n, _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "fixedm_attn_fwd")
 
 
@@ -263,8 +264,8 @@ def attn_fwd_final(desc: BoundsDesc, run: RunState, q, k_chunks, v_chunks, works
     _check_out(desc.p, out, lse)
     ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
     st = lib().fixedm_attn_fwd_final(ctypes.byref(desc), ctypes.byref(run), tensor_desc(q), ks, vs,
-                                     lens, n, _ptr(workspace), tensor_desc(out), dt, _ptr(lse),
-                                     _stream(stream))
+                                     lens, n, _ptr(workspace), _nbytes(workspace), tensor_desc(out), dt,
+                                     _ptr(lse), _stream(stream))
     _check(st, "fixedm_attn_fwd_final")
 
 
@@ -274,7 +275,7 @@ def finalize(desc: BoundsDesc, run: RunState, workspace, out, lse=None, stream=N
     _need_bytes(workspace, workspace_bytes(desc.p), "workspace")
     _check_out(desc.p, out, lse)
     st = lib().fixedm_finalize(ctypes.byref(desc), ctypes.byref(run), _ptr(workspace),
-                               tensor_desc(out), dt, _ptr(lse), _stream(stream))
+                               _nbytes(workspace), tensor_desc(out), dt, _ptr(lse), _stream(stream))
     _check(st, "fixedm_finalize")
 
 

@@ -32,7 +32,9 @@
  *     are accepted.  ptr must be 16-byte aligned and every stride a multiple of 8
  *     elements (bf16) or 4 elements (fp32).
  *   - Every device pointer and the stream belong to the caller.  The library never
- *     allocates, frees or synchronises, and keeps no pointer after a call returns.
+ *     allocates, frees or synchronises, and keeps no pointer after a call returns.  The
+ *     scratch buffers it writes (bounds buffer, workspace) come with their byte sizes,
+ *     checked against the problem before anything is enqueued.
  *     Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default stream).
  *   - Host-checkable errors are returned before anything is enqueued.  A failed launch
  *     returns FIXEDM_ERR_HIP.  Data-dependent ineligibility is never an error: it selects
@@ -170,14 +172,15 @@ fixedm_status fixedm_constants(int64_t n, int32_t* log2_n, int32_t* C, int32_t* 
  *   and the attention calls shift row i by m_i (eligibility stays the block's).
  * q: [B, sq, H, D]; k_chunks/v_chunks: n_chunks tensors of [B, chunk_len[c], H, D];
  * sum(chunk_len) must equal p->sk_total.  k_mean_in: device fp32 [B, H, D] contiguous,
- * required iff center == SUPPLIED.  bounds_dev: device buffer of fixedm_bounds_bytes(p)
- * bytes, 256-byte aligned.  On success *out describes the result (valid once the stream
+ * required iff center == SUPPLIED.  bounds_dev: device buffer of bounds_dev_bytes >=
+ * fixedm_bounds_bytes(p) bytes, 256-byte aligned (a smaller size ->
+ * FIXEDM_ERR_INVALID_ARGUMENT).  On success *out describes the result (valid once the stream
  * reaches this point).  Enqueues 4-6 kernels; no host synchronisation. */
 fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q,
                             const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
                             const int64_t* chunk_len, int32_t n_chunks,
                             const float* k_mean_in, void* bounds_dev,
-                            fixedm_bounds_t* out, void* stream);
+                            size_t bounds_dev_bytes, fixedm_bounds_t* out, void* stream);
 
 /* Starts a new ring pass over the descriptor's K/V: zero keys visited. */
 fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run);
@@ -188,14 +191,16 @@ fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run);
  * initialise the workspace, later ones add to it: pure addition for eligible blocks,
  * the online-softmax rescale merge for the others.  q: [B, sq, H, D] (the same rows the
  * bounds were computed from); chunks as in fixedm_bounds.  workspace: device buffer of
- * fixedm_workspace_bytes() bytes, 256-byte aligned.  Errors: FIXEDM_ERR_BOUNDS_MISMATCH
+ * workspace_bytes >= fixedm_workspace_bytes() bytes, 256-byte aligned (a smaller size ->
+ * FIXEDM_ERR_INVALID_ARGUMENT).  Errors: FIXEDM_ERR_BOUNDS_MISMATCH
  * if run->token does not match the descriptor, FIXEDM_ERR_STATE if the keys visited
  * would exceed sk_total or the run was completed by fixedm_attn_fwd_final.  Updates *run
  * on success. */
 fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run,
                               fixedm_tensor q, const fixedm_tensor* k_chunks,
                               const fixedm_tensor* v_chunks, const int64_t* chunk_len,
-                              int32_t n_chunks, void* workspace, void* stream);
+                              int32_t n_chunks, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* The last ring step(s) of a run fused with the finalize ([CM] "Accumulate, then normalize
  * once": the last step folds and normalises in one pass; "The ring loop").  Folds
@@ -211,17 +216,20 @@ fixedm_status fixedm_attn_fwd(const fixedm_bounds_t* bounds, fixedm_run_t* run,
 fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t* run,
                                     fixedm_tensor q, const fixedm_tensor* k_chunks,
                                     const fixedm_tensor* v_chunks, const int64_t* chunk_len,
-                                    int32_t n_chunks, void* workspace, fixedm_tensor out,
+                                    int32_t n_chunks, void* workspace, size_t workspace_bytes,
+                                    fixedm_tensor out,
                                     int32_t out_dtype, float* lse, void* stream);
 
 /* O = acc / l, cast to out_dtype (bf16 by round-to-nearest-even, or fp32), written to
  * out [B, sq, H, D]; if lse is non-NULL also lse[b, h, i] = ln2 * (r_i + log2 l_i), the
  * natural-log log-sum-exp of row i ([CM] Interface table, training output), as a
  * contiguous fp32 [B, H, sq] device array.  Requires run->kv_visited == sk_total
- * and a run not completed by fixedm_attn_fwd_final (FIXEDM_ERR_STATE otherwise).  Reads
- * the workspace only, so it may be called again. */
+ * and a run not completed by fixedm_attn_fwd_final (FIXEDM_ERR_STATE otherwise); workspace
+ * and workspace_bytes as in fixedm_attn_fwd.  Reads the workspace only, so it may be
+ * called again. */
 fixedm_status fixedm_finalize(const fixedm_bounds_t* bounds, const fixedm_run_t* run,
-                              const void* workspace, fixedm_tensor out, int32_t out_dtype,
+                              const void* workspace, size_t workspace_bytes,
+                              fixedm_tensor out, int32_t out_dtype,
                               float* lse, void* stream);
 
 /* Static string naming a status code. */

@@ -97,14 +97,15 @@ def test_bad_abi_version(version):
 
 
 def _call_bounds(L, p, q=None, kc=None, vc=None, lens=None, n=1, kmean=None, dev=0x10000,
-                 out=True):
+                 out=True, nbytes=None):
     T = F.Tensor
     q = q if q is not None else T(0x20000, 0, 40 * 128, 128)
     kc = kc if kc is not None else (T * 1)(T(0x40000, 0, 40 * 128, 128))
     vc = vc if vc is not None else (T * 1)(T(0x80000, 0, 40 * 128, 128))
     lens = lens if lens is not None else (ctypes.c_int64 * 1)(p.sk_total)
     desc = F.BoundsDesc()
-    return L.fixedm_bounds(ctypes.byref(p), q, kc, vc, lens, n, kmean, dev,
+    nbytes = nbytes if nbytes is not None else max(F.bounds_bytes(p), 1)
+    return L.fixedm_bounds(ctypes.byref(p), q, kc, vc, lens, n, kmean, dev, nbytes,
                            ctypes.byref(desc) if out else None, None)
 
 
@@ -114,6 +115,8 @@ def test_bounds_argument_errors_before_launch(L):
     assert _call_bounds(L, p, out=False) == -1                              # no descriptor
     assert _call_bounds(L, p, dev=0) == -1                                  # no buffer
     assert _call_bounds(L, p, dev=0x10010) == -1                            # buffer not 256-aligned
+    assert _call_bounds(L, p, nbytes=F.bounds_bytes(p) - 1) == -1            # buffer too small
+    assert _call_bounds(L, p, nbytes=0) == -1
     assert _call_bounds(L, p, q=T(0, 0, 5120, 128)) == -1                   # null q
     assert _call_bounds(L, p, q=T(0x20008, 0, 5120, 128)) == -3             # q not 16-aligned
     assert _call_bounds(L, p, q=T(0x20000, 0, 5121, 128)) == -3             # stride not 8-multiple
@@ -137,16 +140,17 @@ def test_forged_descriptor_is_rejected(L):
     T = F.Tensor
     kc = (T * 1)(T(0x40000, 0, 5120, 128))
     lens = (ctypes.c_int64 * 1)(10)
+    big = 1 << 40
     assert L.fixedm_attn_fwd(ctypes.byref(d), ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc,
-                             lens, 1, 0x100000, None) == -4
-    assert L.fixedm_finalize(ctypes.byref(d), ctypes.byref(run), 0x100000, T(0x20000, 0, 5120, 128),
+                             lens, 1, 0x100000, big, None) == -4
+    assert L.fixedm_finalize(ctypes.byref(d), ctypes.byref(run), 0x100000, big, T(0x20000, 0, 5120, 128),
                              1, None, None) == -4
     assert L.fixedm_attn_fwd_final(ctypes.byref(d), ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc,
-                                   lens, 1, 0x100000, T(0x20000, 0, 5120, 128), 1, None, None) == -4
+                                   lens, 1, 0x100000, big, T(0x20000, 0, 5120, 128), 1, None, None) == -4
     assert L.fixedm_attn_fwd_final(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
-                                   0x100000, T(0x20000, 0, 5120, 128), 1, None, None) == -1
+                                   0x100000, big, T(0x20000, 0, 5120, 128), 1, None, None) == -1
     assert L.fixedm_attn_fwd(None, ctypes.byref(run), T(0x20000, 0, 5120, 128), kc, kc, lens, 1,
-                             0x100000, None) == -1
+                             0x100000, big, None) == -1
 
 
 def test_binding_checks_sizes_and_shapes():

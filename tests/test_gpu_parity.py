@@ -337,6 +337,15 @@ def test_state_contracts(F):
     with pytest.raises(F.FixedmError) as e:
         F.finalize(desc, run, ws, out)                 # only half the keys visited
     assert e.value.status == -5
+    # the C ABI itself rejects a workspace smaller than fixedm_workspace_bytes, before any launch
+    import ctypes
+    kk, vv, lens, nch = F._chunk_arrays(ks[1:], vs[1:])
+    short = F.workspace_bytes(p) - 1
+    assert F.lib().fixedm_attn_fwd(ctypes.byref(desc), ctypes.byref(run), F.tensor_desc(q), kk, vv, lens, nch,
+                                   F._ptr(ws), short, F._stream(None)) == -1
+    assert F.lib().fixedm_finalize(ctypes.byref(desc), ctypes.byref(run), F._ptr(ws), short,
+                                   F.tensor_desc(out), F.F32, None, F._stream(None)) == -1
+    assert run.kv_visited == 64
     F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)
     with pytest.raises(F.FixedmError) as e:
         F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)   # more keys than sk_total
