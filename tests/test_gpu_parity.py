@@ -285,6 +285,37 @@ def test_v_magnitude_forces_fallback(F):
     assert not ob.v_ok and not ob.elig.any()
 
 
+# (chunk, (b, key in chunk, h, d)) over 521 keys in chunks of 300 and 221: the first key,
+# the first key of the second wave, the last key of a 256-key work item, the first and
+# the last key of the second chunk, and the last key of the ragged tail.
+V_POKES = [(0, (0, 0, 0, 0)), (0, (0, 64, 2, 5)), (0, (0, 255, 1, -1)), (1, (0, 0, 2, 3)),
+           (1, (0, 211, 0, -1)), (1, (0, 220, 2, -1))]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("val", [300.0, -258.0, float("nan"), 256.0, -256.0])
+def test_v_check_anywhere(F, dtype, D, val):
+    """One value row element set to val, at each of V_POKES in turn: the check fails for
+    |val| > 256 and NaN and passes at exactly 256, wherever the element lies."""
+    import torch
+    say(f"edge: V check, {dtype} D={D}, v={val}")
+    B, H, Sq, chunks = 1, 3, 100, (300, 221)
+    p = F.make_problem(dtype, B, H, D, Sq, sum(chunks), 64)
+    for c, (b0, j0, h0, d0) in V_POKES:
+        inp = WL.generic_inputs(51, dtype, B, H, D, Sq, chunks, q_block=64)
+        d0 = d0 % D
+        if dtype == "bf16":
+            inp.v_store[c][b0, j0, h0, d0] = WL.bf16_bits_from_f32(np.array([val], np.float32))[0]
+        else:
+            inp.v_store[c][b0, j0, h0, d0] = val
+        q, ks, vs, _ = device_inputs(inp)
+        desc, buf = F.bounds(p, q, ks, vs)
+        torch.cuda.synchronize()
+        ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=64, dtype=dtype)
+        assert ob.v_ok == (abs(val) <= 256.0), (c, j0, val)
+        check_bounds(gpu_bounds_dict(desc, buf), ob)
+
+
 def test_every_element_written_and_deterministic(F):
     import torch
     say("edge: NaN sentinel + determinism")
