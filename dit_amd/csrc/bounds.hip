@@ -82,23 +82,45 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   if (h >= a.H) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int ci = 0;                                    // chunk of the current key (uniform)
-  for (int64_t j = (int64_t)blockIdx.x * 8; j < a.N; j += (int64_t)a.kslabs * 8) {
-    float f[8][8];
+  const int64_t stride = (int64_t)a.kslabs * 8;
+  // bf16: two of the workgroup's blocks per pass (16 keys in flight a thread), kept as raw
+  // 16-byte words until they are added in key order.
+  constexpr int kRows = sizeof(T) == 2 ? 16 : 8, kW = (int)sizeof(T) / 2;
+  for (int64_t j = (int64_t)blockIdx.x * 8; j < a.N; j += (kRows / 8) * stride) {
+    uint4 raw[kRows][kW];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t jj = j + u;
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t jj = j + (u < 8 ? u : stride + u - 8);
       if (jj < a.N) {
         while (ci + 1 < a.n_chunks && jj >= a.ch[ci + 1].start) ++ci;
         const ChunkDesc& cd = a.ch[ci];
-        load8(reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (jj - cd.start) * cd.k_ss + h * cd.k_sh + 8 * c,
-              f[u]);
+        const uint4* src = reinterpret_cast<const uint4*>(
+            reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + (jj - cd.start) * cd.k_ss + h * cd.k_sh + 8 * c);
+#pragma unroll
+        for (int w = 0; w < kW; ++w) raw[u][w] = src[w];
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j + u < a.N)
+    for (int u = 0; u < kRows; ++u) {
+      if (j + (u < 8 ? u : stride + u - 8) < a.N) {
+        float f[8];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t x[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[u][i];
+          for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(x[i] << 16);
+            f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+          }
+        } else {
+          const uint32_t x[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
+                                 raw[u][kW - 1].x, raw[u][kW - 1].y, raw[u][kW - 1].z, raw[u][kW - 1].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[i];
+      }
+    }
   }
   double* dst = a.kpart + ((int64_t)blockIdx.x * a.B * a.H + (int64_t)b * a.H + h) * a.D + 8 * c;
 #pragma unroll
