@@ -129,8 +129,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the multi-GPU ring is a design note, not built.",
+        print(f"bench.py: the fixed-m benchmark runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the multi-GPU ring is described, not implemented.",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
