@@ -108,6 +108,29 @@ def lse_bound_bf16(q, k_all, scale: float) -> np.ndarray:
     return np.log(2.0) * 2.0**-8 * out + np.log1p(2.0**-8) + 1e-5
 
 
+def out_bound_bf16(q, k_all, v_all, scale: float, ref) -> np.ndarray:
+    """Worst-case |O - ref| of the bf16 path per element, [B, Sq, H, D], for rows over few keys,
+    where the errors do not average out: each probability enters the PV product rounded to bf16
+    (relative <= 2^-8, l sums the fp32 values), which moves O by at most 2^-8 max_j |v_jd|; the
+    logits come from bf16(alpha q), so each moves by at most E = 2^-8 max_j sum_d |alpha q_d k_jd|
+    (base 2) and every normalised weight by a factor within 2^(+-2E), which moves O by at most
+    (2^(2E) - 1) max_j |v_jd - ref_d|.  1e-5 covers the fp32 accumulation.  Holds O(Sq N) memory
+    per (b, h): meant for short key sets."""
+    alpha = float(np.float32(scale)) * O.LOG2E
+    qa = np.abs(alpha * np.asarray(q, np.float64))
+    ka = np.abs(np.asarray(k_all, np.float64))
+    va = np.asarray(v_all, np.float64)
+    ref = np.asarray(ref, np.float64)
+    e = 2.0**-8 * np.einsum("bihd,bjhd->bhij", qa, ka).max(axis=3)        # [B, H, Sq]
+    grow = np.exp2(2.0 * e) - 1.0
+    vmax = np.abs(va).max(axis=1)                                            # [B, H, D]
+    out = np.empty_like(ref)
+    for i in range(ref.shape[1]):
+        spread = np.abs(va - ref[:, i:i + 1]).max(axis=1)                    # [B, H, D]
+        out[:, i] = 2.0**-8 * vmax + grow[:, :, i, None] * spread + 1e-5
+    return out
+
+
 def bf16_rne_bits(x_f32: np.ndarray) -> np.ndarray:
     from dit_amd.workloads import bf16_bits_from_f32
     return bf16_bits_from_f32(x_f32)

@@ -60,6 +60,7 @@ def test_sizes_of_valid_problems():
     assert r.q2_row - r.m_row >= 40 * 18900 * 4 and r.u_row - r.q2_row >= 40 * 18900 * 8
     assert r.scratch - r.u_row >= 40 * 18900 * 8 and all(o % 256 == 0 for o in (r.m_row, r.q2_row, r.u_row))
     assert F.workspace_bytes(_p(shift="row")) == ws
+    assert F.bounds_bytes(_p(batch=3, heads=21845, sq=1, sk_total=2, q_block=64)) > 0   # the most heads
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -79,6 +80,7 @@ def test_sizes_of_valid_problems():
     (dict(softmax_scale=-0.1), -1),
     (dict(softmax_scale=float("nan")), -1),
     (dict(batch=2, heads=40000), -3),
+    (dict(batch=1, heads=65536), -3),         # batch x heads above 65,535
 ])
 def test_invalid_problems(kw, code):
     p = _p(**kw)
