@@ -285,6 +285,34 @@ def test_no_reads_past_a_chunk(F, dtype):
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL[dtype]
 
 
+def test_offsets_past_4gib(F):
+    """A chunk whose key rows lie 16 KiB apart (a view of the first 2 of 64 NaN-filled heads),
+    so its last keys sit past 4 GiB from its base, followed by a small chunk: every address
+    the bounds and attention kernels form stays 64-bit, and no read leaves the view."""
+    import torch
+    say("edge: key offsets past 4 GiB (bf16)")
+    chunks = (262_200, 1000)
+    inp = WL.generic_inputs(63, "bf16", 1, 2, 128, 16, chunks, q_block=64, center="compute")
+    q, ks, vs, _ = device_inputs(inp)
+    big = []
+    for t in (ks[0], vs[0]):
+        pad = torch.full((1, chunks[0], 64, 128), float("nan"), device="cuda", dtype=t.dtype)
+        pad[:, :, :2] = t
+        big.append(pad[:, :, :2])
+    del ks[0], vs[0]
+    assert big[0].stride(1) * (chunks[0] - 1) * 2 >= 2**32
+    ks.insert(0, big[0])
+    vs.insert(0, big[1])
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, center="compute", out_dtype=torch.float32,
+                                    want_lse=True)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=64, center="compute", dtype="bf16")
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    check_output(out.cpu().numpy(), ref, "bf16")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
+
+
 def test_v_magnitude_forces_fallback(F):
     say("edge: |v| > 256")
     ob, _ = _generic(F, 35, "bf16", 1, 2, 128, 200, (150, 100), q_block=64,
