@@ -41,8 +41,8 @@ fixedm_status check_problem(const fixedm_problem* p) {
   if (p->dtype == FIXEDM_F32 && p->head_dim != 64 && p->head_dim != 128) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   if (p->q_block < 64 || p->q_block % 64 != 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   // grid limits of the kernels (y dimension = B*H; 32-bit row indices)
-  if (p->batch * p->heads > 65535) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
-  if (p->sq > (int64_t)1 << 30 || p->sk_total > ((int64_t)1 << 40)) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->batch > 65535 || p->heads > 65535 || p->batch * p->heads > 65535) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->sq > (int64_t)1 << 30 || p->sk_total > ((int64_t)1 << 38)) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   const int64_t n_qtiles = (p->sq + kQTile - 1) / kQTile;
   if (p->batch * p->heads * n_qtiles > ((int64_t)1 << 31) - 1) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   return FIXEDM_OK;

@@ -94,11 +94,11 @@ typedef struct {
 typedef struct {
   int32_t abi_version;   /* must be FIXEDM_ABI_VERSION */
   int32_t dtype;         /* fixedm_dtype of q, k and v */
-  int64_t batch;         /* B >= 1 */
+  int64_t batch;         /* B >= 1; B x H <= 65,535 */
   int64_t heads;         /* H >= 1; MHA only (K/V have the same H as Q) */
   int64_t head_dim;      /* D: 128 (bf16 and fp32) or 64 (fp32 only) */
-  int64_t sq;            /* resident query rows, >= 1 */
-  int64_t sk_total;      /* N: real keys over all chunks, >= 1 (unpadded, [UR] Summary) */
+  int64_t sq;            /* resident query rows, 1 .. 2^30; B x H x ceil(sq / 256) < 2^31 */
+  int64_t sk_total;      /* N: real keys over all chunks, 1 .. 2^38 (unpadded, [UR] Summary) */
   int64_t q_block;       /* rows per shift/eligibility block: positive multiple of 64 */
   float softmax_scale;   /* s; 0 selects fp32(1/sqrt(D)) ([CM] Interface table) */
   int32_t center;        /* fixedm_center */

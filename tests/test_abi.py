@@ -81,6 +81,8 @@ def test_sizes_of_valid_problems():
     (dict(softmax_scale=float("nan")), -1),
     (dict(batch=2, heads=40000), -3),
     (dict(batch=1, heads=65536), -3),         # batch x heads above 65,535
+    (dict(batch=2**40, heads=2**40), -3),     # no overflow in the product check
+    (dict(sk_total=2**38 + 1), -3),
 ])
 def test_invalid_problems(kw, code):
     p = _p(**kw)
