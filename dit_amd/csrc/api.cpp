@@ -42,7 +42,7 @@ fixedm_status check_problem(const fixedm_problem* p) {
   if (p->q_block < 64 || p->q_block % 64 != 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   // grid limits of the kernels (y dimension = B*H; 32-bit row indices)
   if (p->batch > 65535 || p->heads > 65535 || p->batch * p->heads > 65535) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
-  if (p->sq > (int64_t)1 << 30 || p->sk_total > ((int64_t)1 << 38)) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  if (p->sq > (int64_t)1 << 30 || p->sk_total > kMaxKeys) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   const int64_t n_qtiles = (p->sq + kQTile - 1) / kQTile;
   if (p->batch * p->heads * n_qtiles > ((int64_t)1 << 31) - 1) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   return FIXEDM_OK;
@@ -77,13 +77,15 @@ fixedm_status check_chunks(const fixedm_problem& p, const fixedm_tensor* kc, con
   if (n < 1 || kc == nullptr || vc == nullptr || len == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
   int64_t s = 0;
   for (int32_t c = 0; c < n; ++c) {
-    if (len[c] < 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+    // each length and the running sum stay within the key limit, so the sum cannot wrap
+    if (len[c] < 0 || len[c] > kMaxKeys) return FIXEDM_ERR_INVALID_ARGUMENT;
     if (len[c] == 0) continue;
     fixedm_status st = check_tensor(p, kc[c]);
     if (st != FIXEDM_OK) return st;
     st = check_tensor(p, vc[c]);
     if (st != FIXEDM_OK) return st;
     s += len[c];
+    if (s > kMaxKeys) return FIXEDM_ERR_INVALID_ARGUMENT;
   }
   *total = s;
   return FIXEDM_OK;
@@ -356,7 +358,8 @@ fixedm_status check_attn_call(const fixedm_bounds_t* bounds, const fixedm_run_t*
       (st = check_chunks(p, k_chunks, v_chunks, chunk_len, n_chunks, total)) != FIXEDM_OK)
     return st;
   if (run->finalized != 0) return FIXEDM_ERR_STATE;
-  if (run->kv_visited < 0 || run->kv_visited + *total > p.sk_total) return FIXEDM_ERR_STATE;
+  if (run->kv_visited < 0 || run->kv_visited > p.sk_total || run->kv_visited + *total > p.sk_total)
+    return FIXEDM_ERR_STATE;
   return FIXEDM_OK;
 }
 

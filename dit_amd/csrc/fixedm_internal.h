@@ -13,6 +13,7 @@ constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (L
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
 constexpr int kMaxParts = 4;             // key-range parts of a split tail tile (bf16 kernel)
 constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
+constexpr int64_t kMaxKeys = (int64_t)1 << 38;   // most keys of a problem (and of a chunk)
 
 // Grid-tail split of the bf16 attention launch.  The tiles fill whole rounds of one
 // workgroup per compute unit; the remaining `tail` tiles would leave most CUs idle for a

@@ -126,6 +126,11 @@ def test_bounds_argument_errors_before_launch(L):
     assert _call_bounds(L, p, q=T(0x20000, 0, 5121, 128)) == -3             # stride not 8-multiple
     assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(999)) == -1         # sum != sk_total
     assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(-1)) == -1
+    big = 2**62                                                            # four lengths summing to
+    kc4 = (T * 4)(*([T(0x40000, 0, 40 * 128, 128)] * 4))                  # 2^64 + 1000 would wrap
+    lens4 = (ctypes.c_int64 * 4)(big, big, big, big + 1000)                # to sk_total
+    assert _call_bounds(L, p, kc=kc4, vc=kc4, lens=lens4, n=4) == -1
+    assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(2**38 + 1)) == -1
     assert _call_bounds(L, p, n=0) == -1
     assert _call_bounds(L, p, n=33) == -3                                   # too many chunks
     ps = _p(sk_total=1000, sq=100, center="supplied")

@@ -423,6 +423,11 @@ def test_state_contracts(F):
     assert F.lib().fixedm_finalize(ctypes.byref(desc), ctypes.byref(run), F._ptr(ws), short,
                                    F.tensor_desc(out), F.F32, None, F._stream(None)) == -1
     assert run.kv_visited == 64
+    run.kv_visited = 2**63 - 10                        # a forged count: rejected, no wrap-around
+    with pytest.raises(F.FixedmError) as e:
+        F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)
+    assert e.value.status == -5
+    run.kv_visited = 64
     F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)
     with pytest.raises(F.FixedmError) as e:
         F.attn_fwd(desc, run, q, ks[1:], vs[1:], ws)   # more keys than sk_total
