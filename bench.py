@@ -10,6 +10,7 @@ head_dim 128, 18,900 resident queries, 75,600 keys in 4 chunks), resident in HBM
 the timed region starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--per-chunk] [--no-cpu-baseline]
+                    [--fallback none|all|FRACTION]
 """
 from __future__ import annotations
 
@@ -111,6 +112,39 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
+def apply_fallback(inp, mode: str, q_block: int, np, WL):
+    """Edits the drawn inputs so that some q-blocks fail the gate and take the online-softmax
+    body (for timing that body).  Returns the number of (b, h, q-block) pairs scaled, or None."""
+    if mode == "none":
+        return None
+    wl = inp.wl
+
+    def put(store, x):
+        return WL.bf16_bits_from_f32(x) if wl.dtype == "bf16" else x.astype(np.float32)
+
+    if mode == "all":
+        v0 = inp._f32(inp.v_store[0]).copy()
+        v0[0, 0, 0, 0] = 300.0
+        inp.v_store[0] = put(inp.v_store[0], v0)
+        return None
+    frac = float(mode)
+    if not 0.0 < frac <= 1.0:
+        raise SystemExit(f"bench.py: --fallback {mode}: expected none, all or a fraction in (0, 1]")
+    every = max(1, int(round(1.0 / frac)))
+    nqb = -(-wl.sq // q_block)
+    qf = inp._f32(inp.q_store).copy()
+    n = 0
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            for beta in range(nqb):
+                if ((b * wl.heads + h) * nqb + beta) % every == 0:
+                    lo, hi = beta * q_block, min((beta + 1) * q_block, wl.sq)
+                    qf[b, lo:hi, h] *= np.float32(8.0)
+                    n += 1
+    inp.q_store = put(inp.q_store, qf)
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +155,15 @@ def main():
     ap.add_argument("--per-chunk", action="store_true",
                     help="one fixedm_attn_fwd per ring chunk + fixedm_finalize instead of one "
                          "fixedm_attn_fwd_final over all chunks")
+    ap.add_argument("--fallback", default="none",
+                    help="which q-blocks take the online-softmax body: 'none' (the workload as "
+                         "drawn), 'all' (one V element set to 300 fails the |v| <= 256 check, so "
+                         "every block falls back), or a fraction such as 0.01 (that share of the "
+                         "(head, q-block) pairs, every 1/fraction-th, gets its queries scaled by 8, "
+                         "which lifts its bound above the gate)")
+    ap.add_argument("--q-block", type=int, default=None,
+                    help="rows per shift/eligibility block (default: the workload's, 256); 64 puts "
+                         "four blocks in one workgroup, so a loud block shares it with fixed-m waves")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB fp32 read+write kernel (3 times): the reference "
@@ -156,6 +199,8 @@ def main():
     wl = WL.get(args.config)
     log(f"bench: drawing inputs for config {wl.cid} ({wl.name})")
     inp = WL.make_inputs(wl.cid)
+    q_block = args.q_block or wl.q_block
+    loud_blocks = apply_fallback(inp, args.fallback, q_block, np, WL)
     q = to_dev(inp.q_store, wl.dtype, torch, np)
     ks = [to_dev(c, wl.dtype, torch, np) for c in inp.k_store]
     vs = [to_dev(c, wl.dtype, torch, np) for c in inp.v_store]
@@ -163,7 +208,7 @@ def main():
     order = [0] + list(range(len(ks) - 1, 0, -1))        # rank 0's ring visit order
     ks, vs = [ks[i] for i in order], [vs[i] for i in order]
 
-    p = F.make_problem(wl.dtype, wl.batch, wl.heads, wl.head_dim, wl.sq, wl.sk, wl.q_block,
+    p = F.make_problem(wl.dtype, wl.batch, wl.heads, wl.head_dim, wl.sq, wl.sk, q_block,
                        0.0, wl.center)
     buf = torch.empty(F.bounds_bytes(p), dtype=torch.uint8, device="cuda")
     ws = F.alloc_workspace(p, q.device)
@@ -253,7 +298,8 @@ def main():
         "config": {
             "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
             "sq": wl.sq, "sk": wl.sk, "chunks": list(wl.chunks), "ring_order": order,
-            "q_block": wl.q_block, "centering": wl.center, "eligible_fraction": elig_frac,
+            "q_block": q_block, "centering": wl.center, "eligible_fraction": elig_frac,
+            "fallback": args.fallback, "loud_qblocks": loud_blocks,
             "step": ("bounds + attn_fwd_final over the 4 ring chunks (bf16 out written by the "
                      "attention launch)" if fused else
                      "bounds + 4 x attn_fwd (one per ring chunk) + finalize(bf16 out)"),

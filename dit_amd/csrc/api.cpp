@@ -59,6 +59,9 @@ fixedm_status check_tensor(const fixedm_problem& p, const fixedm_tensor& t) {
   const int64_t vec = p.dtype == FIXEDM_BF16 ? 8 : 4;  // elements per 16 bytes
   if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   if (t.stride_b % vec || t.stride_s % vec || t.stride_h % vec) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  // The bf16 attention kernel's K/V loads take a row's byte offset within a 32-row tile as
+  // an unsigned 32-bit lane offset (31 rows x stride_s x 2 bytes + 240 must stay below 2^32).
+  if (p.dtype == FIXEDM_BF16 && t.stride_s > kMaxRowStrideBf16) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   return FIXEDM_OK;
 }
 
@@ -164,8 +167,7 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out) {
   out->q2_row = off; off = align256(off + rows * 8);
   out->u_row = off; off = align256(off + rows * 8);
   out->scratch = off;
-  if (p.center == FIXEDM_CENTER_COMPUTE)
-    off = align256(off + (size_t)kmean_slabs(p.batch, p.heads, p.sk_total) * bh * p.head_dim * 8);
+  off += bounds_scratch(p).total;           // key-mean partial sums and flags (COMPUTE only)
   out->total = off;
   return true;
 }
@@ -255,14 +257,21 @@ size_t fixedm_workspace_bytes(const fixedm_problem* p) {
   return w.total;
 }
 
-fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
-                            const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
-                            const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
-                            fixedm_bounds_t* out, void* stream) {
-  fixedm_status st = check_problem(p);
-  if (st != FIXEDM_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// fixedm_bounds: the checks, the descriptor and the launches.  bounds_dev holds the outputs
+// (need_bytes of it checked); the scratch of COMPUTE centring lies at scratch_base with the
+// given layout.
+fixedm_status bounds_impl(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
+                          const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
+                          const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
+                          size_t need_bytes, char* scratch_base, const BoundsScratch& sc,
+                          fixedm_bounds_t* out, void* stream) {
+  fixedm_status st = FIXEDM_OK;
   if (out == nullptr || bounds_dev == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
-  if (bounds_dev_bytes < fixedm_bounds_bytes(p)) return FIXEDM_ERR_INVALID_ARGUMENT;
+  if (bounds_dev_bytes < need_bytes) return FIXEDM_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)bounds_dev & 255) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
   if ((st = check_tensor(*p, q)) != FIXEDM_OK) return st;
   if (n_chunks > kMaxBoundsChunks) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
@@ -313,8 +322,9 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixe
   a.k2 = reinterpret_cast<unsigned long long*>(base + lay.k2);
   a.k_mean = reinterpret_cast<float*>(base + lay.k_mean);
   a.v_bad = reinterpret_cast<int32_t*>(base + lay.v_bad);
-  a.kpart = reinterpret_cast<double*>(base + lay.scratch);
-  a.kslabs = kmean_slabs(p->batch, p->heads, p->sk_total);
+  a.kpart = reinterpret_cast<double*>(scratch_base + sc.kpart);
+  a.kflag = reinterpret_cast<int32_t*>(scratch_base + sc.kflag);
+  a.kslabs = sc.slabs;
   if (p->shift == FIXEDM_SHIFT_ROW) {
     a.m_row = reinterpret_cast<int32_t*>(base + lay.m_row);
     a.q2_row = reinterpret_cast<double*>(base + lay.q2_row);
@@ -323,6 +333,22 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixe
   if (launch_bounds(a, static_cast<hipStream_t>(stream)) != hipSuccess) return FIXEDM_ERR_HIP;
   *out = d;
   return FIXEDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
+                            const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
+                            const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
+                            fixedm_bounds_t* out, void* stream) {
+  const fixedm_status st = check_problem(p);
+  if (st != FIXEDM_OK) return st;
+  BoundsLayout lay;
+  bounds_layout(*p, &lay);
+  return bounds_impl(p, q, k_chunks, v_chunks, chunk_len, n_chunks, k_mean_in, bounds_dev, bounds_dev_bytes,
+                     lay.total, static_cast<char*>(bounds_dev) + lay.scratch, bounds_scratch(*p), out, stream);
 }
 
 fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run) {
@@ -393,6 +419,7 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.m = reinterpret_cast<const int32_t*>(bbase + lay.m);
   a.m_row = p.shift == FIXEDM_SHIFT_ROW ? reinterpret_cast<const int32_t*>(bbase + lay.m_row) : nullptr;
   a.elig = reinterpret_cast<const uint8_t*>(bbase + lay.elig);
+  a.u = reinterpret_cast<const double*>(bbase + lay.u);
   a.k_mean = reinterpret_cast<const float*>(bbase + lay.k_mean);
   a.alpha = bounds->alpha;
   a.alpha64 = (double)p.softmax_scale * kLog2e;

@@ -30,8 +30,10 @@
 //   * Fixed-m body, software-pipelined per 32-key tile t: the MFMAs of O += V(t-1) P(t-1)
 //     are independent of the VALU work exp2(alpha S(t) - shift), so the matrix cores and
 //     the vector ALUs overlap within one wave.
-//   * The body (fixed-m or online softmax) is chosen per wave from the eligibility byte of
-//     its q-block: a wave-uniform branch, no divergence on the eligible path.
+//   * The body is chosen per wave from its q-block's eligibility byte and bound U: the
+//     fixed-m assembly loop on bf16(alpha q) (U <= kR17MaxU), the fixed-m assembly loop that
+//     applies alpha in fp32 (eligible, U above it), or online softmax (ineligible).  A
+//     wave-uniform branch.
 //   * One launch folds one K/V chunk (one ring step) into the workspace.
 //   * Ragged KV tails: rows past a chunk's end are clamped to its last row on load and
 //     their probabilities forced to zero; no padding copies.  Query rows past Sq are
@@ -62,6 +64,12 @@ constexpr int kAhead = kStages - 2;            // tiles in flight ahead of the c
 constexpr int kLoadsPerTile = 4;               // global->LDS instructions per wave per tile
 constexpr int kVRing = kStages * kTileBytes;   // the V ring starts after the K ring
 constexpr int kLdsBytes = 2 * kStages * kTileBytes;   // 128 KB
+// Largest block bound U for which the fixed-m body takes its logits from bf16(alpha q).  The
+// rounding (relative <= 2^-8 per element) moves a base-2 logit by at most 2^-8 sum_d
+// |alpha q_d k_d| <= 2^-8 U; in practice the moves are random and far smaller, and up to
+// U = 20 they add about 1e-3 at most to the output error of the bf16 probabilities (sharp
+// rows over 64 keys), while above it they grow with U.  Blocks above it apply alpha in fp32.
+constexpr double kR17MaxU = 20.0;
 
 // s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -352,6 +360,22 @@ __device__ __attribute__((always_inline)) void softmax_fixed(const f32x16 (&s)[2
   }
 }
 
+// Fixed-m probabilities with the logit factor applied in fp32 (a one-tile chunk piece of an
+// eligible block whose bound is above kR17MaxU): S holds q . k from the unscaled query
+// fragments (masked rows -inf), e = alpha S - (m + c_i), p = 2^e.  No max, no rescale.
+__device__ __attribute__((always_inline)) void softmax_fixed_fp32(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
+                                                                  float (&lsum)[2], const float (&shift)[2],
+                                                                  float alpha) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    f32x16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -shift[n]));
+    p[n][0] = pack8_sum(e, 0, lsum[n]);
+    p[n][1] = pack8_sum(e, 8, lsum[n]);
+  }
+}
+
 // Online-softmax probabilities of one tile (the fallback body): raise the running max,
 // rescale the accumulator and the row sum, then exponentiate against the new max.  Masked
 // rows arrive as -inf scores (every tile this body visits has at least one real key).
@@ -403,7 +427,12 @@ __device__ inline FixedSchedule fixed_schedule(int64_t len) {
   return {fast, tail, kStages * (fast + tail)};
 }
 
-template <bool kFixed>
+// The three bodies a wave can run: the fixed-m assembly loop with logits from bf16(alpha q),
+// the fixed-m assembly loop that applies the logit factor in fp32 (one FMA per score), and
+// the online-softmax fallback (compiled).
+enum Body { kFixedAsm, kFixedAsmF32, kOnline };
+
+template <Body kBody>
 __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, const ChunkDesc& cd,
                                                          const uint8_t* smem, const bf16x8 (&qf)[2][8],
                                                          f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
@@ -449,14 +478,17 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
   for (int t = 0; t < kAhead; ++t) issue_tile(const_cast<uint8_t*>(smem), g, t, t);
   wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
   barrier();
-  if (kFixed) {
+  if (kBody == kFixedAsm || kBody == kFixedAsmF32) {
     const float nshift[2] = {-shift[0], -shift[1]};
     if (n_tiles == 1) {
       f32x16 s[2];
       bf16x8 p[2][2];
-      compute_s_fixed(smem, g, 0, qf, s, nshift, tile_rows(g, 0), hh);
+      // the S chain starts from -(m + c_i) (bf16(alpha q) fragments) or from 0 (fp32 alpha)
+      const float init[2] = {kBody == kFixedAsm ? nshift[0] : 0.0f, kBody == kFixedAsm ? nshift[1] : 0.0f};
+      compute_s_fixed(smem, g, 0, qf, s, init, tile_rows(g, 0), hh);
       ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
-      softmax_fixed(s, p, lsum);
+      if (kBody == kFixedAsm) softmax_fixed(s, p, lsum);
+      else softmax_fixed_fp32(s, p, lsum, shift, a.alpha);
       bf16x8 vf[2][4];
       load_v(smem, g, 0, vf);
       pv_tile_asm(o, vf, p);
@@ -484,10 +516,16 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       const int n_full = (int)(g.len / kKT), rem = (int)(g.len - (int64_t)n_full * kKT);
       // tile 1 is whole, or (33..63 keys) the partial last tile whose real keys start at 32 - rem
       const uint32_t lo1 = n_full >= 2 ? 0u : (uint32_t)(kKT - rem);
-      fixed_loop_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
-                     uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last, (uint32_t)n_full,
-                     (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast, (uint32_t)sched.tail,
-                     (uint32_t)(kStages * sched.fast + 2));
+      if (kBody == kFixedAsm)
+        fixed_loop_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
+                       uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last, (uint32_t)n_full,
+                       (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast, (uint32_t)sched.tail,
+                       (uint32_t)(kStages * sched.fast + 2));
+      else
+        fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
+                             uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last,
+                             (uint32_t)n_full, (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast,
+                             (uint32_t)sched.tail, (uint32_t)(kStages * sched.fast + 2), a.alpha);
     }
   } else {
     const float zero[2] = {0.0f, 0.0f};
@@ -520,7 +558,7 @@ __device__ __attribute__((always_inline)) inline void pin_state(f32x16 (&o)[2][4
 // Folds keys [klo, khi) of the launch's chunk sequence (the chunks concatenated in call
 // order) into the resident accumulators: one ring pass per chunk piece, the accumulators
 // and the online body's running max carried in registers from piece to piece.
-template <bool kFixed>
+template <Body kBody>
 __device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64_t klo, int64_t khi,
                                                         const uint8_t* smem, const bf16x8 (&qf)[2][8],
                                                         f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
@@ -534,9 +572,9 @@ __device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64
     cd.k = reinterpret_cast<const uint16_t*>(cd.k) + (s0 - c0) * cd.k_ss;
     cd.v = reinterpret_cast<const uint16_t*>(cd.v) + (s0 - c0) * cd.v_ss;
     cd.len = s1 - s0;
-    if (kFixed) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
-    run_chunk<kFixed>(a, cd, smem, qf, o, lsum, shift, b, h);
-    if (kFixed) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
+    if (kBody != kOnline) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
+    run_chunk<kBody>(a, cd, smem, qf, o, lsum, shift, b, h);
+    if (kBody != kOnline) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
   }
 }
 
@@ -573,12 +611,16 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   // barriers and assembly that keeps its state in fixed registers).
   const bool fixed = __builtin_amdgcn_readfirstlane((int)a.elig[bq]) != 0;
   const int mshift = __builtin_amdgcn_readfirstlane(a.m[bq]);
+  // Eligible blocks with a bound above kR17MaxU take the fixed-m body with the logit factor
+  // applied in fp32: the rounding of bf16(alpha q) moves a base-2 logit by up to 2^-8 U.
+  const bool r17 = fixed && __builtin_amdgcn_readfirstlane((int)(a.u[bq] <= kR17MaxU)) != 0;
 
   // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean.
-  // The fixed-m body takes its logits in base 2 straight from the MFMA: its query fragments
-  // are bf16(alpha q) (fp32 product, one rounding: the base-2 rescale of Q that the TPU path
-  // folds into Q's producer, [FM] Summary "Relayout optimization") and c_i = (alpha q_i) .
-  // k_mean.  The online body keeps q and scales its scores by alpha.
+  // The fixed-m assembly body takes its logits in base 2 straight from the MFMA: its query
+  // fragments are bf16(alpha q) (fp32 product, one rounding: the base-2 rescale of Q that the
+  // TPU path folds into Q's producer, [FM] Summary "Relayout optimization", bit-identical
+  // there by the [UR] review thread) and c_i = (alpha q_i) . k_mean.  The other two bodies
+  // keep q and scale their scores by alpha in fp32 (c_i = alpha (q_i . k_mean)).
   bf16x8 qf[2][8];
   float cdot[2];
   const float* km = a.k_mean + (int64_t)bh * kD;
@@ -592,7 +634,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) {
       const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * hh);
       uint32_t u[4] = {w.x, w.y, w.z, w.w};
-      if (fixed) {
+      if (r17) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x2 x = {__uint_as_float(u[i] << 16) * a.alpha, __uint_as_float(u[i] & 0xffff0000u) * a.alpha};
@@ -607,9 +649,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
         dot = __builtin_fmaf(__uint_as_float(u[i] & 0xffff0000u), km[16 * kk + 8 * hh + 2 * i + 1], dot);
       }
     }
-    // q . k_mean: this half's dims plus the other half's, low half first on both lanes
+    // q . k_mean: this half's dims plus the other half's, low half first on both lanes; the
+    // assembly body's fragments already carry alpha, the fp32-factor body applies it here
     const float other = __shfl_xor(dot, 32, 64);
     cdot[n] = hh == 0 ? dot + other : other + dot;
+    if (!r17) cdot[n] *= a.alpha;
   }
   // The query fragments are read only as MFMA B operands, which may sit in accumulation
   // registers: pin them there so the 256 architectural VGPRs hold S, P and the K/V
@@ -637,10 +681,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
       }
       shift[n] = (float)mm + cdot[n];
     }
-    run_keys<true>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
+    if (r17) run_keys<kFixedAsm>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
+    else run_keys<kFixedAsmF32>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;
-    run_keys<false>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
+    run_keys<kOnline>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
   }
 
   if (a.final_out && !split) {

@@ -14,11 +14,15 @@
 //
 // Arithmetic contract: every sum of squares runs over d in index order in fp64, without
 // contraction (this file is built with -ffp-contract=off); products of bf16/fp32 values
-// are exact in fp64.  Maxima are order-free.  The k_mean sum is a fixed-order tree in
-// fp64; for bf16/fp32 keys of ordinary magnitude every partial sum is exact, so the result
-// equals the in-order sum.  U = alpha64 * sqrt(Q2 * K2) in exactly that order.
+// are exact in fp64.  Maxima are order-free.  The key sum behind k_mean is EXACT, rounded
+// once to fp64, then divided by N in fp64 and rounded to fp32, so no summation order enters:
+// the key-slab partial sums run in fp64 with every addition checked for exactness (TwoSum),
+// the exact partials are combined in a fixed-point accumulator, and any element whose
+// partial sums were not exact is summed again, key by key, in that accumulator.
+// U = alpha64 * sqrt(Q2 * K2) in exactly that order.
 #include <math.h>
 
+#include "exact_sum.h"
 #include "fixedm_internal.h"
 
 namespace fixedm {
@@ -64,6 +68,7 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
     if (i < nkm) {
       if (a.center == FIXEDM_CENTER_NONE) a.k_mean[i] = 0.0f;
       else if (a.center == FIXEDM_CENTER_SUPPLIED) a.k_mean[i] = a.k_mean_in[i];
+      else a.kflag[i] = 0;
     }
     if (i == 0) *a.v_bad = 0;
   }
@@ -74,6 +79,58 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
 // of blocks w, w + kslabs, w + 2 kslabs, ... (8 keys a block).  A key's rows of the head group
 // are adjacent in memory, so each key is one contiguous read of the workgroup, and the
 // workgroups in flight stream one contiguous window of keys.
+//
+// Exactness: the thread also keeps, per element, the largest |x| and the smallest nonzero |x|
+// of its keys (integer max / min of the magnitude bits, which order like the values; packed
+// 16-bit ops for bf16).  Every key is then a multiple of the smallest one's unit in the last
+// place, and every partial sum of n keys, in any order, stays below n max|x|; when that is
+// below 2^53 such units, every fp64 addition was exact.  Otherwise (keys spanning many
+// binades, a NaN or an infinity) the element is flagged for the exact re-summation.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct MagRange;                     // largest and smallest-nonzero magnitude bits per element
+template <>
+struct MagRange<uint16_t> {
+  static constexpr int kMant = 7;    // explicit mantissa bits of bf16
+  u16x2 mx[4], mn[4];                // element 2 i + half in word i
+  __device__ void init() {
+    for (int i = 0; i < 4; ++i) { mx[i] = u16x2{0, 0}; mn[i] = u16x2{0xffff, 0xffff}; }
+  }
+  __device__ void add(const uint32_t (&w)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u16x2 m = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
+      mx[i] = __builtin_elementwise_max(mx[i], m);
+      mn[i] = __builtin_elementwise_min(mn[i], (u16x2)(m - (u16x2){1, 1}));   // 0 wraps to 0xffff
+    }
+  }
+  __device__ uint32_t hi(int e) const { return mx[e >> 1][e & 1]; }
+  __device__ uint32_t lo1(int e) const { return mn[e >> 1][e & 1]; }   // min nonzero - 1
+  static constexpr uint32_t kNone = 0xffffu;
+  __device__ static int exp_field(uint32_t m) { return (int)(m >> kMant); }
+};
+template <>
+struct MagRange<float> {
+  static constexpr int kMant = 23;
+  uint32_t mx[8], mn[8];
+  __device__ void init() {
+    for (int i = 0; i < 8; ++i) { mx[i] = 0; mn[i] = 0xffffffffu; }
+  }
+  __device__ void add(const uint32_t (&w)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = w[i] & 0x7fffffffu;
+      mx[i] = max(mx[i], m);
+      mn[i] = min(mn[i], m - 1u);
+    }
+  }
+  __device__ uint32_t hi(int e) const { return mx[e]; }
+  __device__ uint32_t lo1(int e) const { return mn[e]; }
+  static constexpr uint32_t kNone = 0xffffffffu;
+  __device__ static int exp_field(uint32_t m) { return (int)(m >> kMant); }
+};
+
 template <typename T>
 __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   const int per = a.D / 8;
@@ -81,6 +138,9 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   const int b = blockIdx.y, h = blockIdx.z * kBoundsHeads + hl;
   if (h >= a.H) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  MagRange<T> mag;
+  mag.init();
+  int64_t count = 0;                             // keys this thread adds
   int ci = 0;                                    // chunk of the current key (uniform)
   const int64_t stride = (int64_t)a.kslabs * 8;
   // bf16: two of the workgroup's blocks per pass (16 keys in flight a thread), kept as raw
@@ -104,8 +164,10 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
     for (int u = 0; u < kRows; ++u) {
       if (j + (u < 8 ? u : stride + u - 8) < a.N) {
         float f[8];
+        ++count;
         if constexpr (sizeof(T) == 2) {
           const uint32_t x[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
+          mag.add(x);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f[2 * i] = __uint_as_float(x[i] << 16);
@@ -114,6 +176,7 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
         } else {
           const uint32_t x[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
                                  raw[u][kW - 1].x, raw[u][kW - 1].y, raw[u][kW - 1].z, raw[u][kW - 1].w};
+          mag.add(x);
 #pragma unroll
           for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(x[i]);
         }
@@ -122,37 +185,98 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
       }
     }
   }
-  double* dst = a.kpart + ((int64_t)blockIdx.x * a.B * a.H + (int64_t)b * a.H + h) * a.D + 8 * c;
+  // ceil(log2 count): partial sums stay below 2^lc max|x|
+  int lc = 0;
+  while (((int64_t)1 << lc) < count) ++lc;
+  const int64_t el = ((int64_t)b * a.H + h) * a.D + 8 * c;
+  double* dst = a.kpart + (int64_t)blockIdx.x * a.B * a.H * a.D + el;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = acc[i];
+  for (int i = 0; i < 8; ++i) {
+    dst[i] = acc[i];
+    const uint32_t lo1 = mag.lo1(i), hi = mag.hi(i);
+    if (lo1 == MagRange<T>::kNone) continue;                 // no nonzero key: the sum is 0
+    const int emax = MagRange<T>::exp_field(hi), emin = MagRange<T>::exp_field(lo1 + 1);
+    // |x| < 2^(max(emax,1) - 126) and x a multiple of 2^(max(emin,1) - 127 - mant):
+    // exact while max(emax,1) - 126 + lc <= max(emin,1) - 127 - mant + 53
+    const bool nonfinite = emax == 255;
+    const int top = (emax > 1 ? emax : 1) + lc, room = (emin > 1 ? emin : 1) + 52 - MagRange<T>::kMant;
+    if (nonfinite || top > room) atomicOr(a.kflag + el + i, 1);
+  }
 }
 
-// k_mean[b,h,d] = fp32(sum of the partial sums / N): thread (g, e) of a 256-thread workgroup
-// adds partials g, g + 8, ... for element e; the 8 group sums are then added in g order.
+// k_mean[b,h,d] = fp32(fl64(exact key sum) / N) for the elements whose slab partial sums are
+// all exact (kflag clear): thread (g, e) of a 256-thread workgroup adds partials g, g + 8, ...
+// of element e into its own fixed-point accumulator in LDS (exact, so no order enters); the
+// 8 accumulators of the element are then added and rounded once.  Flagged elements are left
+// to kmean_exact_kernel.
 __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
-  __shared__ double part[8][32];
+  __shared__ int64_t lim[8][32][kLimbs];
   const int64_t n = (int64_t)a.B * a.H * a.D;
   const int g = threadIdx.x >> 5, el = threadIdx.x & 31;
   const int64_t i = (int64_t)blockIdx.x * 32 + el;
-  double s = 0.0;
-  if (i < n) {
+  const bool mine = i < n && a.kflag[i] == 0;
+  int64_t* acc = lim[g][el];
+  for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
+  if (mine) {
     int sl = g;
-    for (; sl + 56 < a.kslabs; sl += 64) {      // eight partials in flight, added in order
+    for (; sl + 56 < a.kslabs; sl += 64) {      // eight partials in flight
       double x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) x[u] = a.kpart[(int64_t)(sl + 8 * u) * n + i];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s = s + x[u];
+      for (int u = 0; u < 8; ++u) exact_add(acc, x[u]);
     }
-    for (; sl < a.kslabs; sl += 8) s = s + a.kpart[(int64_t)sl * n + i];
+    for (; sl < a.kslabs; sl += 8) exact_add(acc, a.kpart[(int64_t)sl * n + i]);
   }
-  part[g][el] = s;
   __syncthreads();
-  if (g == 0 && i < n) {
-    double t = part[0][el];
-    for (int k = 1; k < 8; ++k) t = t + part[k][el];
-    a.k_mean[i] = (float)(t / (double)a.N);
+  if (g == 0 && mine) {
+    int64_t tot[kLimbs];
+    for (int k = 0; k < kLimbs; ++k) {
+      int64_t t = 0;
+      for (int gg = 0; gg < 8; ++gg) t += lim[gg][el][k];
+      tot[k] = t;
+    }
+    a.k_mean[i] = (float)(exact_round(tot) / (double)a.N);
   }
+}
+
+// k_mean for the flagged elements (a slab partial sum that was not exact, or a non-finite
+// key): one workgroup per (b, h), thread d re-sums dim d over every key of every chunk in
+// the fixed-point accumulator (key rows are read coalesced across the threads).  A NaN, or
+// both infinities, give NaN; otherwise an infinity gives itself.  Elements with kflag clear
+// return at once, so the launch costs a few microseconds when nothing is flagged.
+template <typename T>
+__global__ __launch_bounds__(128) void kmean_exact_kernel(BoundsArgs a) {
+  __shared__ int64_t lim[128][kLimbs];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int d = threadIdx.x;
+  if (d >= a.D) return;
+  const int64_t i = (int64_t)bh * a.D + d;
+  if (a.kflag[i] == 0) return;
+  int64_t* acc = lim[d];
+  for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
+  bool nan = false, pinf = false, ninf = false;
+  int64_t since = 0;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const ChunkDesc& cd = a.ch[c];
+    const T* col = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + h * cd.k_sh + d;
+    for (int64_t j = 0; j < cd.len; ++j) {
+      const double x = (double)load_elem(col + j * cd.k_ss);
+      if (isnan(x)) nan = true;
+      else if (isinf(x)) (x > 0 ? pinf : ninf) = true;
+      else exact_add(acc, x);
+      if (++since == ((int64_t)1 << 28)) {
+        exact_normalize(acc);
+        since = 0;
+      }
+    }
+  }
+  double sum;
+  if (nan || (pinf && ninf)) sum = __longlong_as_double(0x7ff8000000000000ll);
+  else if (pinf) sum = __longlong_as_double(0x7ff0000000000000ll);
+  else if (ninf) sum = -__longlong_as_double(0x7ff0000000000000ll);
+  else sum = exact_round(acc);
+  a.k_mean[i] = (float)(sum / (double)a.N);
 }
 
 // One row per thread in the norm kernels: every 16-byte piece of the row is loaded before
@@ -411,6 +535,7 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
     kmean_partial_kernel<T><<<dim3((unsigned)a.kslabs, (unsigned)a.B, groups), hpg * (a.D / 8), 0, s>>>(a);
     const int64_t n = (int64_t)a.B * a.H * a.D;
     kmean_final_kernel<<<(unsigned)((n + 31) / 32), 256, 0, s>>>(a);
+    kmean_exact_kernel<T><<<(unsigned)(a.B * a.H), 128, 0, s>>>(a);
   }
   constexpr int W = NormGeom<T>::kWaves;
   const int64_t n_hq = (a.H + W - 1) / W;

@@ -14,6 +14,7 @@ constexpr int kQTile = 256;              // query rows per attention workgroup (
 constexpr int kMaxParts = 4;             // key-range parts of a split tail tile (bf16 kernel)
 constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
 constexpr int64_t kMaxKeys = (int64_t)1 << 38;   // most keys of a problem (and of a chunk)
+constexpr int64_t kMaxRowStrideBf16 = (int64_t)1 << 26;   // largest sequence stride of a bf16 tensor
 
 // Grid-tail split of the bf16 attention launch.  The tiles fill whole rounds of one
 // workgroup per compute unit; the remaining `tail` tiles would leave most CUs idle for a
@@ -38,14 +39,33 @@ inline SplitPlan split_plan(int64_t tiles, int cus) {
   return sp;
 }
 
-// Key slabs of the deterministic k_mean reduction: enough workgroups to fill the chip
-// (about 512 with B x head groups), at most one slab per 16 keys.
-inline int kmean_slabs(int64_t B, int64_t H, int64_t N) {
+// Key slabs of the k_mean reduction: enough workgroups to fill the chip (about 512 with
+// B x head groups), at most one slab per 16 keys, and at most max_slabs.  The key sum is
+// exact, so the slab count changes the speed only, never a bit of the result.
+inline int kmean_slabs(int64_t B, int64_t H, int64_t N, int64_t max_slabs = 1 << 30) {
   const int64_t groups = B * ((H + kBoundsHeads - 1) / kBoundsHeads);
   int64_t s = (512 + groups - 1) / groups;
   if (s > N / 16) s = N / 16;
+  if (s > max_slabs) s = max_slabs;
   if (s < 1) s = 1;
   return (int)s;
+}
+
+// Scratch of one bounds call in COMPUTE centring: the key-mean partial sums
+// [slabs][B*H][D] fp64, then their exactness flags [B*H][D] int32 (byte offsets from the
+// scratch base, 256-byte aligned).  Empty for the other centring modes.
+struct BoundsScratch {
+  int32_t slabs;
+  size_t kpart, kflag, total;
+};
+inline BoundsScratch bounds_scratch(const fixedm_problem& p, int64_t max_slabs = 1 << 30) {
+  BoundsScratch s{0, 0, 0, 0};
+  if (p.center != FIXEDM_CENTER_COMPUTE) return s;
+  const size_t el = (size_t)(p.batch * p.heads) * (size_t)p.head_dim;
+  s.slabs = kmean_slabs(p.batch, p.heads, p.sk_total, max_slabs);
+  s.kflag = ((size_t)s.slabs * el * 8 + 255) & ~(size_t)255;
+  s.total = (s.kflag + el * 4 + 255) & ~(size_t)255;
+  return s;
 }
 
 struct ChunkDesc {
@@ -94,6 +114,7 @@ struct BoundsArgs {
   float* k_mean;
   int32_t* v_bad;
   double* kpart;            // [kslabs][B*H][D] partial key sums
+  int32_t* kflag;           // [B*H][D]: nonzero when a partial sum of that element rounded
   int32_t kslabs;
   // per-row shifts (shift == FIXEDM_SHIFT_ROW; null otherwise): [B, H, Sq]
   int32_t* m_row;
@@ -114,6 +135,7 @@ struct AttnArgs {
   const int32_t* m;
   const int32_t* m_row;   // per-row shifts [B, H, Sq], or null for one shift per q-block
   const uint8_t* elig;
+  const double* u;        // per-block bound U [B, H, nQB]
   const float* k_mean;
   float alpha;       // fp32(scale * log2 e)
   double alpha64;    // fp64 scale * log2 e (fp32 path)

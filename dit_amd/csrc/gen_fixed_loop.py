@@ -83,6 +83,7 @@ S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
 S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
 S_KT6, S_VT6, S_LO1 = 82, 84, 86      # tile 6's addresses (the priming step's DMA); tile 1's first real row
 KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
+ALPHA = 180                           # v180: alpha (fp32), the logit factor of the fp32a variant
 LSUM_HI = 186                         # v186-v187: row sums of the high halves
 
 
@@ -142,6 +143,11 @@ EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it 
 BARRIER_AFTER = 2                     # PV MFMAs issued before a step's vmcnt wait and barrier
 DMA_WITH_KREAD = True                 # a K fragment read between each M0 write and its DMA
                                       # (DMAs first with s_nop 0, K reads after: same speed)
+ROWSUM = os.environ.get("FIXEDM_ROWSUM", "f32add")   # how the row sums add a word of P:
+                                      # "f32add": the two fp32 probabilities (two adds);
+                                      # "dot2": the word's two bf16 values, v_dot2_f32_bf16
+                                      # against (1, 1) (one op; the sum the PV product sees)
+ONES = 191                            # v191: bf16 pair (1.0, 1.0) for the dot2 row sums
 V_TR_PER_SLOT, V_TR_FIRST = 2, 0      # V^T transpose reads per S MFMA slot, from this slot on
                                       # (one per slot over all 16, or two per slot in the second
                                       # half, measured 0.5-0.6% slower)
@@ -178,6 +184,11 @@ def softmax_plan(buf):
         x = s_first(buf, n) + 2 * i
         pw = p_first(buf, n) + i
         cvt = add(f"v_cvt_pk_bf16_f32 v{pw}, v{x}, v{x + 1}", True, word_exps[w])
+        if ROWSUM == "dot2":
+            acc = (LSUM if i % 2 == 0 else LSUM_HI) + n
+            d2 = add(f"v_dot2_f32_bf16 v{acc}, v{pw}, v{ONES}, v{acc}", False, [cvt], acc=acc)
+            plain += [cvt, d2]
+            continue
         a_lo = add(f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{x}", True, [word_exps[w][0]], acc=LSUM + n)
         a_hi = add(f"v_add_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{x + 1}", True, [word_exps[w][1]],
                    acc=LSUM_HI + n)
@@ -251,7 +262,7 @@ class Emitter:
         self.count += 1
 
 
-def step(e: Emitter, jj: int, tail: bool, first: bool = False):
+def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = False):
     """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).  A tail step clamps its
     DMA to the chunk's last 32-key window and masks the keys of the next tile that are not
     real, so steps past the chunk's end (and the partial last tile) run the same code.
@@ -315,6 +326,11 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False):
     def valu_slot():
         nonlocal slot
         for text, reads in plan[slot]:
+            if fp32a and text.startswith("v_exp_f32"):
+                # fp32a: the exponent is alpha S - (m + c_i), one FMA right before the exp
+                r = int(text.split()[1].rstrip(",")[1:])
+                n = (r - s_first(cur, 0)) // 16
+                e.emit(f"v_fma_f32 v{r}, v{r}, v{ALPHA}, v{NSHIFT + n}", reads_sbuf=cur)
             e.emit(text, reads_sbuf=cur if reads else None)
         slot += 1
 
@@ -354,7 +370,8 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False):
             key = 8 * (r >> 2) + (r & 3)                          # row of register r, lane half 0
             e.emit(f"v_cmp_lt_i32_e32 vcc, {key}, v{MASK_X}")
             for n in range(2):
-                e.emit(f"v_cndmask_b32_e32 v{SHIFT_BASE + 16 * n + r}, v{NSHIFT + n}, v{NEG_INF}, vcc")
+                init = "0" if fp32a else f"v{NSHIFT + n}"
+                e.emit(f"v_cndmask_b32_e32 v{SHIFT_BASE + 16 * n + r}, {init}, v{NEG_INF}, vcc")
         e.emit("s_nop 1")
     # S(t+1) = K(t+1) Q^T - (m + c), with the V(t) transpose reads in the first half
     e.emit("s_waitcnt lgkmcnt(0)")
@@ -377,11 +394,13 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False):
     assert slot == 32 and ti == 16
 
 
-def generate() -> str:
+def generate_variant(fp32a: bool) -> str:
+    """One assembly function: the bf16(alpha q) loop, or (fp32a) the loop that applies alpha
+    in fp32 with an FMA per score."""
     e = Emitter()
     for n in range(2):
         for i in range(16):
-            e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, v{NSHIFT + n}")
+            e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, {'0' if fp32a else f'v{NSHIFT + n}'}")
     e.emit(f"v_mov_b32 v{NEG_INF}, 0xff800000")
     e.emit(f"v_mov_b32 v{LSUM_HI}, 0")
     e.emit(f"v_mov_b32 v{LSUM_HI + 1}, 0")
@@ -398,7 +417,7 @@ def generate() -> str:
             src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
             e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(0, kk)}, {q_reg(n, kk)}, {src_c}",
                    writes_sbuf=0)
-    step(e, 0, tail=False, first=True)
+    step(e, 0, tail=False, first=True, fp32a=fp32a)
     e.emit(f"s_cmp_eq_u32 s{S_CNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
     # fast groups: every tile they prefetch and every S tile they compute is a full one
@@ -406,7 +425,7 @@ def generate() -> str:
     # the loop's back edge: the previous group's last S MFMAs may be a few instructions away
     e.s_written = {0: e.count - 1, 1: e.count - 1}
     for jj in range(STAGES):
-        step(e, jj, tail=False)
+        step(e, jj, tail=False, fp32a=fp32a)
     e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
     e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_group_%=")
@@ -414,7 +433,7 @@ def generate() -> str:
     e.lines.append("L_fixedm_tail_%=:")
     e.s_written = {0: e.count - 1, 1: e.count - 1}
     for jj in range(STAGES):
-        step(e, jj, tail=True)
+        step(e, jj, tail=True, fp32a=fp32a)
     e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
     e.emit(f"s_cmp_lg_u32 s{S_TCNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
@@ -441,6 +460,10 @@ def generate() -> str:
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
     ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
     ins += [f'"{{v{KB4}}}"(kb4)']
+    if fp32a:
+        ins += [f'"{{v{ALPHA}}}"(alpha)']
+    if ROWSUM == "dot2":
+        ins += [f'"{{v{ONES}}}"(0x3f803f80u)']
     ins += [f'"{{s[{S_KT6}:{S_KT6 + 1}]}}"(kt6)', f'"{{s[{S_VT6}:{S_VT6 + 1}]}}"(vt6)', f'"{{s{S_LO1}}}"(lo1)']
     ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
             f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s[{S_KLAST}:{S_KLAST + 1}]}}"(k_last)',
@@ -456,7 +479,12 @@ def generate() -> str:
     def join(items):
         return ",\n        ".join(items)
 
-    return f"""// Generated by gen_fixed_loop.py; do not edit by hand.
+    name = "fixed_loop_fp32a_asm" if fp32a else "fixed_loop_asm"
+    what = ("the query fragments are bf16(q) and each exponent is alpha S - (m + c_i) (one FMA "
+            "before its exp; the S chain starts from 0)" if fp32a else
+            "the query fragments are bf16(alpha q) and the S chain starts from -(m + c_i), so S is "
+            "the exponent")
+    return f"""// {what}.
 // The fixed-m pass over a chunk of >= 2 tiles: the priming step (S(0), then step t = 0: P(0),
 // S(1), V(0)'s fragments, the DMA of tile 6), `groups` fast groups, then `tail_groups` (>= 1)
 // tail groups of 8 pipelined 32-key steps, tiles t0 .. t0 + 8 (groups + tail_groups) - 1 with
@@ -466,12 +494,12 @@ def generate() -> str:
 // tile whose S the first tail step computes).  The steps past the chunk's last tile see only
 // masked keys (p = 0), so the last of them completes the PV product of the last tile.  On
 // exit every LDS read has completed.
-__device__ __attribute__((always_inline)) inline void fixed_loop_asm(
+__device__ __attribute__((always_inline)) inline void {name}(
     f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8],
     float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
     const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt6, uint64_t vt6, uint32_t lo1, uint64_t kt, uint64_t vt,
     uint64_t ktile, uint64_t vtile, uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full,
-    uint32_t lo_part, uint32_t groups, uint32_t tail_groups, uint32_t next_tile) {{
+    uint32_t lo_part, uint32_t groups, uint32_t tail_groups, uint32_t next_tile{", float alpha" if fp32a else ""}) {{
   asm volatile(
 {body}
       : {join(outs)}
@@ -479,6 +507,11 @@ __device__ __attribute__((always_inline)) inline void fixed_loop_asm(
       : {clob_text});
 }}
 """
+
+
+def generate() -> str:
+    return ("// Generated by gen_fixed_loop.py; do not edit by hand.\n\n" + generate_variant(False) + "\n"
+            + generate_variant(True))
 
 
 def main(out_path=None):

@@ -28,9 +28,11 @@
  * Conventions shared by every entry point:
  *   - Tensors are described by fixedm_tensor: a device pointer plus element strides for
  *     the batch, sequence and head axes; the head_dim axis is contiguous (stride 1).
- *     Layout is token-major [B, S, H, D] as in the [CM] Interface table, but any strides
- *     are accepted.  ptr must be 16-byte aligned and every stride a multiple of 8
- *     elements (bf16) or 4 elements (fp32).
+ *     Layout is token-major [B, S, H, D] as in the [CM] Interface table, but any
+ *     non-negative strides are accepted, within these limits: ptr must be 16-byte aligned,
+ *     every stride a multiple of 8 elements (bf16) or 4 elements (fp32), and a bf16
+ *     tensor's sequence stride at most 2^26 elements (FIXEDM_ERR_UNSUPPORTED_SHAPE
+ *     otherwise).
  *   - Every device pointer and the stream belong to the caller.  The library never
  *     allocates, frees or synchronises, and keeps no pointer after a call returns.  The
  *     scratch buffers it writes (bounds buffer, workspace) come with their byte sizes,

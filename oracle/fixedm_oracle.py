@@ -25,8 +25,9 @@ Readings taken where the pages leave a step open (listed again in the design doc):
   * Vmax = 256, so ceil(log2 Vmax) = 8 ([FM] review thread on the V check);
   * the gate test is inclusive: U <= gate;
   * q-blocks are consecutive runs of ``q_block`` real query rows; the last one is short;
-  * sums over d run in index order; sums over keys run in chunk order, then position;
-  * k_mean is fp32(sum_j k_j / N) with the sum and the division in fp64;
+  * sums over d run in index order (fp64);
+  * k_mean is fp32(fl64(sum_j k_j) / N): the exact sum of the keys rounded once to fp64
+    (so no summation order enters), the division in fp64, one rounding to fp32;
   * non-finite U: ineligible and m = INT32_MAX;
   * per-row shifts (the per-query-row bound of [CM]): m_i = ceil(U_i) - C(N) with
     U_i = alpha * sqrt(||q_i||^2 * K2); eligibility stays per q-block (every row of the
@@ -46,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "LOG2E", "VMAX", "INT32_MAX", "ceil_log2", "constants", "default_scale", "alpha_of",
-    "Bounds", "k_mean_of", "bounds", "attention", "attention_rows", "attention_bruteforce",
+    "Bounds", "exact_sum_f64", "k_mean_of", "bounds", "attention", "attention_rows", "attention_bruteforce",
     "fixed_m_emulate", "online_softmax_emulate", "method_forward", "max_shifted_exponent",
     "raw_key_unsound_case", "window_lower_edge", "softmax_mass",
 ]
@@ -113,20 +114,69 @@ class Bounds:
     m_row: np.ndarray | None = None    # [B, H, Sq] int64: ceil(u_row) - C
 
 
+_EXP_LO = -172          # every fp32 (hence bf16) value is an integer multiple of 2^-149; with
+                        # frexp's 24-bit integer mantissas the lowest weight is 2^(-148-24)
+_N_BINS = 104 + 24 - _EXP_LO + 1     # frexp exponents of fp32 values lie in [-148, 128]
+
+
+def exact_sum_f64(k_chunks) -> np.ndarray:
+    """sum_j k_j over the real keys of every chunk, as the fp64 number nearest the EXACT sum
+    (round to nearest, ties to even), for bf16 / fp32 keys; [B, H, D].
+
+    Each key element is an integer mantissa times a power of two (frexp: x = m 2^e,
+    M = m 2^24 an integer below 2^24 in magnitude).  The integer mantissas are added per
+    (element, exponent) in fp64, which is exact (fewer than 2^29 keys, so every such sum
+    stays below 2^53); the bins are then combined as Python integers, exactly, and the
+    integer is rounded once to fp64 (int to float conversion rounds to nearest, ties to
+    even).  A NaN, or both infinities, give NaN; otherwise an infinity gives itself.
+    Order of the keys plays no part: the sum is exact before its one rounding."""
+    chunks = [np.asarray(c, dtype=np.float64) for c in k_chunks]
+    B, _, H, D = chunks[0].shape
+    E = B * H * D
+    assert sum(c.shape[1] for c in chunks) < 2**29, "bin sums would leave the exact fp64 range"
+    bins = np.zeros(E * _N_BINS, dtype=np.float64)
+    any_nan = np.zeros(E, bool)
+    pos_inf = np.zeros(E, bool)
+    neg_inf = np.zeros(E, bool)
+    elem = np.arange(E, dtype=np.int64)
+    for c in chunks:
+        for j in range(c.shape[1]):
+            x = c[:, j].reshape(E)
+            any_nan |= np.isnan(x)
+            pos_inf |= x == np.inf
+            neg_inf |= x == -np.inf
+            fin = np.isfinite(x) & (x != 0.0)
+            m, e = np.frexp(np.where(fin, x, 0.0))
+            M = np.ldexp(m, 24)                      # integer-valued, |M| < 2^24
+            assert np.array_equal(M, np.round(M)), "keys must be fp32-representable"
+            idx = elem * _N_BINS + (e.astype(np.int64) - 24 - _EXP_LO)
+            np.add.at(bins, idx[fin], M[fin])
+    bins = bins.reshape(E, _N_BINS)
+    out = np.empty(E, dtype=np.float64)
+    for i in range(E):
+        if any_nan[i] or (pos_inf[i] and neg_inf[i]):
+            out[i] = np.nan
+        elif pos_inf[i] or neg_inf[i]:
+            out[i] = np.inf if pos_inf[i] else -np.inf
+        else:
+            total = 0
+            for t in np.nonzero(bins[i])[0]:
+                total += int(bins[i, t]) << int(t)   # exact: weight 2^(t + _EXP_LO)
+            out[i] = math.ldexp(float(total), _EXP_LO) if total else 0.0
+    return out.reshape(B, H, D)
+
+
 def k_mean_of(k_chunks) -> np.ndarray:
     """Global virtual K-centring mean over the real keys of every chunk ([UR] Summary:
     the key mean is taken on real, unpadded tokens, the same for every ring step).
 
-    fp64 running sum in key order (chunk by chunk, position by position), one fp64
-    division by N, one round-to-nearest-even to fp32."""
+    The exact sum rounded once to fp64 (exact_sum_f64), one fp64 division by N, one
+    round-to-nearest-even to fp32.  The pages do not fix a summation order; taking the sum
+    exactly makes the mean independent of the order of chunks, keys and any partial sums
+    (a running fp64 sum of fp32 keys over tens of thousands of keys is not exact)."""
     chunks = [np.asarray(c, dtype=np.float64) for c in k_chunks]
-    B, _, H, D = chunks[0].shape
     n = sum(c.shape[1] for c in chunks)
-    acc = np.zeros((B, H, D), dtype=np.float64)
-    for c in chunks:
-        for j in range(c.shape[1]):
-            acc += c[:, j]
-    return (acc / n).astype(np.float32)
+    return (exact_sum_f64(chunks) / n).astype(np.float32)
 
 
 def _rowsum_sq_in_order(x: np.ndarray) -> np.ndarray:

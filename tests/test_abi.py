@@ -124,6 +124,15 @@ def test_bounds_argument_errors_before_launch(L):
     assert _call_bounds(L, p, q=T(0, 0, 5120, 128)) == -1                   # null q
     assert _call_bounds(L, p, q=T(0x20008, 0, 5120, 128)) == -3             # q not 16-aligned
     assert _call_bounds(L, p, q=T(0x20000, 0, 5121, 128)) == -3             # stride not 8-multiple
+    # bf16 sequence strides up to 2^26 elements pass; beyond, the attention kernel's 32-bit
+    # lane offsets (31 rows x stride x 2 bytes) could wrap, so the ABI rejects them
+    assert _call_bounds(L, p, q=T(0x20000, 0, 2**26 + 8, 128)) == -3
+    kbig = (T * 1)(T(0x40000, 0, 2**26 + 8, 128))
+    assert _call_bounds(L, p, kc=kbig) == -3 and _call_bounds(L, p, vc=kbig) == -3
+    # fp32 has no such limit: the same stride passes the tensor checks and the call fails
+    # only later, on the chunk lengths that do not sum to sk_total
+    assert _call_bounds(L, _p(dtype="fp32", head_dim=64, sk_total=1000, sq=100),
+                        q=T(0x20000, 0, 2**26 + 8, 64), lens=(ctypes.c_int64 * 1)(999)) == -1
     assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(999)) == -1         # sum != sk_total
     assert _call_bounds(L, p, lens=(ctypes.c_int64 * 1)(-1)) == -1
     big = 2**62                                                            # four lengths summing to
@@ -192,3 +201,4 @@ def test_binding_checks_sizes_and_shapes():
         F.finalize(d, run, ws, out, lse=torch.empty((1, 40, 100), dtype=torch.float64))
     with pytest.raises(ValueError, match="workspace"):
         F.attn_fwd_final(d, run, q, k, k, torch.empty(8, dtype=torch.uint8), out)
+

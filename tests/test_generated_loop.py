@@ -81,7 +81,7 @@ def test_mfma_results_are_waited_for(gen):
             for b, regs in s_regs.items():
                 if lo in regs:
                     written[b] = count
-        elif ln.startswith(("v_exp", "v_cvt_pk", "v_add_f32")):
+        elif ln.startswith(("v_exp", "v_cvt_pk", "v_add_f32", "v_fma_f32")):
             for r in (int(x) for x in re.findall(r"v(\d+)", ln)[1:]):
                 for b, regs in s_regs.items():
                     if r in regs and b in written:

@@ -54,6 +54,8 @@ def test_config1_tiny_fp32(F, q_block):
     say(f"config 1 q_block={q_block}")
     inp = WL.make_inputs(1)
     out, lse, desc, buf, _ = _run(F, inp, q_block=q_block)
+    # softmax_scale 0 resolves to fp32(1/sqrt(d)), the [CM] Interface table default
+    assert desc.p.softmax_scale == O.default_scale(64) == inp.wl.scale
     ob = _oracle_bounds(inp, q_block)
     check_bounds(gpu_bounds_dict(desc, buf), ob)
     ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
@@ -80,9 +82,22 @@ def test_config2_wan_block_bf16(F):
     assert np.array_equal(bits, bf16_rne_bits(got))
 
 
-def _sample_rows(sq, q_block):
+def _sample_rows(sq, q_block, seed=7):
+    """Query rows checked at the full sizes: wave 0 of the first 256-row tile, the last 64
+    rows (the ragged last q-block and tile), one seeded row of every 256-row tile, and one
+    seeded row of each of the four 64-row waves in three middle tiles (every tile runs the
+    long-chunk loop schedule on its own workgroup, XCD-remapped)."""
     last_lo = ((sq - 1) // q_block) * q_block
     rows = list(range(0, 64)) + list(range(max(sq - 64, last_lo), sq))
+    rng = np.random.default_rng(seed)
+    n_tiles = -(-sq // 256)
+    for t in range(n_tiles):
+        rows.append(t * 256 + int(rng.integers(0, min(256, sq - t * 256))))
+    for t in sorted({n_tiles // 4, n_tiles // 2, (3 * n_tiles) // 4}):
+        for w in range(4):
+            lo = t * 256 + 64 * w
+            if lo < sq:
+                rows.append(lo + int(rng.integers(0, min(64, sq - lo))))
     return np.array(sorted(set(rows)))
 
 
@@ -151,10 +166,14 @@ def test_config5_adversarial_fp32(F):
 # ------------------------------------------------------------------ edge cases --------
 def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_scale=1.0,
              k_offset=0.0, v_poke=None, loud_rows=None, shift="block", lse_worst_case=False,
-             few_keys=False, **fwd):
+             few_keys=False, scale=None, **fwd):
+    """One seeded edge case through the C ABI against the oracle.  scale: an explicit
+    softmax scale handed to the ABI (None: the ABI's default, 0, which resolves to the
+    oracle's default_scale(D))."""
     import torch
     inp = WL.generic_inputs(seed, dtype, B, H, D, Sq, chunks, q_block=q_block, center=center,
                             q_scale=q_scale, k_offset=k_offset)
+    oscale = O.default_scale(D) if scale is None else float(np.float32(scale))
     if loud_rows is not None:                      # (head, lo, hi, factor): a loud q-block
         h, lo, hi, fac = loud_rows
         qf = inp.q.copy()
@@ -171,17 +190,20 @@ def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_s
         inp.k_mean = None
     q, ks, vs, km = device_inputs(inp)
     out, lse, desc, buf = F.forward(q, ks, vs, q_block=q_block, center=center, k_mean=km,
-                                    out_dtype=torch.float32, want_lse=True, shift=shift, **fwd)
+                                    out_dtype=torch.float32, want_lse=True, shift=shift,
+                                    softmax_scale=0.0 if scale is None else scale, **fwd)
     torch.cuda.synchronize()
-    ob = O.bounds(inp.q, inp.k, inp.v, scale=inp.wl.scale, q_block=q_block, center=center,
+    assert desc.p.softmax_scale == oscale, (desc.p.softmax_scale, oscale)
+    assert desc.alpha == np.float32(O.alpha_of(oscale))
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=oscale, q_block=q_block, center=center,
                   k_mean=kmean, dtype=dtype, shift=shift)
     check_bounds(gpu_bounds_dict(desc, buf), ob)
-    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), oscale)
     got = out.cpu().numpy()
     if few_keys and dtype == "bf16":
         # rows over a handful of keys: the bf16 roundings do not average out, so each element
         # is held to the worst case of the bf16 arithmetic instead of the many-key tolerance
-        bound = out_bound_bf16(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), inp.wl.scale, ref)
+        bound = out_bound_bf16(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), oscale, ref)
         assert np.isfinite(got).all()
         assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
     elif v_poke is None:
@@ -196,7 +218,7 @@ def _generic(F, seed, dtype, B, H, D, Sq, chunks, q_block=64, center="none", q_s
         col = np.abs(got[:, :, h0, d0] - ref[:, :, h0, d0]).max()
         assert col <= 1e-2 * abs(val) / 4.0, col
     if (lse_worst_case or few_keys) and dtype == "bf16":
-        bound = lse_bound_bf16(inp.q, np.concatenate(inp.k, 1), inp.wl.scale)
+        bound = lse_bound_bf16(inp.q, np.concatenate(inp.k, 1), oscale)
         assert (np.abs(lse.cpu().numpy() - lse_ref) <= bound).all()
     else:
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL[dtype]
@@ -687,3 +709,167 @@ def test_combined_options(F):
                      center="supplied", k_offset=3.0, loud_rows=(3, 192, 384, 14.0), shift="row",
                      **FUSED)
     assert ob.elig.any() and not ob.elig[:, 3, 1].any()
+
+
+# A query row whose bound is exactly the gate at N = 4096 (C = 107, W = 232 even, gate 116)
+# against keys k = -2^-10 q: in-order fp64 sums give Q2 * K2 = Q2^2 2^-20, so
+# U = alpha * Q2 * 2^-10 = 116.0 exactly with alpha = fp32(1/sqrt(128)) log2 e.  These bf16
+# components were found by a greedy search for that fp64 value (the test re-checks U).
+GATE_EDGE_Q = [964.0, 47.0, 2.609375, 0.26953125, 0.031005859375, 0.0024261474609375,
+               0.0002346038818359375, 1.52587890625e-05]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("shift", ["block", "row"])
+def test_bound_exactly_at_the_gate(F, dtype, shift):
+    """The lower edge of the fixed-m window ([FM] Summary inequality: exponents >= C - (U +
+    ceil U) >= -125).  With U = 116 = gate and m = ceil(U) - C = 9, every key of head 0 is
+    anti-aligned with the loud query row at full norm, so that row's exponents all sit at
+    C - 2 gate = -125 (on the bf16 path the rounding of alpha q moves a logit by at most 2^-8 of
+    sum_d |alpha q_d k_d| = 116, to no lower than about -125.45: still a normal fp32).  The
+    block's other rows are the loud row scaled by 2^-s (exponents from -125 up to -9) and a few
+    N(0,1) rows.  The block is eligible, every probability is normal, and the output matches
+    the oracle; the loud row, whose keys are identical, is the mean of V.  Head 1 holds
+    ordinary N(0,1) data."""
+    import torch
+    say(f"edge: U exactly at the gate ({dtype}, shift={shift})")
+    B, H, D, Sq, chunks = 1, 2, 128, 64, (2048, 2048)
+    inp = WL.generic_inputs(71, dtype, B, H, D, Sq, chunks, q_block=64)
+    qf, kf = inp.q.copy(), np.concatenate(inp.k, 1).copy()
+    loud = np.zeros(D, np.float32)
+    loud[:len(GATE_EDGE_Q)] = GATE_EDGE_Q
+    for i in range(48):
+        qf[0, i, 0] = loud * np.float32(2.0 ** -(i % 8))
+    kf[0, :, 0] = -(2.0 ** -10) * loud
+    store = (lambda x: WL.bf16_bits_from_f32(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    assert np.array_equal(WL.f32_from_bf16_bits(store(qf)) if dtype == "bf16" else qf, qf)
+    inp.q_store = store(qf)
+    inp.k_store = [np.ascontiguousarray(store(kf)[:, :2048]), np.ascontiguousarray(store(kf)[:, 2048:])]
+    q, ks, vs, _ = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, out_dtype=torch.float32, want_lse=True,
+                                    shift=shift, **FUSED)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=O.default_scale(D), q_block=64, dtype=dtype, shift=shift)
+    assert (ob.C, ob.W, ob.gate) == (107, 232, 116)
+    assert ob.u[0, 0, 0] == 116.0 and ob.m[0, 0, 0] == 9 and ob.elig.all()
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), O.default_scale(D))
+    got = out.cpu().numpy()
+    mean_v = np.concatenate(inp.v, 1)[0, :, 0].astype(np.float64).mean(axis=0)
+    say(f"  loud row vs mean of V: {np.abs(got[0, 0, 0] - mean_v).max():.3e}")
+    check_output(got, ref, dtype)
+    assert np.abs(got[0, 0, 0] - mean_v).max() <= (1e-3 if dtype == "bf16" else 5e-6)
+    # Head 0's keys are identical, so a row's l is the fp32 sum of 4,096 equal terms, whose
+    # rounding errors do not cancel: its relative error is bounded by (N - 1) 2^-24, and lse
+    # = ln l + const moves by as much.  (The bf16 tolerance covers it already.)
+    lse_tol = max(LSE_TOL[dtype], sum(chunks) * 2.0**-24 + 1e-5)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= lse_tol
+
+
+@pytest.mark.parametrize("dtype,D,scale", [("bf16", 128, 0.05), ("bf16", 128, 0.13), ("fp32", 64, 0.3)])
+def test_explicit_softmax_scale(F, dtype, D, scale):
+    """A softmax scale given by the caller (not the 1/sqrt(d) default): the descriptor holds
+    its fp32 value and alpha = fp32(scale log2 e); bounds bit-exact, output within tolerance,
+    on the fused and the per-chunk paths."""
+    say(f"edge: softmax scale {scale} ({dtype})")
+    _generic(F, 72, dtype, 1, 3, D, 300, (257, 190), q_block=64, scale=scale, **FUSED)
+    _generic(F, 73, dtype, 1, 3, D, 300, (257, 190), q_block=128, scale=scale, center="compute",
+             k_offset=2.0)
+
+
+@pytest.mark.parametrize("fwd", [FUSED, dict(chunks_per_call=1)], ids=["fused", "per_chunk"])
+def test_three_bodies_in_one_workgroup(F, fwd):
+    """q_block 64 puts four blocks in one 256-row workgroup; the query rows of each are scaled
+    so the waves take different bodies: U <= 32 (fixed-m assembly loop, logits from
+    bf16(alpha q)), 32 < U <= gate (eligible, fixed-m with alpha applied in fp32), U > gate
+    (online softmax), and U <= 32 again.  Loud eligible rows are where the bf16 rounding of
+    alpha q would matter (a base-2 logit moves by up to 2^-8 U), so they are held to the
+    flat bf16 tolerance like every other row.  Both heads, ragged Sq and chunk lengths."""
+    import torch
+    say(f"edge: three bodies in one workgroup ({'fused' if fwd is FUSED else 'per chunk'})")
+    inp = WL.generic_inputs(74, "bf16", 1, 2, 128, 300, (700, 333), q_block=64)
+    qf = inp.q.copy()
+    for lo, fac in ((64, 4.5), (128, 8.0), (256, 4.0)):
+        qf[0, lo:lo + 64] *= np.float32(fac)
+    inp.q_store = WL.bf16_bits_from_f32(qf)
+    q, ks, vs, _ = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, out_dtype=torch.float32, want_lse=True, **fwd)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=O.default_scale(128), q_block=64, dtype="bf16")
+    say(f"  U per block (head 0): {np.round(ob.u[0, 0], 2).tolist()}, gate {ob.gate}")
+    u0 = ob.u[0, 0]
+    assert u0[0] <= 32 and 32 < u0[1] <= ob.gate and u0[2] > ob.gate and u0[3] <= 32 < u0[4] <= ob.gate
+    assert ob.elig[0, 0].tolist() == [True, True, False, True, True]
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    ref, lse_ref = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), O.default_scale(128))
+    got = out.cpu().numpy()
+    check_output(got, ref, "bf16")
+    for lo, hi in ((64, 128), (256, 300)):
+        say(f"  loud eligible rows {lo}..{hi}: max|d| {np.abs(got[0, lo:hi] - ref[0, lo:hi]).max():.2e}")
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= LSE_TOL["bf16"]
+
+
+def _keys_wide(rng, shape, lo_exp, hi_exp, dtype):
+    m = rng.uniform(1.0, 2.0, size=shape)
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    x = (rng.choice([-1.0, 1.0], size=shape) * np.ldexp(m, e)).astype(np.float32)
+    return WL.bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype,D,lo,hi", [("fp32", 64, -20, 20), ("fp32", 128, -60, 60),
+                                           ("bf16", 128, -40, 40), ("fp32", 64, -149, -80)])
+def test_key_mean_is_the_rounded_exact_sum(F, dtype, D, lo, hi):
+    """COMPUTE centring on keys whose magnitudes span many binades (fp32 2^+-20 and 2^+-60,
+    bf16 2^+-40, fp32 denormals): running fp64 sums of such keys round, so the key mean is
+    defined as the exact sum rounded once to fp64, divided by N in fp64, rounded to fp32
+    (every bit independent of summation order).  The GPU's slab partial sums detect the
+    rounding and re-sum those elements exactly; k_mean, K2, U, m and the mask must equal the
+    oracle's bit for bit.  Ragged chunks, several heads, batch 2."""
+    import torch
+    say(f"key mean: {dtype} D={D} keys 2^{lo}..2^{hi}")
+    B, H, Sq, chunks = 2, 3, 70, (901, 77, 1500)
+    inp = WL.generic_inputs(81, dtype, B, H, D, Sq, chunks, q_block=64, center="compute")
+    rng = np.random.default_rng(82 + abs(lo))
+    inp.k_store = [np.ascontiguousarray(_keys_wide(rng, (B, n, H, D), lo, hi, dtype)) for n in chunks]
+    q, ks, vs, _ = device_inputs(inp)
+    p = F.make_problem(dtype, B, H, D, Sq, sum(chunks), 64, 0.0, "compute")
+    desc, buf = F.bounds(p, q, ks, vs)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=O.default_scale(D), q_block=64, center="compute", dtype=dtype)
+    # the case is meant to need the exact sum: a running fp64 sum differs from it somewhere
+    run = np.zeros((B, H, D))
+    for c in inp.k:
+        for j in range(c.shape[1]):
+            run += c[:, j].astype(np.float64)
+    assert not np.array_equal(run, O.exact_sum_f64(inp.k))
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+
+
+def test_key_mean_fp32_gaussian_many_keys(F):
+    """fp32 N(0,1) keys over 20,000 keys under COMPUTE centring (a running fp64 sum of these
+    rounds for some elements); bounds bit-exact and the output within tolerance."""
+    say("key mean: fp32 N(0,1), 20,000 keys")
+    _generic(F, 83, "fp32", 1, 4, 64, 130, (12000, 8000), q_block=64, center="compute", k_offset=1.5)
+
+
+def test_key_mean_nonfinite_keys(F):
+    """A NaN key element, and an element holding both infinities, make that element's key
+    mean NaN; one holding +inf only makes it +inf.  Those heads' K2, U are NaN and their
+    blocks ineligible with m = INT32_MAX; the other heads are untouched (bit-exact)."""
+    import torch
+    say("key mean: non-finite keys")
+    B, H, D, Sq, chunks = 1, 4, 64, 70, (300, 211)
+    inp = WL.generic_inputs(84, "fp32", B, H, D, Sq, chunks, q_block=64, center="compute")
+    k0, k1 = inp.k_store[0].copy(), inp.k_store[1].copy()
+    k0[0, 3, 0, 5] = np.nan
+    k0[0, 7, 1, 2], k1[0, 9, 1, 2] = np.inf, -np.inf
+    k1[0, 200, 2, 9] = np.inf
+    inp.k_store = [k0, k1]
+    q, ks, vs, _ = device_inputs(inp)
+    p = F.make_problem("fp32", B, H, D, Sq, sum(chunks), 64, 0.0, "compute")
+    desc, buf = F.bounds(p, q, ks, vs)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=O.default_scale(D), q_block=64, center="compute", dtype="fp32")
+    assert np.isnan(ob.k_mean[0, 0, 5]) and np.isnan(ob.k_mean[0, 1, 2]) and ob.k_mean[0, 2, 9] == np.inf
+    assert not ob.elig[0, :3].any() and ob.elig[0, 3].all()
+    check_bounds(gpu_bounds_dict(desc, buf), ob)

@@ -272,6 +272,47 @@ def test_attention_bruteforce_and_scipy():
     assert np.max(np.abs(lse - scipy.special.logsumexp(s, axis=-1))) < 1e-12
 
 
+def test_attention_rows_bruteforce():
+    """attention_rows (the checker of the sampled rows at full sizes) against the pure-Python
+    triple loop on the same rows: rows given out of order, repeated, across two batches and
+    three heads, and including the last row of a ragged last q-block (Sq = 11 with q-blocks of
+    4).  A mistake in the row indexing (wrong axis, sorting, dropping a repeat) fails here."""
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 11, 3, 4))
+    k = rng.standard_normal((2, 6, 3, 4))
+    v = rng.standard_normal((2, 6, 3, 4))
+    rows = np.array([10, 0, 7, 7, 3, 8])
+    o, lse = O.attention_rows(q, k, v, 0.6, rows)
+    assert o.shape == (2, len(rows), 3, 4) and lse.shape == (2, 3, len(rows))
+    ob = O.attention_bruteforce(q[:, rows], k, v, 0.6)
+    assert np.max(np.abs(o - ob)) < 1e-13
+    s = float(np.float32(0.6)) * np.einsum("bqhd,bkhd->bhqk", q[:, rows], k)
+    assert np.max(np.abs(lse - scipy.special.logsumexp(s, axis=-1))) < 1e-12
+    # closed form: a zero query row gives the mean of v wherever it sits in the list
+    qz = q.copy()
+    qz[:, 8] = 0.0
+    oz, lz = O.attention_rows(qz, k, v, 0.6, rows)
+    assert np.allclose(oz[:, 5], v.mean(axis=1), atol=1e-14)
+    assert np.allclose(lz[:, :, 5], math.log(6), atol=1e-14)
+
+
+def test_default_scale_closed_form():
+    """softmax_scale defaults to 1/sqrt(d) ([CM] Interface table), held as an fp32: exact
+    powers of two where d is a power of 4, and otherwise the fp32 nearest to 1/sqrt(d)."""
+    assert O.default_scale(64) == 0.125
+    assert O.default_scale(16) == 0.25 and O.default_scale(256) == 0.0625
+    for d in (128, 96, 80, 72):
+        s = O.default_scale(d)
+        exact = Fraction(1) / Fraction(math.isqrt(d * 10**40)) * 10**20   # 1/sqrt(d) to ~1e-20
+        f = np.float32(s)
+        assert float(f) == s
+        lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(1))
+        # the neighbours of s are both further from 1/sqrt(d) than s is
+        assert abs(Fraction(float(s)) - exact) < abs(Fraction(float(lo)) - exact)
+        assert abs(Fraction(float(s)) - exact) < abs(Fraction(float(hi)) - exact)
+    assert O.default_scale(128) == float(np.float32(2.0**-3.5))
+
+
 def test_attention_special_cases(golden_dir):
     rng = np.random.default_rng(4)
     k = rng.standard_normal((1, 9, 2, 4))
@@ -453,3 +494,74 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     rng = np.random.default_rng(3)
     qq, kk, vv = (rng.standard_normal((1, 5, 1, 4)) for _ in range(3))
     assert np.max(np.abs(O.attention(qq, kk, kk, 0.7)[0] - O.attention_bruteforce(qq, kk, vv, 0.7))) > 1e-3
+
+
+# ---------------------------------------------------------------- exact key sum --------
+def _fraction_sum(col):
+    """The exact sum of fp64 numbers as a Fraction, rounded once to fp64 (Fraction -> float
+    rounds to nearest, ties to even)."""
+    return float(sum((Fraction(float(x)) for x in col), Fraction(0)))
+
+
+def _wide_fp32(rng, shape, lo_exp, hi_exp):
+    """fp32 values with random signs, mantissas and exponents in [lo_exp, hi_exp]."""
+    m = rng.uniform(1.0, 2.0, size=shape)
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    s = rng.choice([-1.0, 1.0], size=shape)
+    return (s * np.ldexp(m, e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("lo_exp,hi_exp", [(-20, 20), (-60, 60), (-149, -120), (100, 127)])
+def test_exact_key_sum_against_fractions(lo_exp, hi_exp):
+    """exact_sum_f64 equals the exact rational sum rounded once to fp64, on fp32 keys whose
+    magnitudes span many binades (where a running fp64 sum loses bits), fp32 denormals, and
+    values near the top of the fp32 range; chunked unevenly."""
+    rng = np.random.default_rng(lo_exp + 1000)
+    k = _wide_fp32(rng, (2, 301, 2, 3), lo_exp, hi_exp)
+    k[0, 5, 0, 0] = 0.0
+    got = O.exact_sum_f64([k[:, :100], k[:, 100:101], k[:, 101:]])
+    for b in range(2):
+        for h in range(2):
+            for d in range(3):
+                assert got[b, h, d] == _fraction_sum(k[b, :, h, d].astype(np.float64)), (b, h, d)
+
+
+def test_exact_key_sum_cancellation_and_order():
+    """A sum a running fp64 sum gets wrong (2^60 + 1 - 2^60 = 1, not 0), the same keys in
+    every order and chunking giving the same bits, bf16 keys, and math.fsum agreeing on
+    ordinary data."""
+    k = np.zeros((1, 3, 1, 1), np.float32)
+    k[0, :, 0, 0] = [2.0**60, 1.0, -(2.0**60)]
+    assert O.exact_sum_f64([k])[0, 0, 0] == 1.0
+    naive = 0.0
+    for x in k[0, :, 0, 0].astype(np.float64):
+        naive += x
+    assert naive == 0.0                                      # the running sum drops the 1
+    rng = np.random.default_rng(8)
+    k = _wide_fp32(rng, (1, 500, 3, 4), -40, 40)
+    ref = O.exact_sum_f64([k])
+    perm = rng.permutation(500)
+    assert np.array_equal(O.exact_sum_f64([k[:, perm[:123]], k[:, perm[123:]]]), ref)
+    kb = WL.f32_from_bf16_bits(WL.bf16_bits_from_f32(_wide_fp32(rng, (1, 400, 2, 5), -30, 30)))
+    got = O.exact_sum_f64([kb])
+    for h in range(2):
+        for d in range(5):
+            assert got[0, h, d] == _fraction_sum(kb[0, :, h, d].astype(np.float64))
+    kn = rng.standard_normal((1, 5000, 2, 4)).astype(np.float32)
+    got = O.exact_sum_f64([kn])
+    for h in range(2):
+        for d in range(4):
+            assert got[0, h, d] == math.fsum(kn[0, :, h, d].astype(np.float64))
+
+
+def test_exact_key_sum_nonfinite():
+    """NaN anywhere, or both infinities, give NaN; one infinity gives itself (IEEE sums)."""
+    k = np.ones((1, 4, 1, 4), np.float32)
+    k[0, 1, 0, 0] = np.nan
+    k[0, 0, 0, 1], k[0, 2, 0, 1] = np.inf, -np.inf
+    k[0, 3, 0, 2] = np.inf
+    k[0, 3, 0, 3] = -np.inf
+    got = O.exact_sum_f64([k])[0, 0]
+    assert np.isnan(got[0]) and np.isnan(got[1]) and got[2] == np.inf and got[3] == -np.inf
+    km = O.k_mean_of([k])[0, 0]
+    assert np.isnan(km[0]) and km[2] == np.inf and km[3] == -np.inf
