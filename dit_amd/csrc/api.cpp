@@ -261,9 +261,10 @@ size_t fixedm_workspace_bytes(const fixedm_problem* p) {
 
 namespace {
 
-// fixedm_bounds: the checks, the descriptor and the launches.  bounds_dev holds the outputs
-// (need_bytes of it checked); the scratch of COMPUTE centring lies at scratch_base with the
-// given layout.
+// fixedm_bounds and fixedm_bounds_static: the checks, the descriptor and the launches.
+// bounds_dev holds the outputs (need_bytes of it checked); the scratch of COMPUTE centring
+// lies at scratch_base with the given layout, or (scratch_base null) in the static array,
+// whose address is looked up only once every host-checkable error has been ruled out.
 fixedm_status bounds_impl(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
                           const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
                           const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
@@ -281,6 +282,10 @@ fixedm_status bounds_impl(const fixedm_problem* p, fixedm_tensor q, const fixedm
   if (p->center == FIXEDM_CENTER_SUPPLIED) {
     if (k_mean_in == nullptr) return FIXEDM_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)k_mean_in & 3) != 0) return FIXEDM_ERR_INVALID_ARGUMENT;
+  }
+  if (scratch_base == nullptr && sc.total > 0) {
+    scratch_base = static_cast<char*>(static_scratch());
+    if (scratch_base == nullptr) return FIXEDM_ERR_HIP;
   }
 
   fixedm_bounds_t d;
@@ -349,6 +354,24 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q, const fixe
   bounds_layout(*p, &lay);
   return bounds_impl(p, q, k_chunks, v_chunks, chunk_len, n_chunks, k_mean_in, bounds_dev, bounds_dev_bytes,
                      lay.total, static_cast<char*>(bounds_dev) + lay.scratch, bounds_scratch(*p), out, stream);
+}
+
+fixedm_status fixedm_bounds_static(const fixedm_problem* p, fixedm_tensor q, const fixedm_tensor* k_chunks,
+                                   const fixedm_tensor* v_chunks, const int64_t* chunk_len, int32_t n_chunks,
+                                   const float* k_mean_in, void* bounds_dev, size_t bounds_dev_bytes,
+                                   fixedm_bounds_t* out, void* stream) {
+  const fixedm_status st = check_problem(p);
+  if (st != FIXEDM_OK) return st;
+  BoundsLayout lay;
+  bounds_layout(*p, &lay);
+  // as few key slabs as the static array needs: its size bounds the partial sums
+  const size_t el = (size_t)(p->batch * p->heads) * (size_t)p->head_dim;
+  const size_t flags = (el * 4 + 255) & ~(size_t)255;
+  if (kStaticScratchBytes < flags + el * 8) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  const BoundsScratch sc = bounds_scratch(*p, (int64_t)((kStaticScratchBytes - flags - 255) / (el * 8)));
+  if (sc.total > kStaticScratchBytes) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  return bounds_impl(p, q, k_chunks, v_chunks, chunk_len, n_chunks, k_mean_in, bounds_dev, bounds_dev_bytes,
+                     lay.scratch, nullptr, sc, out, stream);
 }
 
 fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run) {

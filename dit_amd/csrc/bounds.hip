@@ -22,6 +22,8 @@
 // U = alpha64 * sqrt(Q2 * K2) in exactly that order.
 #include <math.h>
 
+#include <atomic>
+
 #include "exact_sum.h"
 #include "fixedm_internal.h"
 
@@ -553,6 +555,25 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Scratch of fixedm_bounds_static (the key-mean partial sums and their flags): one array per
+// GPU, held for the life of the process.  In host code `scratch` names a host-side stand-in,
+// not the device array: host code uses only the address hipGetSymbolAddress returns on each
+// device.  Calls of fixedm_bounds_static that overlap on one GPU share it and race.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+void* static_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s) {
   const int64_t nqb_all = (int64_t)a.B * a.H * a.nqb;

@@ -68,6 +68,13 @@ inline BoundsScratch bounds_scratch(const fixedm_problem& p, int64_t max_slabs =
   return s;
 }
 
+// The no-allocation variant of fixedm_bounds keeps its scratch in one static device array
+// of this many bytes per GPU (defined in bounds.hip).
+constexpr size_t kStaticScratchBytes = (size_t)24 << 20;
+// Device address of that array on the current device (looked up once per device), or null
+// if the lookup fails.
+void* static_scratch();
+
 struct ChunkDesc {
   const void* k;
   const void* v;

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.fixedm_bounds.argtypes = [P(Problem), Tensor, P(Tensor), P(Tensor), P(ctypes.c_int64),
                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 P(BoundsDesc), ctypes.c_void_p]
+    L.fixedm_bounds_static.restype = ctypes.c_int
+    L.fixedm_bounds_static.argtypes = L.fixedm_bounds.argtypes
     L.fixedm_run_init.restype = ctypes.c_int
     L.fixedm_run_init.argtypes = [P(BoundsDesc), P(RunState)]
     L.fixedm_attn_fwd.restype = ctypes.c_int
@@ -237,6 +239,25 @@ def bounds(p: Problem, q, k_chunks, v_chunks, k_mean=None, buf=None, stream=None
     st = lib().fixedm_bounds(ctypes.byref(p), tensor_desc(q), ks, vs, lens, n, _ptr(k_mean),
                              _ptr(buf), _nbytes(buf), ctypes.byref(desc), _stream(stream))
     _check(st, "fixedm_bounds")
+    return desc, buf
+
+
+def bounds_static(p: Problem, q, k_chunks, v_chunks, k_mean=None, buf=None, stream=None):
+    """fixedm_bounds_static: as bounds(), with the scratch in the library's static device
+    array; buf needs only the output arrays (bounds_layout(p).scratch bytes)."""
+    import torch
+    nbytes = bounds_layout(p).scratch
+    if buf is None:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _need_bytes(buf, nbytes, "bounds buffer")
+    _check_qkv(p, q, k_chunks, v_chunks)
+    if p.center == CENTER["supplied"]:
+        _need_shape(k_mean, (p.batch, p.heads, p.head_dim), "k_mean")
+    ks, vs, lens, n = _chunk_arrays(k_chunks, v_chunks)
+    desc = BoundsDesc()
+    st = lib().fixedm_bounds_static(ctypes.byref(p), tensor_desc(q), ks, vs, lens, n, _ptr(k_mean),
+                                    _ptr(buf), _nbytes(buf), ctypes.byref(desc), _stream(stream))
+    _check(st, "fixedm_bounds_static")
     return desc, buf
 
 

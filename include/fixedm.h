@@ -184,6 +184,25 @@ fixedm_status fixedm_bounds(const fixedm_problem* p, fixedm_tensor q,
                             const float* k_mean_in, void* bounds_dev,
                             size_t bounds_dev_bytes, fixedm_bounds_t* out, void* stream);
 
+/* fixedm_bounds for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation and results, with
+ * the scratch fixedm_bounds keeps at the end of its buffer (the key-mean partial sums of
+ * COMPUTE centring) held instead in one static device array of 24 MiB per GPU, allocated
+ * when the library's code is loaded on that GPU and kept until the process ends.  bounds_dev
+ * needs only the output arrays: bounds_dev_bytes >= the `scratch` offset of
+ * fixedm_bounds_layout.  Problems whose partial sums cannot fit that array even with a
+ * single key slab (batch x heads x head_dim x 12 bytes above 24 MiB) are rejected with
+ * FIXEDM_ERR_UNSUPPORTED_SHAPE.  Allocates nothing and calls no allocating routine; a failed
+ * lookup of the array's address returns FIXEDM_ERR_HIP.  Every call on one GPU uses the same
+ * array: calls that overlap on one GPU (other streams, other host threads) race; calls on
+ * one stream, or separated by synchronisation, are safe.  The descriptor it fills is used
+ * exactly like fixedm_bounds's. */
+fixedm_status fixedm_bounds_static(const fixedm_problem* p, fixedm_tensor q,
+                                   const fixedm_tensor* k_chunks, const fixedm_tensor* v_chunks,
+                                   const int64_t* chunk_len, int32_t n_chunks,
+                                   const float* k_mean_in, void* bounds_dev,
+                                   size_t bounds_dev_bytes, fixedm_bounds_t* out, void* stream);
+
 /* Starts a new ring pass over the descriptor's K/V: zero keys visited. */
 fixedm_status fixedm_run_init(const fixedm_bounds_t* bounds, fixedm_run_t* run);
 

@@ -202,3 +202,25 @@ def test_binding_checks_sizes_and_shapes():
     with pytest.raises(ValueError, match="workspace"):
         F.attn_fwd_final(d, run, q, k, k, torch.empty(8, dtype=torch.uint8), out)
 
+
+def test_static_bounds_argument_errors_before_launch(L):
+    """fixedm_bounds_static checks like fixedm_bounds, wants only the output arrays of the
+    buffer, and rejects problems whose key-mean partial sums cannot fit its static array."""
+    p = _p(sk_total=1000, sq=100)
+    T = F.Tensor
+    kc = (T * 1)(T(0x40000, 0, 40 * 128, 128))
+    lens = (ctypes.c_int64 * 1)(1000)
+    lay = F.bounds_layout(p)
+    d = F.BoundsDesc()
+
+    def call(p_, dev=0x10000, nbytes=lay.scratch, out=True, q=T(0x20000, 0, 40 * 128, 128), ln=lens):
+        return L.fixedm_bounds_static(ctypes.byref(p_), q, kc, kc, ln, 1, None, dev, nbytes,
+                                      ctypes.byref(d) if out else None, None)
+    assert call(p, out=False) == -1 and call(p, dev=0) == -1 and call(p, dev=0x10010) == -1
+    assert call(p, nbytes=lay.scratch - 1) == -1
+    assert call(p, q=T(0x20008, 0, 5120, 128)) == -3
+    assert call(p, ln=(ctypes.c_int64 * 1)(999)) == -1
+    # 65,535 (batch, head) pairs x 128 dims: one slab of fp64 partial sums is 64 MiB
+    big = _p(batch=3, heads=21845, sk_total=1000, sq=100)
+    assert call(big, nbytes=F.bounds_layout(big).scratch) == -3
+    assert call(_p(dtype=3)) == -2
