@@ -189,6 +189,8 @@ bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out) {
     out->l_x = off; off = align256(off + xt * kQTile * 4);
     out->r_x = off; off = align256(off + xt * kQTile * 4);
   }
+  out->queue = off;
+  if (p.dtype == FIXEDM_BF16) off = align256(off + 8 * sizeof(unsigned long long));
   out->total = off;
   return true;
 }
@@ -452,6 +454,7 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.acc_x = reinterpret_cast<float*>(wbase + wl.acc_x);
   a.l_x = reinterpret_cast<float*>(wbase + wl.l_x);
   a.r_x = reinterpret_cast<float*>(wbase + wl.r_x);
+  a.queue = reinterpret_cast<unsigned long long*>(wbase + wl.queue);
   const SplitPlan sp = plan_of(p, wl);
   a.n_whole = sp.n_whole;
   a.parts = sp.parts;

@@ -38,8 +38,9 @@
 //   * Ragged KV tails: rows past a chunk's end are clamped to its last row on load and
 //     their probabilities forced to zero; no padding copies.  Query rows past Sq are
 //     clamped on load and land in padded workspace rows that finalize never reads.
-//   * Workgroup ids are remapped so each XCD works through consecutive tiles of the same
-//     head and shares the K/V stream in its L2.
+//   * Persistent workgroups (one per compute unit) take query tiles from per-XCD queues:
+//     each XCD works through consecutive tiles of the same heads (sharing the K/V stream in
+//     its L2) and, once its queue is empty, takes work from the back of the others.
 #include <math.h>
 
 #include "fixedm_internal.h"
@@ -85,14 +86,6 @@ __device__ inline void barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ inline int remap_tile(int bid, int nb) {
-  // The dispatcher hands workgroup i to XCD i % 8.  Give XCD x the contiguous tile range
-  // [x*T8, (x+1)*T8) so one head's query tiles share that XCD's L2.
-  const int t8 = nb / 8;
-  if (bid < 8 * t8) return (bid % 8) * t8 + bid / 8;
-  return bid;
 }
 
 // One 16-byte-per-lane global->LDS load; lane L's 16 bytes land at LDS byte lds + 16 L.
@@ -407,9 +400,11 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
 // other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
 // loading tile t+kAhead into stage t-2.
 __device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ring& g, int t, int stage) {
-  wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
+  if (kPairSteps && (t & 1)) return;   // one barrier per two steps: tiles t, t+1 waited at t-1
+  wait_vmcnt<(kAhead - 2 - kPairSteps) * kLoadsPerTile>();
   barrier();
   issue_tile(smem, g, t + kAhead, (stage + kAhead) % kStages);
+  if (kPairSteps) issue_tile(smem, g, t + kAhead + 1, (stage + kAhead + 1) % kStages);
 }
 
 // Steps of the fixed-m assembly loop for a chunk of n_tiles >= 2 tiles: fast groups while every
@@ -422,7 +417,9 @@ struct FixedSchedule {
 __device__ inline FixedSchedule fixed_schedule(int64_t len) {
   const int n_tiles = (int)((len + kKT - 1) / kKT), n_full = (int)(len / kKT);
   if (n_tiles < 2) return {0, 0, 0};
-  const int fast = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
+  // a fast group's last step loads tile t + kAhead (+ 1 with paired steps), which must be whole
+  const int last = kAhead + kPairSteps;
+  const int fast = n_full >= 1 + kStages + last ? (n_full - 1 - last) / kStages : 0;
   const int tail = (n_tiles - kStages * fast + kStages - 1) / kStages;
   return {fast, tail, kStages * (fast + tail)};
 }
@@ -578,19 +575,10 @@ __device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  // Whole tiles first (XCD-remapped), then the parts of the split tail tiles: part p of a
-  // tail tile takes keys [lo_p, lo_{p+1}) of the launch's chunk sequence,
-  // lo_p = 32 * floor(call_len p / (32 parts)); a whole tile takes all of them.
-  int tile, part = 0;
-  if ((int)blockIdx.x < a.n_whole) {
-    tile = remap_tile(blockIdx.x, a.n_whole);
-  } else {
-    const int u = blockIdx.x - a.n_whole;
-    tile = a.n_whole + u / a.parts;
-    part = u % a.parts;
-  }
+// One work item: a whole query tile (all keys of the launch's chunk sequence), or part p of a
+// split tail tile: keys [lo_p, lo_{p+1}) with lo_p = 32 * floor(call_len p / (32 parts)).
+__device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, uint8_t* smem, int tile,
+                                                            int part) {
   const bool split = a.parts > 1 && tile >= a.n_whole;
   int64_t klo = 0, khi = a.call_len;
   if (split) {
@@ -800,12 +788,81 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   }
 }
 
+// Work items: the n_whole whole tiles, then the split parts (tile n_whole + u / parts, part
+// u % parts).  They are dealt to kQueues queues, one per XCD: queue x holds whole tiles
+// [x W / 8, (x + 1) W / 8) followed by parts [x P / 8, (x + 1) P / 8), so each XCD works
+// through consecutive tiles of the same heads and shares their K/V stream in its L2.  A
+// queue is one 64-bit counter: the low half counts items taken from its front (by its own
+// XCD), the high half items taken from its back (by other XCDs, once theirs are empty).
+// Both halves only grow and every take returns the counter before its own increment, so the
+// k-th take of a queue sees k - 1 items gone and exactly `size` takes succeed: each item is
+// processed once.  The XCDs run at different clocks under load, so stealing keeps them all
+// busy to the end.
+constexpr int kQueues = 8;
+
+struct QueueRange {
+  int64_t w0, nw, p0, size;
+};
+__device__ inline QueueRange queue_range(const AttnArgs& a, int q) {
+  const int64_t W = a.n_whole, P = (int64_t)(a.B * a.H * a.n_qtiles - a.n_whole) * a.parts;
+  QueueRange r;
+  r.w0 = W * q / kQueues;
+  r.nw = W * (q + 1) / kQueues - r.w0;
+  r.p0 = P * q / kQueues;
+  r.size = r.nw + P * (q + 1) / kQueues - r.p0;
+  return r;
+}
+
+// Takes the next item for a workgroup on XCD `xcc` (one thread calls it): the front of its own
+// queue, else the back of the others in turn.  `dead` marks queues seen empty.  -1: none left.
+__device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) {
+  for (int k = 0; k < kQueues; ++k) {
+    const int q = (xcc + k) % kQueues;
+    if ((dead >> q) & 1u) continue;
+    const QueueRange r = queue_range(a, q);
+    const unsigned long long old = atomicAdd(a.queue + q, k == 0 ? 1ull : (1ull << 32));
+    const int64_t f = (int64_t)(old & 0xffffffffull), bk = (int64_t)(old >> 32);
+    if (f + bk >= r.size) {
+      dead |= 1u << q;
+      continue;
+    }
+    const int64_t j = k == 0 ? f : r.size - 1 - bk;
+    return j < r.nw ? r.w0 + j : a.n_whole + r.p0 + (j - r.nw);
+  }
+  return -1;
+}
+
+// Persistent: one workgroup per compute unit, each taking items until every queue is empty.
+__global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ int64_t next_item;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) % kQueues);   // HW_REG_XCC_ID
+  uint32_t dead = 0;
+  for (;;) {
+    if (threadIdx.x == 0) next_item = take_item(a, xcc, dead);
+    __syncthreads();
+    const int64_t item = next_item;
+    __syncthreads();   // read by every thread before thread 0 takes the next one
+    if (item < 0) break;
+    const int64_t u = item < a.n_whole ? 0 : item - a.n_whole;
+    const int tile = item < a.n_whole ? (int)item : (int)(a.n_whole + u / a.parts);
+    process_item(a, smem, tile, item < a.n_whole ? 0 : (int)(u % a.parts));
+  }
+}
+
+__global__ void queue_reset_kernel(unsigned long long* q) {
+  if (threadIdx.x < kQueues) q[threadIdx.x] = 0ull;
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  const int tiles = a.B * a.H * a.n_qtiles;
-  const int nb = a.n_whole + (tiles - a.n_whole) * a.parts;
-  attn_bf16_d128_kernel<<<nb, 256, 0, s>>>(a);
+  const int64_t tiles = (int64_t)a.B * a.H * a.n_qtiles;
+  const int64_t items = a.n_whole + (tiles - a.n_whole) * a.parts;
+  const int cus = device_cus();
+  const int64_t grid = items < cus || cus <= 0 ? items : cus;
+  queue_reset_kernel<<<1, 64, 0, s>>>(a.queue);
+  attn_bf16_d128_kernel<<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -93,10 +93,10 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out);
 
 // Workspace: acc fp32, then row sum l and row shift r, per padded query row; for the bf16
 // kernel also the same three for parts 1.. of split tail tiles ([kMaxParts - 1] per tile,
-// room for kMaxSplitTail tiles).
+// room for kMaxSplitTail tiles), and the work-queue counters of its launches.
 struct WorkspaceLayout {
   int64_t n_qtiles, sq_pad;
-  size_t acc, l, r, acc_x, l_x, r_x, total;
+  size_t acc, l, r, acc_x, l_x, r_x, queue, total;
 };
 bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out);
 
@@ -151,6 +151,7 @@ struct AttnArgs {
   float* r;
   int32_t accumulate;  // 0: these keys open the run (initialise); 1: merge into workspace
   int32_t n_whole, parts;      // split plan (bf16 kernel)
+  unsigned long long* queue;   // bf16 kernel: 8 work-queue counters (cleared before each launch)
   float* acc_x;                // parts 1.. of split tiles: [(tile - n_whole) * (parts - 1) + part - 1]
   float* l_x;
   float* r_x;

@@ -74,7 +74,9 @@ STAGES = 8
 AHEAD = 6
 TILE_BYTES = 8192
 V_RING = STAGES * TILE_BYTES          # the V ring starts 64 KB into the shared buffer
-DMA_WAIT = (AHEAD - 2) * 4            # DMA instructions allowed in flight at a step start
+PAIRS = os.environ.get("FIXEDM_PAIRS", "0") == "1"   # one barrier per two steps (see step())
+# DMA instructions allowed in flight at a barrier: tile t+1 (and with PAIRS t+2) must have landed
+DMA_WAIT = (AHEAD - 2 - (1 if PAIRS else 0)) * 4
 
 O_BASE, Q_BASE, K_BASE, V0_ABASE = 0, 128, 192, 224
 S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
@@ -277,7 +279,12 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
     stage_next = (t_mod + 1) % STAGES
     stage_dma = (t_mod + AHEAD) % STAGES
 
-    early = 0 if first else BARRIER_AFTER
+    # With PAIRS only even steps meet at the barrier: they wait for tiles t+1 and t+2 and load
+    # tiles t+6 and t+7 (into the stages of tiles t-2 and t-1, both read by every wave before
+    # this barrier); odd steps read tiles that landed before the previous barrier.
+    barrier_step = first or not PAIRS or t_mod % 2 == 0
+    dma_offsets = ([AHEAD, AHEAD + 1] if PAIRS else [AHEAD]) if barrier_step else []
+    early = 0 if first else (BARRIER_AFTER if barrier_step else None)
     if early == 0:
         e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
         e.emit("s_barrier")
@@ -299,26 +306,36 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
         # overwrite: let them take their operands first
         e.emit("s_nop 7")
         e.emit("s_nop 7")
-    if tail:
-        # tile t+6 may be the partial last tile or lie past the end: clamp its address to the
-        # start of the chunk's last 32-key window before the DMA reads it
-        clamp = []
-        for ptr, last in ((S_KT, S_KLAST), (S_VT, S_VLAST)):
-            clamp += [f"s_sub_u32 s{S_TMP}, s{last}, s{ptr}", f"s_subb_u32 s{S_TMP + 1}, s{last + 1}, s{ptr + 1}",
-                      f"s_cselect_b64 s[{ptr}:{ptr + 1}], s[{last}:{last + 1}], s[{ptr}:{ptr + 1}]"]
-        for ins in clamp:
-            e.emit(ins)
-    kt_reg, vt_reg = (S_KT6, S_VT6) if first else (S_KT, S_VT)
-    for i in range(2):
-        for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, kt_reg),
-                                    (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, vt_reg)):
-            between = kreads.pop(0) if DMA_WITH_KREAD else "s_nop 0"
-            extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", between,
-                          f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
+    # tail steps: a tile to load may be the partial last tile or lie past the end: its address
+    # is clamped to the start of the chunk's last 32-key window before the DMA reads it
+    clamp = []
+    for ptr, last in ((S_KT, S_KLAST), (S_VT, S_VLAST)):
+        clamp += [f"s_sub_u32 s{S_TMP}, s{last}, s{ptr}", f"s_subb_u32 s{S_TMP + 1}, s{last + 1}, s{ptr + 1}",
+                  f"s_cselect_b64 s[{ptr}:{ptr + 1}], s[{last}:{last + 1}], s[{ptr}:{ptr + 1}]"]
+    advance = [[f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"]
+               for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE))]
+    for di, off in enumerate(dma_offsets):
+        stage_dma = (t_mod + off) % STAGES
+        # the priming step loads tile 6 from its own registers (dead after it, clamped already)
+        from_t6 = first and off == AHEAD
+        kt_reg, vt_reg = (S_KT6, S_VT6) if from_t6 else (S_KT, S_VT)
+        if tail and not from_t6:
+            if di == 0:
+                for ins in clamp:
+                    e.emit(ins)
+            else:
+                extra.append(list(clamp))
+        for i in range(2):
+            for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, kt_reg),
+                                        (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, vt_reg)):
+                between = kreads.pop(0) if DMA_WITH_KREAD and kreads else "s_nop 0"
+                extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", between,
+                              f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
+        if not from_t6 and di + 1 < len(dma_offsets):     # the next tile to load
+            extra += [list(a) for a in advance]
     extra += [[kr] for kr in kreads]
-    if not first:     # the loop's next DMA address (the priming step's tile-6 registers are dead after it)
-        for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE)):
-            extra.append([f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"])
+    if dma_offsets and not (first and len(dma_offsets) == 1):
+        extra += [list(a) for a in advance]
 
     plan = softmax_plan(cur)
     slot = 0
@@ -344,10 +361,10 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
                 p = vreg(p_first(prv, n) + 4 * st, 4)
                 if not first:
                     e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
-                if i_mfma == early - 1:
+                if early is not None and i_mfma == early - 1:
                     e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
                     e.emit("s_barrier")
-                if extra and i_mfma >= early:
+                if extra and i_mfma >= (early or 0):
                     for ins in extra.pop(0):
                         e.emit(ins)
                 valu_slot()
@@ -510,8 +527,11 @@ __device__ __attribute__((always_inline)) inline void {name}(
 
 
 def generate() -> str:
-    return ("// Generated by gen_fixed_loop.py; do not edit by hand.\n\n" + generate_variant(False) + "\n"
-            + generate_variant(True))
+    head = ("// Generated by gen_fixed_loop.py; do not edit by hand.\n\n"
+            "// Ring protocol of the loops below, which the compiled bodies follow too: 1 = one barrier\n"
+            "// per two steps (tiles t+1, t+2 waited for and t+6, t+7 loaded at even steps), 0 = every step.\n"
+            f"constexpr int kPairSteps = {1 if PAIRS else 0};\n\n")
+    return head + generate_variant(False) + "\n" + generate_variant(True)
 
 
 def main(out_path=None):
