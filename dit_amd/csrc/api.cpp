@@ -190,7 +190,9 @@ bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out) {
     out->r_x = off; off = align256(off + xt * kQTile * 4);
   }
   out->queue = off;
-  if (p.dtype == FIXEDM_BF16) off = align256(off + 8 * sizeof(unsigned long long));
+  if (p.dtype == FIXEDM_BF16) off = align256(off + 16 * sizeof(unsigned long long));
+  out->slow_list = off;
+  if (p.dtype == FIXEDM_BF16) off = align256(off + (size_t)(p.batch * p.heads * out->n_qtiles) * 4);
   out->total = off;
   return true;
 }
@@ -455,6 +457,7 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.l_x = reinterpret_cast<float*>(wbase + wl.l_x);
   a.r_x = reinterpret_cast<float*>(wbase + wl.r_x);
   a.queue = reinterpret_cast<unsigned long long*>(wbase + wl.queue);
+  a.slow_list = reinterpret_cast<int32_t*>(wbase + wl.slow_list);
   const SplitPlan sp = plan_of(p, wl);
   a.n_whole = sp.n_whole;
   a.parts = sp.parts;

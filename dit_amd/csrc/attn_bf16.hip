@@ -813,9 +813,35 @@ __device__ inline QueueRange queue_range(const AttnArgs& a, int q) {
   return r;
 }
 
-// Takes the next item for a workgroup on XCD `xcc` (one thread calls it): the front of its own
-// queue, else the back of the others in turn.  `dead` marks queues seen empty.  -1: none left.
+// Whole tiles with a wave on the online-softmax body (an ineligible q-block) take ~3x as long
+// as fixed-m ones at the same clock; taken late, one of them would end the launch well after
+// the rest.  They are therefore taken first: the prep kernel lists them (queue[kSlowCount]
+// entries in slow_list), every workgroup drains that list before its queues (queue[kSlowTaken]
+// counts takes), and queue takes skip them.
+constexpr int kSlowCount = kQueues, kSlowTaken = kQueues + 1;
+
+__device__ inline bool tile_is_slow(const AttnArgs& a, int64_t tile) {
+  const int64_t bh = tile / a.n_qtiles;
+  const int qt = (int)(tile % a.n_qtiles);
+  for (int w = 0; w < 4; ++w) {
+    const int q0 = qt * kQTile + 64 * w;
+    const int beta = (q0 < a.Sq ? q0 : a.Sq - 1) / a.q_block;
+    if (a.elig[bh * a.nqb + beta] == 0) return true;
+  }
+  return false;
+}
+
+// Takes the next item for a workgroup on XCD `xcc` (one thread calls it): a listed slow tile,
+// else the front of its own queue, else the back of the others in turn.  `dead` marks queues
+// seen empty (bit kQueues: the slow list).  -1: none left.
 __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) {
+  if (!((dead >> kQueues) & 1u)) {
+    const unsigned long long n_slow = __hip_atomic_load(a.queue + kSlowCount, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long i = n_slow > 0 ? atomicAdd(a.queue + kSlowTaken, 1ull) : n_slow;
+    if (i < n_slow) return a.slow_list[i];
+    dead |= 1u << kQueues;
+  }
   for (int k = 0; k < kQueues; ++k) {
     const int q = (xcc + k) % kQueues;
     if ((dead >> q) & 1u) continue;
@@ -827,6 +853,10 @@ __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) 
       continue;
     }
     const int64_t j = k == 0 ? f : r.size - 1 - bk;
+    if (j < r.nw && tile_is_slow(a, r.w0 + j)) {   // listed: taken from the slow list
+      --k;                                          // this queue again
+      continue;
+    }
     return j < r.nw ? r.w0 + j : a.n_whole + r.p0 + (j - r.nw);
   }
   return -1;
@@ -850,8 +880,17 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   }
 }
 
-__global__ void queue_reset_kernel(unsigned long long* q) {
-  if (threadIdx.x < kQueues) q[threadIdx.x] = 0ull;
+// Before each launch: clears the queue counters and lists the slow whole tiles (in no
+// particular order: each tile's result does not depend on when it runs).
+__global__ __launch_bounds__(1024) void queue_prep_kernel(AttnArgs a) {
+  __shared__ unsigned int n_slow;
+  if (threadIdx.x == 0) n_slow = 0;
+  if (threadIdx.x <= kSlowTaken) a.queue[threadIdx.x] = 0ull;
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < a.n_whole; t += blockDim.x)
+    if (tile_is_slow(a, t)) a.slow_list[atomicAdd(&n_slow, 1u)] = (int32_t)t;
+  __syncthreads();
+  if (threadIdx.x == 0) a.queue[kSlowCount] = n_slow;
 }
 
 }  // namespace
@@ -861,7 +900,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int64_t items = a.n_whole + (tiles - a.n_whole) * a.parts;
   const int cus = device_cus();
   const int64_t grid = items < cus || cus <= 0 ? items : cus;
-  queue_reset_kernel<<<1, 64, 0, s>>>(a.queue);
+  queue_prep_kernel<<<1, 1024, 0, s>>>(a);
   attn_bf16_d128_kernel<<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -96,7 +96,7 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out);
 // room for kMaxSplitTail tiles), and the work-queue counters of its launches.
 struct WorkspaceLayout {
   int64_t n_qtiles, sq_pad;
-  size_t acc, l, r, acc_x, l_x, r_x, queue, total;
+  size_t acc, l, r, acc_x, l_x, r_x, queue, slow_list, total;
 };
 bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out);
 
@@ -151,7 +151,9 @@ struct AttnArgs {
   float* r;
   int32_t accumulate;  // 0: these keys open the run (initialise); 1: merge into workspace
   int32_t n_whole, parts;      // split plan (bf16 kernel)
-  unsigned long long* queue;   // bf16 kernel: 8 work-queue counters (cleared before each launch)
+  unsigned long long* queue;   // bf16 kernel: 8 work-queue counters, the slow-list length and
+                               // take counter (set up before each launch)
+  int32_t* slow_list;          // bf16 kernel: whole tiles taken first (room for every tile)
   float* acc_x;                // parts 1.. of split tiles: [(tile - n_whole) * (parts - 1) + part - 1]
   float* l_x;
   float* r_x;
