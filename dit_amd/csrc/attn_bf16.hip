@@ -400,28 +400,24 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
 // other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
 // loading tile t+kAhead into stage t-2.
 __device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ring& g, int t, int stage) {
-  if (kPairSteps && (t & 1)) return;   // one barrier per two steps: tiles t, t+1 waited at t-1
-  wait_vmcnt<(kAhead - 2 - kPairSteps) * kLoadsPerTile>();
+  wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
   barrier();
   issue_tile(smem, g, t + kAhead, (stage + kAhead) % kStages);
-  if (kPairSteps) issue_tile(smem, g, t + kAhead + 1, (stage + kAhead + 1) % kStages);
 }
 
-// Steps of the fixed-m assembly loop for a chunk of n_tiles >= 2 tiles: fast groups while every
-// tile they prefetch and score is a full one, then tail groups through the last tile and
-// past it (the steps past the end see only masked keys).  The online body takes the same
-// number of ring steps so both bodies meet at the same barriers.
+// Steps of the fixed-m assembly loop for a chunk of n_tiles >= 2 tiles: after the priming step
+// t = 0, fast groups of 8 steps while every tile they prefetch and score is a full one, then
+// single tail steps through step t = n_tiles, whose PV product completes the last tile.  The
+// online body takes n_tiles + 1 ring steps too, so both bodies meet at the same barriers.
 struct FixedSchedule {
-  int fast, tail, steps;
+  int fast, tail;
 };
 __device__ inline FixedSchedule fixed_schedule(int64_t len) {
   const int n_tiles = (int)((len + kKT - 1) / kKT), n_full = (int)(len / kKT);
-  if (n_tiles < 2) return {0, 0, 0};
-  // a fast group's last step loads tile t + kAhead (+ 1 with paired steps), which must be whole
-  const int last = kAhead + kPairSteps;
-  const int fast = n_full >= 1 + kStages + last ? (n_full - 1 - last) / kStages : 0;
-  const int tail = (n_tiles - kStages * fast + kStages - 1) / kStages;
-  return {fast, tail, kStages * (fast + tail)};
+  if (n_tiles < 2) return {0, 0};
+  // a fast group's last step t loads tile t + kAhead, which must be whole
+  const int fast = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
+  return {fast, n_tiles - kStages * fast};
 }
 
 // The three bodies a wave can run: the fixed-m assembly loop with logits from bf16(alpha q),
@@ -535,9 +531,9 @@ __device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, cons
       softmax_online(s, p, lsum, shift, o, a.alpha);
       compute_pv(smem, g, stage, p, o);
     }
-    // the fixed-m waves of this workgroup run sched.steps assembly steps after two prologue
-    // ring steps: take the same number of barriers (and keep loading the ring)
-    for (int t = n_tiles; t < sched.steps + 1; ++t) ring_step(const_cast<uint8_t*>(smem), g, t, t % kStages);
+    // the fixed-m waves of this workgroup meet n_tiles + 1 barriers after the prologue's (the
+    // priming step and steps 1 .. n_tiles): take the same number (and keep loading the ring)
+    if (n_tiles >= 2) ring_step(const_cast<uint8_t*>(smem), g, n_tiles, n_tiles % kStages);
   }
   wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is released
   barrier();

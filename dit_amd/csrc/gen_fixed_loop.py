@@ -74,9 +74,9 @@ STAGES = 8
 AHEAD = 6
 TILE_BYTES = 8192
 V_RING = STAGES * TILE_BYTES          # the V ring starts 64 KB into the shared buffer
-PAIRS = os.environ.get("FIXEDM_PAIRS", "0") == "1"   # one barrier per two steps (see step())
-# DMA instructions allowed in flight at a barrier: tile t+1 (and with PAIRS t+2) must have landed
-DMA_WAIT = (AHEAD - 2 - (1 if PAIRS else 0)) * 4
+# DMA instructions allowed in flight at a barrier: tile t+1 must have landed (one barrier per two
+# steps, waiting for tiles t+1 and t+2 and loading t+6 and t+7 at even steps, measured 0.6% slower)
+DMA_WAIT = (AHEAD - 2) * 4
 
 O_BASE, Q_BASE, K_BASE, V0_ABASE = 0, 128, 192, 224
 S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
@@ -279,12 +279,8 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
     stage_next = (t_mod + 1) % STAGES
     stage_dma = (t_mod + AHEAD) % STAGES
 
-    # With PAIRS only even steps meet at the barrier: they wait for tiles t+1 and t+2 and load
-    # tiles t+6 and t+7 (into the stages of tiles t-2 and t-1, both read by every wave before
-    # this barrier); odd steps read tiles that landed before the previous barrier.
-    barrier_step = first or not PAIRS or t_mod % 2 == 0
-    dma_offsets = ([AHEAD, AHEAD + 1] if PAIRS else [AHEAD]) if barrier_step else []
-    early = 0 if first else (BARRIER_AFTER if barrier_step else None)
+    dma_offsets = [AHEAD]
+    early = 0 if first else BARRIER_AFTER
     if early == 0:
         e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
         e.emit("s_barrier")
@@ -361,10 +357,10 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
                 p = vreg(p_first(prv, n) + 4 * st, 4)
                 if not first:
                     e.emit(f"v_mfma_f32_32x32x16_bf16 {o_reg(n, m)}, {vf}, {p}, {o_reg(n, m)}")
-                if early is not None and i_mfma == early - 1:
+                if i_mfma == early - 1:
                     e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
                     e.emit("s_barrier")
-                if extra and i_mfma >= (early or 0):
+                if extra and i_mfma >= early:
                     for ins in extra.pop(0):
                         e.emit(ins)
                 valu_slot()
@@ -446,14 +442,18 @@ def generate_variant(fp32a: bool) -> str:
     e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
     e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
     e.emit("s_cbranch_scc1 L_fixedm_group_%=")
-    # tail groups: clamped DMA and masked keys, through the chunk's last tile and past it
+    # tail steps: clamped DMA and masked keys, through step t = n_tiles (the PV product of the
+    # chunk's last tile): s[S_TCNT] counts the steps left, and the loop leaves after the step
+    # that brings it to 0, wherever that falls in the unrolled group of 8
     e.lines.append("L_fixedm_tail_%=:")
     e.s_written = {0: e.count - 1, 1: e.count - 1}
     for jj in range(STAGES):
         step(e, jj, tail=True, fp32a=fp32a)
-    e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
-    e.emit(f"s_cmp_lg_u32 s{S_TCNT}, 0")
-    e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
+        e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
+        e.emit(f"s_cmp_eq_u32 s{S_TCNT}, 0")
+        e.emit("s_cbranch_scc1 L_fixedm_end_%=")
+    e.emit("s_branch L_fixedm_tail_%=")
+    e.lines.append("L_fixedm_end_%=:")
     e.emit(f"v_add_f32 v{LSUM}, v{LSUM}, v{LSUM_HI}")
     e.emit(f"v_add_f32 v{LSUM + 1}, v{LSUM + 1}, v{LSUM_HI + 1}")
     e.emit("s_waitcnt lgkmcnt(0)")
@@ -467,7 +467,7 @@ def generate_variant(fp32a: bool) -> str:
             outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
-             f'"+{{s{S_CNT}}}"(groups)', f'"+{{s{S_TCNT}}}"(tail_groups)', f'"+{{s{S_J}}}"(next_tile)']
+             f'"+{{s{S_CNT}}}"(groups)', f'"+{{s{S_TCNT}}}"(tail_steps)', f'"+{{s{S_J}}}"(next_tile)']
     ins = []
     for n in range(2):
         for kk in range(8):
@@ -503,20 +503,21 @@ def generate_variant(fp32a: bool) -> str:
             "the exponent")
     return f"""// {what}.
 // The fixed-m pass over a chunk of >= 2 tiles: the priming step (S(0), then step t = 0: P(0),
-// S(1), V(0)'s fragments, the DMA of tile 6), `groups` fast groups, then `tail_groups` (>= 1)
-// tail groups of 8 pipelined 32-key steps, tiles t0 .. t0 + 8 (groups + tail_groups) - 1 with
-// t0 = 1.  On entry: tiles 0 .. 5 issued and tile 0 in LDS (waited and met at a barrier),
-// kt6 / vt6 = the addresses of tile 6 and kt / vt those of tile 7 (each clamped to the
-// chunk's last 32-key window), lo1 = tile 1's first real row, next_tile = 8 groups + 2 (the
-// tile whose S the first tail step computes).  The steps past the chunk's last tile see only
-// masked keys (p = 0), so the last of them completes the PV product of the last tile.  On
-// exit every LDS read has completed.
+// S(1), V(0)'s fragments, the DMA of tile 6), `groups` fast groups of 8 pipelined 32-key
+// steps, then `tail_steps` (>= 1) tail steps, so steps t = 1 .. 8 groups + tail_steps run;
+// step t turns S(t) into P(t), adds V(t-1) P(t-1) to O and computes S(t+1).  On entry: tiles
+// 0 .. 5 issued and tile 0 in LDS (waited and met at a barrier), kt6 / vt6 = the addresses of
+// tile 6 and kt / vt those of tile 7 (each clamped to the chunk's last 32-key window), lo1 =
+// tile 1's first real row, next_tile = 8 groups + 2 (the tile whose S the first tail step
+// computes).  Keys past the chunk's last tile are masked (p = 0); with tail_steps = n_tiles -
+// 8 groups the last step completes the PV product of the last tile.  On exit every LDS read
+// has completed.
 __device__ __attribute__((always_inline)) inline void {name}(
     f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8],
     float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
     const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt6, uint64_t vt6, uint32_t lo1, uint64_t kt, uint64_t vt,
     uint64_t ktile, uint64_t vtile, uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full,
-    uint32_t lo_part, uint32_t groups, uint32_t tail_groups, uint32_t next_tile{", float alpha" if fp32a else ""}) {{
+    uint32_t lo_part, uint32_t groups, uint32_t tail_steps, uint32_t next_tile{", float alpha" if fp32a else ""}) {{
   asm volatile(
 {body}
       : {join(outs)}
@@ -527,10 +528,7 @@ __device__ __attribute__((always_inline)) inline void {name}(
 
 
 def generate() -> str:
-    head = ("// Generated by gen_fixed_loop.py; do not edit by hand.\n\n"
-            "// Ring protocol of the loops below, which the compiled bodies follow too: 1 = one barrier\n"
-            "// per two steps (tiles t+1, t+2 waited for and t+6, t+7 loaded at even steps), 0 = every step.\n"
-            f"constexpr int kPairSteps = {1 if PAIRS else 0};\n\n")
+    head = "// Generated by gen_fixed_loop.py; do not edit by hand.\n\n"
     return head + generate_variant(False) + "\n" + generate_variant(True)
 
 
