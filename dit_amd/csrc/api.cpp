@@ -43,6 +43,8 @@ fixedm_status check_problem(const fixedm_problem* p) {
   // grid limits of the kernels (y dimension = B*H; 32-bit row indices)
   if (p->batch > 65535 || p->heads > 65535 || p->batch * p->heads > 65535) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   if (p->sq > (int64_t)1 << 30 || p->sk_total > kMaxKeys) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  // bf16: the key tiles of one launch are counted in 32 bits
+  if (p->dtype == FIXEDM_BF16 && p->sk_total > kMaxKeysBf16) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   const int64_t n_qtiles = (p->sq + kQTile - 1) / kQTile;
   if (p->batch * p->heads * n_qtiles > ((int64_t)1 << 31) - 1) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   return FIXEDM_OK;
@@ -193,6 +195,9 @@ bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out) {
   if (p.dtype == FIXEDM_BF16) off = align256(off + 16 * sizeof(unsigned long long));
   out->slow_list = off;
   if (p.dtype == FIXEDM_BF16) off = align256(off + (size_t)(p.batch * p.heads * out->n_qtiles) * 4);
+  out->ptable = off;
+  if (p.dtype == FIXEDM_BF16)
+    off = align256(off + (size_t)(p.batch * p.heads) * kPieceLists * kPieceSlots * kPieceWords * 4);
   out->total = off;
   return true;
 }
@@ -458,6 +463,7 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.r_x = reinterpret_cast<float*>(wbase + wl.r_x);
   a.queue = reinterpret_cast<unsigned long long*>(wbase + wl.queue);
   a.slow_list = reinterpret_cast<int32_t*>(wbase + wl.slow_list);
+  a.ptable = reinterpret_cast<uint32_t*>(wbase + wl.ptable);
   const SplitPlan sp = plan_of(p, wl);
   a.n_whole = sp.n_whole;
   a.parts = sp.parts;
@@ -501,10 +507,12 @@ fixedm_status enqueue_attn(AttnArgs a, const fixedm_problem& p, const fixedm_ten
   while (c < n_chunks) {
     a.n_chunks = 0;
     a.call_len = 0;
+    a.call_tiles = 0;
     while (c < n_chunks && a.n_chunks < kMaxChunksPerLaunch) {
       if (chunk_len[c] > 0) {
         a.ch[a.n_chunks++] = make_chunk(k_chunks[c], v_chunks[c], chunk_len[c], a.call_len);
         a.call_len += chunk_len[c];
+        a.call_tiles += (chunk_len[c] + 31) / 32;
       }
       ++c;
     }

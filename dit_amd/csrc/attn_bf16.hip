@@ -88,18 +88,31 @@ __device__ inline void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One 16-byte-per-lane global->LDS load; lane L's 16 bytes land at LDS byte lds + 16 L.
-// Written as inline asm so the compiler's wait-count pass does not treat every later LDS
-// read as aliasing an in-flight DMA (it would insert vmcnt(0) and drain the ring); the
-// ring's vmcnt waits are explicit instead.  The destination is passed as an LDS pointer
-// (with a memory clobber) so the compiler knows the asm writes the shared buffer.  M0
-// carries the wave-uniform LDS address; no compiler-generated instruction here reads M0.
+// One 16-byte-per-lane global->LDS load of a tile row's chunk: lane L's 16 bytes come from
+// sbase + max(row - rsh, 0) * stride + chunk and land at LDS byte lds + 16 L.  Written as
+// inline asm so the compiler's wait-count pass does not treat every later LDS read as
+// aliasing an in-flight load (it would insert vmcnt(0) and drain the ring); the ring's vmcnt
+// waits are explicit instead.  The lane offset is formed inside the block from loop-invariant
+// inputs: the compiler takes a register an asm load reads as busy until the load completes,
+// so rewriting a register that holds an offset would make it wait on the vector memory
+// counter (which also counts the ring's loads) and drain the ring.  The destination is passed
+// as an LDS pointer (with a memory clobber) so the compiler knows the asm writes the shared
+// buffer.  M0 carries the wave-uniform LDS address; no compiler-generated instruction here
+// reads M0.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-__device__ inline void dma16_saddr(uint32_t voff, uint64_t sbase, lds_u8* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
-}
-__device__ inline void dma16_vaddr(const void* g, lds_u8* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+__device__ inline void dma16_row(uint32_t row, uint32_t chunk, uint32_t rsh, uint32_t stride, uint64_t sbase,
+                                 lds_u8* lds) {
+  uint32_t off;
+  asm volatile(
+      "v_subrev_u32 %0, %3, %1\n\t"
+      "v_max_i32 %0, 0, %0\n\t"
+      "v_mul_lo_u32 %0, %0, %4\n\t"
+      "v_add_u32 %0, %0, %2\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "global_load_lds_dwordx4 %0, %6"
+      : "=&v"(off)
+      : "v"(row), "v"(chunk), "s"(rsh), "s"(stride), "s"(lds), "s"(sbase)
+      : "memory");
 }
 
 __device__ inline uint64_t uniform_u64(uint64_t x) {
@@ -108,88 +121,137 @@ __device__ inline uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Per-workgroup context of one chunk: source rows, DMA lane offsets, LDS read bases.
-struct Ring {
-  uint64_t kbase, vbase;        // byte address of key row 0 of this (b, h) in K and V
-  uint64_t ktile, vtile;        // bytes between consecutive 32-key tiles
-  int64_t len;                  // real keys in the chunk
-  int64_t k_ss, v_ss;           // row strides (elements)
-  uint32_t kdma[2], vdma[2];    // lane byte offsets of this wave's two rows in a tile
-  int row[2];                   // those rows (0..31)
-  int ck[2], cv[2];             // logical 16-byte chunk each lane fetches
-  int wave;
-  uint32_t koff[8];             // K fragment LDS offsets (stage 0) for k-steps 0..7
-  uint32_t voff[4];             // V^T fragment LDS offsets (stage 0) for dim tiles 0..3
+// LDS read offsets of this lane in stage 0: the K fragment rows of k-steps 0..7 and the V^T
+// transpose reads of dim tiles 0..3 (XOR-swizzled like the DMA placement below).
+struct LdsOff {
+  uint32_t koff[8];
+  uint32_t voff[4];
 };
+__device__ inline LdsOff lds_offsets(int lane) {
+  LdsOff g;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, j = lane & 15, dhalf = grp & 1;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) g.koff[kk] = (uint32_t)(lq * kRowBytes + (((2 * kk + hh) ^ (lq & 15)) << 4));
+  const int r0 = 4 * hh + (j >> 2);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int chunk = 4 * m + 2 * dhalf + ((j & 3) >> 1);
+    g.voff[m] = (uint32_t)(kVRing + r0 * kRowBytes + ((chunk ^ ((r0 & 3) << 2)) << 4) + (j & 1) * 8);
+  }
+  return g;
+}
 
-// Issues this wave's share (4 rows of K and 4 of V, 1 KB each) of tile t into LDS stage
-// `stage`.  Lane L of instruction i lands at row 4 (2 w + i) + L / 16, physical chunk
-// L % 16, and fetches the logical chunk the swizzle puts there.  Tile t holds the 32 keys
-// from min(32 t, len - 32): the partial last tile is loaded as the chunk's last 32-key window
-// and tiles past the end repeat it, so every load is one in-bounds tile-wide window (the
-// rows that are not new keys are masked when the scores are formed).  A chunk shorter than
-// one tile clamps each row to the last key instead.
-__device__ __attribute__((always_inline)) void issue_tile(uint8_t* smem, const Ring& g, int t, int stage) {
+// This lane's part of a tile load: lane L of DMA instruction i (0, 1) of wave w writes row
+// 4 (2 w + i) + L / 16 of the tile at physical 16-byte chunk L % 16, and fetches the logical
+// chunk the swizzle puts there (K: phys ^ (row & 15), V: phys ^ ((row & 3) << 2)).  ck / cv
+// are those chunks' byte offsets in the row.
+struct DmaLane {
+  uint32_t row[2], ck[2], cv[2];
+};
+__device__ inline DmaLane dma_lane(int wave, int lane) {
+  DmaLane d;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (2 * wave + i) + (lane >> 4), phys = lane & 15;
+    d.row[i] = (uint32_t)row;
+    d.ck[i] = (uint32_t)(16 * (phys ^ (row & 15)));
+    d.cv[i] = (uint32_t)(16 * (phys ^ ((row & 3) << 2)));
+  }
+  return d;
+}
+
+// The key tiles of one work item are the 32-key tiles of its chunk pieces in order, read
+// from a piece descriptor list (pieces.h) that the prep kernel writes before each launch.
+// The lists are read through the constant address space, so the reads are scalar loads:
+// a vector load here would make the compiler wait on the vector memory counter, which also
+// counts the ring's loads in flight, and drain the ring.
+typedef __attribute__((address_space(4))) const uint32_t desc_word;
+__device__ inline uint32_t desc_at(const uint32_t* d, int i) { return ((const desc_word*)d)[i]; }
+__device__ inline uint64_t desc_u64(const uint32_t* d, int i) {
+  return ((uint64_t)desc_at(d, i + 1) << 32) | desc_at(d, i);
+}
+
+// Load side of the ring as the compiled body runs it (the assembly loop keeps the same
+// cursor in SGPRs): the next tile's addresses, the tiles left in the piece, this lane's
+// offsets into the piece's rows.
+struct DmaCursor {
+  const uint32_t* d;
+  uint64_t kt, vt, ktile, vtile, klast, vlast;
+  uint32_t rem, kss, vss, rsh;
+};
+__device__ inline void dma_load(DmaCursor& c) {
+  const uint32_t* d = c.d;
+  c.kt = desc_u64(d, 0);
+  c.vt = desc_u64(d, 2);
+  c.ktile = desc_u64(d, 4);
+  c.vtile = desc_u64(d, 6);
+  c.klast = desc_u64(d, 8);
+  c.vlast = desc_u64(d, 10);
+  c.rem = desc_at(d, 12);
+  c.kss = desc_at(d, 13);
+  c.vss = desc_at(d, 14);
+  c.rsh = desc_at(d, 15);
+}
+// Issues this wave's share of the next tile (2 KB of K rows, 2 KB of V rows) into LDS stage
+// `stage`, then advances: the piece's last tile is its last window, and past the piece's
+// end the cursor moves to the next descriptor.
+__device__ __attribute__((always_inline)) void dma_next(uint8_t* smem, DmaCursor& c, const DmaLane& ln, int wave,
+                                                        int stage) {
   lds_u8* kl = (lds_u8*)(smem + stage * kTileBytes);
   lds_u8* vl = (lds_u8*)(smem + kVRing + stage * kTileBytes);
-  if (g.len >= kKT) {
-    int64_t row0 = (int64_t)t * kKT;
-    if (row0 > g.len - kKT) row0 = g.len - kKT;
-    const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(row0 * g.k_ss * 2));
-    const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(row0 * g.v_ss * 2));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
-      dma16_saddr(g.kdma[i], kt, kl + blk);
-      dma16_saddr(g.vdma[i], vt, vl + blk);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * g.wave + i));
-      int64_t key = g.row[i];
-      if (key >= g.len) key = g.len - 1;
-      dma16_vaddr((const void*)(g.kbase + (uint64_t)(key * g.k_ss * 2) + 16 * g.ck[i]), kl + blk);
-      dma16_vaddr((const void*)(g.vbase + (uint64_t)(key * g.v_ss * 2) + 16 * g.cv[i]), vl + blk);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * wave + i));
+    dma16_row(ln.row[i], ln.ck[i], c.rsh, c.kss, c.kt, kl + blk);
+    dma16_row(ln.row[i], ln.cv[i], c.rsh, c.vss, c.vt, vl + blk);
   }
+  c.kt += c.ktile;
+  c.vt += c.vtile;
+  if (--c.rem == 1) {
+    c.kt = c.klast;
+    c.vt = c.vlast;
+  } else if (c.rem == 0) {
+    c.d += kPieceWords;
+    dma_load(c);
+  }
+}
+
+// Score side: the first real row of each tile in turn.
+struct MaskCursor {
+  const uint32_t* d;
+  uint32_t rem, lo_last, lo_base;
+};
+__device__ inline void mask_load(MaskCursor& m) {
+  m.rem = desc_at(m.d, 16);
+  m.lo_last = desc_at(m.d, 17);
+  m.lo_base = desc_at(m.d, 18);
+}
+__device__ inline int mask_next(MaskCursor& m) {
+  const int lo = (int)(m.rem == 1 ? m.lo_last : m.lo_base);
+  if (--m.rem == 0) {
+    m.d += kPieceWords;
+    mask_load(m);
+  }
+  return lo;
 }
 
 // Key index within the tile held by accumulator register r of this lane.
 __device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-// Rows of tile t that hold keys not yet counted: [lo, hi) (see issue_tile).
-struct RowRange {
-  int lo, hi;
-};
-__device__ inline RowRange tile_rows(const Ring& g, int t) {
-  if (g.len < kKT) return {0, (int)g.len};
-  const int64_t n_full = g.len / kKT, rem = g.len - n_full * kKT;
-  if (t < n_full) return {0, kKT};
-  if (t == n_full && rem > 0) return {kKT - (int)rem, kKT};
-  return {kKT, kKT};
-}
-
-// S^T(tile) = K(tile) Q^T + init for one 32-key tile and two 32-query tiles: 16 MFMAs.  The
-// fixed-m body starts the chain from -(m + c_i) so S arrives as the exponent; the online
-// body starts from 0.  Rows of the tile outside `rows` start from -inf (p = 0).
-__device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const Ring& g, int stage,
-                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2],
-                                                         const float (&init)[2], RowRange rows, int hh) {
+// S^T(tile) = K(tile) Q^T for one 32-key tile and two 32-query tiles: 16 MFMAs.  Rows of the
+// tile before `lo` (keys that are not real) start from -inf (p = 0), the others from 0.
+__device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const LdsOff& g, int stage,
+                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2], int lo,
+                                                         int hh) {
   const uint8_t* ks = smem + stage * kTileBytes;
   bf16x8 kf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
-  f32x16 c[2];
+  f32x16 c;
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = tile_key(r, hh);
-      c[n][r] = key >= rows.lo && key < rows.hi ? init[n] : -INFINITY;
-    }
-  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], c[0], 0, 0, 0);
-  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], c[1], 0, 0, 0);
+  for (int r = 0; r < 16; ++r) c[r] = tile_key(r, hh) >= lo ? 0.0f : -INFINITY;
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], c, 0, 0, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], c, 0, 0, 0);
 #pragma unroll
   for (int kk = 1; kk < 8; ++kk) {
     s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], s[0], 0, 0, 0);
@@ -197,26 +259,10 @@ __device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, co
   }
 }
 
-// V^T fragments of one tile (the A operands of O^T += V^T P^T): for each 16-key step st and
-// 32-dim tile m, a lane holds one dim and 8 keys in the P register order.  Each fragment
-// comes from two LDS transpose reads, each giving 4 keys x 16 dims to a 16-lane group.
-__device__ __attribute__((always_inline)) void load_v(const uint8_t* smem, const Ring& g, int stage,
-                                                      bf16x8 (&vf)[2][4]) {
-  const uint8_t* vs = smem + stage * kTileBytes;
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint8_t* a0 = vs + g.voff[m] + 4096 * st;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 2048));
-      vf[st][m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
-}
-
-// O^T += V(tile)^T P(tile)^T: four 32-dim tiles x two 16-key steps x two query tiles.
-__device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, const Ring& g, int stage,
+// O^T += V(tile)^T P(tile)^T: four 32-dim tiles x two 16-key steps x two query tiles.  For
+// each 16-key step st and 32-dim tile m a lane holds one dim and 8 keys in the P register
+// order, from two LDS transpose reads (each 4 keys x 16 dims to a 16-lane group).
+__device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, const LdsOff& g, int stage,
                                                           const bf16x8 (&p)[2][2], f32x16 (&o)[2][4]) {
   const uint8_t* vs = smem + stage * kTileBytes;
 #pragma unroll
@@ -233,95 +279,8 @@ __device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, c
   }
 }
 
-// The steady-state fixed-m loop, written out instruction by instruction (generated).
+// The fixed-m pass of a work item, written out instruction by instruction (generated).
 #include "fixed_loop.inc"
-
-// O^T += V(tile)^T P(tile)^T for a chunk piece of a single tile in the fixed-m body, with the
-// accumulators in the AGPRs the assembly loop keeps them in: in a chunk loop a compiled MFMA
-// on O would move the accumulators to other registers for the whole loop.  The leading and
-// trailing wait states cover the VALU-write -> MFMA-read and MFMA-write -> read hazards the
-// compiler cannot see across the block.
-__device__ __attribute__((always_inline)) inline void pv_tile_asm(f32x16 (&o)[2][4], const bf16x8 (&vf)[2][4],
-                                                                  const bf16x8 (&p)[2][2]) {
-  asm volatile(
-      "s_nop 4\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %4, %8, %18, %4\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %9, %16, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %5, %9, %18, %5\n"
-      "v_mfma_f32_32x32x16_bf16 %2, %10, %16, %2\n"
-      "v_mfma_f32_32x32x16_bf16 %6, %10, %18, %6\n"
-      "v_mfma_f32_32x32x16_bf16 %3, %11, %16, %3\n"
-      "v_mfma_f32_32x32x16_bf16 %7, %11, %18, %7\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %12, %17, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %4, %12, %19, %4\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %13, %17, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %5, %13, %19, %5\n"
-      "v_mfma_f32_32x32x16_bf16 %2, %14, %17, %2\n"
-      "v_mfma_f32_32x32x16_bf16 %6, %14, %19, %6\n"
-      "v_mfma_f32_32x32x16_bf16 %3, %15, %17, %3\n"
-      "v_mfma_f32_32x32x16_bf16 %7, %15, %19, %7\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 3\n"
-      : "+{a[0:15]}"(o[0][0]), "+{a[16:31]}"(o[0][1]), "+{a[32:47]}"(o[0][2]), "+{a[48:63]}"(o[0][3]),
-        "+{a[64:79]}"(o[1][0]), "+{a[80:95]}"(o[1][1]), "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3])
-      : "v"(vf[0][0]), "v"(vf[0][1]), "v"(vf[0][2]), "v"(vf[0][3]),
-        "v"(vf[1][0]), "v"(vf[1][1]), "v"(vf[1][2]), "v"(vf[1][3]),
-        "v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]));
-}
-
-// S^T(tile) = K(tile) (alpha Q)^T + init for the fixed-m body, the 16 MFMAs as one asm block
-// with the query fragments in the AGPRs the assembly loop reads them from: the query
-// fragments then keep one home through the chunk loop.  init (in s on entry) is -(m + c_i)
-// for the tile's real keys and -inf for the others.
-__device__ __attribute__((always_inline)) inline void s_tile_asm(f32x16 (&s)[2], const bf16x8 (&kf)[8],
-                                                                 const bf16x8 (&qf)[2][8]) {
-  asm volatile(
-      "s_nop 4\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %2, %18, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %3, %19, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %4, %20, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %5, %21, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %6, %22, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %15, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %7, %23, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %8, %24, %1\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %9, %17, %0\n"
-      "v_mfma_f32_32x32x16_bf16 %1, %9, %25, %1\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 3\n"
-      : "+v"(s[0]), "+v"(s[1])
-      : "v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]), "v"(kf[5]), "v"(kf[6]), "v"(kf[7]),
-        "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
-        "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]), "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
-        "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]), "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
-        "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]), "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]));
-}
-
-__device__ __attribute__((always_inline)) void compute_s_fixed(const uint8_t* smem, const Ring& g, int stage,
-                                                               const bf16x8 (&qf)[2][8], f32x16 (&s)[2],
-                                                               const float (&init)[2], RowRange rows, int hh) {
-  const uint8_t* ks = smem + stage * kTileBytes;
-  bf16x8 kf[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = tile_key(r, hh);
-      s[n][r] = key >= rows.lo && key < rows.hi ? init[n] : -INFINITY;
-    }
-  s_tile_asm(s, kf, qf);
-}
 
 // Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
 // and adds the fp32 probabilities to the row sum, key by key.
@@ -338,40 +297,14 @@ __device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int 
   return r;
 }
 
-// Fixed-m probabilities of one tile: S already holds the exponent alpha q.k - (m + c_i) (the
-// query fragments are pre-scaled by alpha and the MFMA chain starts from -(m + c_i), or
-// from -inf for masked rows), so p = 2^S: no max, no rescale.
-__device__ __attribute__((always_inline)) void softmax_fixed(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
-                                                             float (&lsum)[2]) {
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    f32x16 e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[n][r]);
-    p[n][0] = pack8_sum(e, 0, lsum[n]);
-    p[n][1] = pack8_sum(e, 8, lsum[n]);
-  }
-}
-
-// Fixed-m probabilities with the logit factor applied in fp32 (a one-tile chunk piece of an
-// eligible block whose bound is above kR17MaxU): S holds q . k from the unscaled query
-// fragments (masked rows -inf), e = alpha S - (m + c_i), p = 2^e.  No max, no rescale.
-__device__ __attribute__((always_inline)) void softmax_fixed_fp32(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
-                                                                  float (&lsum)[2], const float (&shift)[2],
-                                                                  float alpha) {
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    f32x16 e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -shift[n]));
-    p[n][0] = pack8_sum(e, 0, lsum[n]);
-    p[n][1] = pack8_sum(e, 8, lsum[n]);
-  }
-}
-
-// Online-softmax probabilities of one tile (the fallback body): raise the running max,
-// rescale the accumulator and the row sum, then exponentiate against the new max.  Masked
-// rows arrive as -inf scores (every tile this body visits has at least one real key).
+// Online-softmax probabilities of one tile (the fallback body).  The running reference r of
+// each query row (base 2) is raised to the row's max only when some row of the wave's query
+// tile exceeds its r by more than kRescaleSlack; the accumulator and the row sum are then
+// rescaled by 2^(r_old - r_new) (one wave-uniform branch).  Between raises the probabilities
+// 2^(alpha s - r) stay below 2^kRescaleSlack, well inside the bf16 and fp32 ranges, and O / l
+// does not depend on which r was used, so most tiles skip the 64 accumulator multiplies.
+// Masked rows arrive as -inf scores (every tile this body visits has at least one real key).
+constexpr float kRescaleSlack = 8.0f;
 __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
                                                               float (&lsum)[2], float (&rmax)[2],
                                                               f32x16 (&o)[2][4], float alpha) {
@@ -381,206 +314,103 @@ __device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float rn = fmaxf(rmax[n], alpha * mx);
-    const float f = __builtin_amdgcn_exp2f(rmax[n] - rn);
-    rmax[n] = rn;
-    lsum[n] *= f;
+    const float am = alpha * mx;
+    if (__builtin_amdgcn_ballot_w64(am > rmax[n] + kRescaleSlack) != 0) {
+      const float rn = fmaxf(rmax[n], am);
+      const float f = __builtin_amdgcn_exp2f(rmax[n] - rn);
+      rmax[n] = rn;
+      lsum[n] *= f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) o[n][m] *= f;
+      for (int m = 0; m < 4; ++m) o[n][m] *= f;
+    }
     f32x16 e;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -rn));
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -rmax[n]));
     p[n][0] = pack8_sum(e, 0, lsum[n]);
     p[n][1] = pack8_sum(e, 8, lsum[n]);
   }
 }
 
-// Ring bookkeeping at the top of every tile step, identical in both bodies so the waves of
-// one workgroup meet at the same barriers: wait for this wave's part of tile t+1, meet the
-// other waves (tile t+1 is then complete in LDS and stage t-2 is no longer read), and start
-// loading tile t+kAhead into stage t-2.
-__device__ __attribute__((always_inline)) void ring_step(uint8_t* smem, const Ring& g, int t, int stage) {
-  wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
-  barrier();
-  issue_tile(smem, g, t + kAhead, (stage + kAhead) % kStages);
-}
-
-// Steps of the fixed-m assembly loop for a chunk of n_tiles >= 2 tiles: after the priming step
-// t = 0, fast groups of 8 steps while every tile they prefetch and score is a full one, then
-// single tail steps through step t = n_tiles, whose PV product completes the last tile.  The
-// online body takes n_tiles + 1 ring steps too, so both bodies meet at the same barriers.
-struct FixedSchedule {
-  int fast, tail;
-};
-__device__ inline FixedSchedule fixed_schedule(int64_t len) {
-  const int n_tiles = (int)((len + kKT - 1) / kKT), n_full = (int)(len / kKT);
-  if (n_tiles < 2) return {0, 0};
-  // a fast group's last step t loads tile t + kAhead, which must be whole
-  const int fast = n_full >= 1 + kStages + kAhead ? (n_full - 1 - kAhead) / kStages : 0;
-  return {fast, n_tiles - kStages * fast};
-}
-
-// The three bodies a wave can run: the fixed-m assembly loop with logits from bf16(alpha q),
-// the fixed-m assembly loop that applies the logit factor in fp32 (one FMA per score), and
-// the online-softmax fallback (compiled).
-enum Body { kFixedAsm, kFixedAsmF32, kOnline };
-
-template <Body kBody>
-__device__ __attribute__((always_inline)) void run_chunk(const AttnArgs& a, const ChunkDesc& cd,
-                                                         const uint8_t* smem, const bf16x8 (&qf)[2][8],
-                                                         f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
-                                                         int b, int h) {
-  // The lane's offsets are rebuilt for every chunk piece from an id the compiler cannot
-  // hoist: kept live across the assembly loop, which uses every register, they would spill.
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, hh = lane >> 5;
-  Ring g;
-  g.wave = tid >> 6;
-  g.len = cd.len;
-  g.k_ss = cd.k_ss;
-  g.v_ss = cd.v_ss;
-  g.kbase = (uint64_t)(reinterpret_cast<const uint16_t*>(cd.k) + b * cd.k_sb + h * cd.k_sh);
-  g.vbase = (uint64_t)(reinterpret_cast<const uint16_t*>(cd.v) + b * cd.v_sb + h * cd.v_sh);
-  g.ktile = (uint64_t)(kKT * cd.k_ss * 2);
-  g.vtile = (uint64_t)(kKT * cd.v_ss * 2);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 4 * (2 * g.wave + i) + (lane >> 4);
-    const int phys = lane & 15;
-    g.row[i] = row;
-    g.ck[i] = phys ^ (row & 15);
-    g.cv[i] = phys ^ ((row & 3) << 2);
-    g.kdma[i] = (uint32_t)(row * cd.k_ss * 2 + 16 * g.ck[i]);
-    g.vdma[i] = (uint32_t)(row * cd.v_ss * 2 + 16 * g.cv[i]);
-  }
-  {
-    const int lq = lane & 31, grp = lane >> 4, j = lane & 15, dhalf = grp & 1;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) g.koff[kk] = (uint32_t)(lq * kRowBytes + (((2 * kk + hh) ^ (lq & 15)) << 4));
-    const int r0 = 4 * hh + (j >> 2);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int chunk = 4 * m + 2 * dhalf + ((j & 3) >> 1);
-      g.voff[m] = (uint32_t)(kVRing + r0 * kRowBytes + ((chunk ^ ((r0 & 3) << 2)) << 4) + (j & 1) * 8);
-    }
-  }
-  const int n_tiles = (int)((cd.len + kKT - 1) / kKT);
-  const FixedSchedule sched = fixed_schedule(cd.len);
-#pragma unroll
-  for (int t = 0; t < kAhead; ++t) issue_tile(const_cast<uint8_t*>(smem), g, t, t);
+// The online-softmax pass of a work item (the fallback body), on the same ring as the
+// assembly loop: the prologue's six tile loads and barrier, then per tile t a barrier
+// (tile t+1 landed, stage t-2 free), the load of tile t+6, and the tile's scores,
+// probabilities and PV product; then one more barrier and load for the assembly loop's
+// step t = n_tiles.  The waves of a workgroup thus meet at the same barriers and load the
+// same tiles whichever body each runs.
+__device__ __attribute__((always_inline)) void run_online(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
+                                                          int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
+                                                          float (&lsum)[2], float (&rmax)[2], int wave, int lane) {
+  const int hh = lane >> 5;
+  const LdsOff g = lds_offsets(lane);
+  const DmaLane ln = dma_lane(wave, lane);
+  // The compiler does not count the ring's loads (inline asm): a vector memory access of its
+  // own still in flight when the loop starts (a spill reload, say) would make it wait on the
+  // counter inside the loop, every iteration, and drain the ring.  Waiting here, before the
+  // first ring load, leaves it nothing to wait for.
+  wait_vmcnt<0>();
+  DmaCursor dc;
+  dc.d = pieces;
+  dma_load(dc);
+  MaskCursor mc;
+  mc.d = pieces;
+  mask_load(mc);
+#pragma unroll 1
+  for (int t = 0; t < kAhead; ++t) dma_next(smem, dc, ln, wave, t);
   wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
   barrier();
-  if (kBody == kFixedAsm || kBody == kFixedAsmF32) {
-    const float nshift[2] = {-shift[0], -shift[1]};
-    if (n_tiles == 1) {
-      f32x16 s[2];
-      bf16x8 p[2][2];
-      // the S chain starts from -(m + c_i) (bf16(alpha q) fragments) or from 0 (fp32 alpha)
-      const float init[2] = {kBody == kFixedAsm ? nshift[0] : 0.0f, kBody == kFixedAsm ? nshift[1] : 0.0f};
-      compute_s_fixed(smem, g, 0, qf, s, init, tile_rows(g, 0), hh);
-      ring_step(const_cast<uint8_t*>(smem), g, 0, 0);
-      if (kBody == kFixedAsm) softmax_fixed(s, p, lsum);
-      else softmax_fixed_fp32(s, p, lsum, shift, a.alpha);
-      bf16x8 vf[2][4];
-      load_v(smem, g, 0, vf);
-      pv_tile_asm(o, vf, p);
-    } else {
-      // the whole pass from tile 0 on runs in the assembly block (priming step, then the loop)
-      const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
-      uint32_t koff[8], voff[4];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) koff[kk] = lds0 + g.koff[kk];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
-      const uint32_t dma[4] = {g.kdma[0], g.kdma[1], g.vdma[0], g.vdma[1]};
-      const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * g.wave);
-      // addresses of tiles kAhead and 1 + kAhead and of the chunk's last 32-key window
-      // (issue_tile's rule: tile t starts at min(32 t, len - 32))
-      const int64_t last_row = g.len - kKT;
-      const int64_t row6 = (int64_t)kAhead * kKT < last_row ? (int64_t)kAhead * kKT : last_row;
-      const int64_t row7 = (int64_t)(1 + kAhead) * kKT < last_row ? (int64_t)(1 + kAhead) * kKT : last_row;
-      const uint64_t kt6 = uniform_u64(g.kbase + (uint64_t)(row6 * g.k_ss * 2));
-      const uint64_t vt6 = uniform_u64(g.vbase + (uint64_t)(row6 * g.v_ss * 2));
-      const uint64_t kt = uniform_u64(g.kbase + (uint64_t)(row7 * g.k_ss * 2));
-      const uint64_t vt = uniform_u64(g.vbase + (uint64_t)(row7 * g.v_ss * 2));
-      const uint64_t k_last = uniform_u64(g.kbase + (uint64_t)(last_row * g.k_ss * 2));
-      const uint64_t v_last = uniform_u64(g.vbase + (uint64_t)(last_row * g.v_ss * 2));
-      const int n_full = (int)(g.len / kKT), rem = (int)(g.len - (int64_t)n_full * kKT);
-      // tile 1 is whole, or (33..63 keys) the partial last tile whose real keys start at 32 - rem
-      const uint32_t lo1 = n_full >= 2 ? 0u : (uint32_t)(kKT - rem);
-      if (kBody == kFixedAsm)
-        fixed_loop_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
-                       uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last, (uint32_t)n_full,
-                       (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast, (uint32_t)sched.tail,
-                       (uint32_t)(kStages * sched.fast + 2));
-      else
-        fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, dma, (uint32_t)(4 * hh), kt6, vt6, lo1, kt, vt,
-                             uniform_u64(g.ktile), uniform_u64(g.vtile), lds_wave, k_last, v_last,
-                             (uint32_t)n_full, (uint32_t)(rem > 0 ? kKT - rem : kKT), (uint32_t)sched.fast,
-                             (uint32_t)sched.tail, (uint32_t)(kStages * sched.fast + 2), a.alpha);
-    }
-  } else {
-    const float zero[2] = {0.0f, 0.0f};
-    for (int t = 0; t < n_tiles; ++t) {
-      const int stage = t % kStages;
-      ring_step(const_cast<uint8_t*>(smem), g, t, stage);
-      f32x16 s[2];
-      bf16x8 p[2][2];
-      compute_s(smem, g, stage, qf, s, zero, tile_rows(g, t), hh);
-      softmax_online(s, p, lsum, shift, o, a.alpha);
-      compute_pv(smem, g, stage, p, o);
-    }
-    // the fixed-m waves of this workgroup meet n_tiles + 1 barriers after the prologue's (the
-    // priming step and steps 1 .. n_tiles): take the same number (and keep loading the ring)
-    if (n_tiles >= 2) ring_step(const_cast<uint8_t*>(smem), g, n_tiles, n_tiles % kStages);
-  }
-  wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is released
-  barrier();
-}
-
-// Pins the accumulators and the query fragments to the AGPRs the assembly blocks use, at a
-// point of the chunk loop: with these at the top and bottom of every iteration the values keep
-// one home through the loop instead of being copied (and spilled) around each asm block.
-__device__ __attribute__((always_inline)) inline void pin_state(f32x16 (&o)[2][4], bf16x8 (&qf)[2][8]) {
-  asm volatile(""
-               : "+{a[0:15]}"(o[0][0]), "+{a[16:31]}"(o[0][1]), "+{a[32:47]}"(o[0][2]), "+{a[48:63]}"(o[0][3]), "+{a[64:79]}"(o[1][0]), "+{a[80:95]}"(o[1][1]), "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3]),
-                 "+{a[128:131]}"(qf[0][0]), "+{a[132:135]}"(qf[0][1]), "+{a[136:139]}"(qf[0][2]), "+{a[140:143]}"(qf[0][3]), "+{a[144:147]}"(qf[0][4]), "+{a[148:151]}"(qf[0][5]), "+{a[152:155]}"(qf[0][6]), "+{a[156:159]}"(qf[0][7]), "+{a[160:163]}"(qf[1][0]), "+{a[164:167]}"(qf[1][1]), "+{a[168:171]}"(qf[1][2]), "+{a[172:175]}"(qf[1][3]), "+{a[176:179]}"(qf[1][4]), "+{a[180:183]}"(qf[1][5]), "+{a[184:187]}"(qf[1][6]), "+{a[188:191]}"(qf[1][7]));
-}
-
-// Folds keys [klo, khi) of the launch's chunk sequence (the chunks concatenated in call
-// order) into the resident accumulators: one ring pass per chunk piece, the accumulators
-// and the online body's running max carried in registers from piece to piece.
-template <Body kBody>
-__device__ __attribute__((always_inline)) void run_keys(const AttnArgs& a, int64_t klo, int64_t khi,
-                                                        const uint8_t* smem, const bf16x8 (&qf)[2][8],
-                                                        f32x16 (&o)[2][4], float (&lsum)[2], float (&shift)[2],
-                                                        int b, int h) {
 #pragma unroll 1
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const int64_t c0 = a.ch[c].start, c1 = c0 + a.ch[c].len;
-    const int64_t s0 = klo > c0 ? klo : c0, s1 = khi < c1 ? khi : c1;
-    if (s1 <= s0) continue;
-    ChunkDesc cd = a.ch[c];
-    cd.k = reinterpret_cast<const uint16_t*>(cd.k) + (s0 - c0) * cd.k_ss;
-    cd.v = reinterpret_cast<const uint16_t*>(cd.v) + (s0 - c0) * cd.v_ss;
-    cd.len = s1 - s0;
-    if (kBody != kOnline) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
-    run_chunk<kBody>(a, cd, smem, qf, o, lsum, shift, b, h);
-    if (kBody != kOnline) pin_state(o, const_cast<bf16x8 (&)[2][8]>(qf));
+  for (int t = 0; t <= n_tiles; ++t) {
+    wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
+    barrier();
+    dma_next(smem, dc, ln, wave, (t + kAhead) % kStages);
+    if (t == n_tiles) break;
+    const int stage = t % kStages;
+    f32x16 s[2];
+    bf16x8 p[2][2];
+    compute_s(smem, g, stage, qf, s, mask_next(mc), hh);
+    softmax_online(s, p, lsum, rmax, o, a.alpha);
+    compute_pv(smem, g, stage, p, o);
   }
 }
 
-// One work item: a whole query tile (all keys of the launch's chunk sequence), or part p of a
-// split tail tile: keys [lo_p, lo_{p+1}) with lo_p = 32 * floor(call_len p / (32 parts)).
+// The fixed-m pass of a work item: the assembly loop, with bf16(alpha q) fragments (r17) or
+// with the logit factor applied in fp32.
+__device__ __attribute__((always_inline)) void run_fixed(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
+                                                         int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
+                                                         float (&lsum)[2], const float (&shift)[2], bool r17,
+                                                         int wave, int lane) {
+  // The lane's offsets are formed from an id the compiler cannot hoist above the assembly
+  // block, so they are not kept live (and spilled) around it.
+  int tid = wave * 64 + lane;
+  asm volatile("" : "+v"(tid));
+  const int w = tid >> 6, l = tid & 63;
+  const LdsOff g = lds_offsets(l);
+  const DmaLane ln = dma_lane(w, l);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem;
+  uint32_t koff[8], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = lds0 + g.koff[kk];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
+  const uint32_t lane6[6] = {ln.row[0], ln.row[1], ln.ck[0], ln.ck[1], ln.cv[0], ln.cv[1]};
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * w);
+  const float nshift[2] = {-shift[0], -shift[1]};
+  const uint64_t list = uniform_u64((uint64_t)(uintptr_t)pieces);
+  const uint32_t nt = __builtin_amdgcn_readfirstlane((uint32_t)n_tiles);
+  if (r17)
+    fixed_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, (uint32_t)(4 * (l >> 5)), list, nt, lds_wave);
+  else
+    fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, lane6, (uint32_t)(4 * (l >> 5)), list, nt, lds_wave,
+                         a.alpha);
+}
+
+// One work item: a whole query tile (all tiles of the launch's chunks), or part p of a split
+// tail tile: the launch's key tiles [T p / parts, T (p + 1) / parts) (T tiles in all).
 __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, uint8_t* smem, int tile,
                                                             int part) {
   const bool split = a.parts > 1 && tile >= a.n_whole;
-  int64_t klo = 0, khi = a.call_len;
-  if (split) {
-    klo = a.call_len * part / a.parts / kKT * kKT;
-    khi = part + 1 == a.parts ? a.call_len : a.call_len * (part + 1) / a.parts / kKT * kKT;
-  }
+  const int64_t T = a.call_tiles;
+  const int n_tiles = split ? (int)(T * (part + 1) / a.parts - T * part / a.parts) : (int)T;
   const int qt = tile % a.n_qtiles;
   const int bh = tile / a.n_qtiles;
   const int b = bh / a.H, h = bh % a.H;
@@ -665,11 +495,15 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
       }
       shift[n] = (float)mm + cdot[n];
     }
-    if (r17) run_keys<kFixedAsm>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
-    else run_keys<kFixedAsmF32>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
   } else {
     shift[0] = shift[1] = -INFINITY;
-    run_keys<kOnline>(a, klo, khi, smem, qf, o, lsum, shift, b, h);
+  }
+  if (n_tiles > 0) {
+    const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
+    if (fixed) run_fixed(a, smem, pieces, n_tiles, qf, o, lsum, shift, r17, wave, lane);
+    else run_online(a, smem, pieces, n_tiles, qf, o, lsum, shift, wave, lane);
+    wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is reused
+    barrier();
   }
 
   if (a.final_out && !split) {
@@ -876,17 +710,41 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_d128_kernel(AttnArgs a) {
   }
 }
 
-// Before each launch: clears the queue counters and lists the slow whole tiles (in no
-// particular order: each tile's result does not depend on when it runs).
-__global__ __launch_bounds__(1024) void queue_prep_kernel(AttnArgs a) {
-  __shared__ unsigned int n_slow;
-  if (threadIdx.x == 0) n_slow = 0;
-  if (threadIdx.x <= kSlowTaken) a.queue[threadIdx.x] = 0ull;
-  __syncthreads();
-  for (int64_t t = threadIdx.x; t < a.n_whole; t += blockDim.x)
-    if (tile_is_slow(a, t)) a.slow_list[atomicAdd(&n_slow, 1u)] = (int32_t)t;
-  __syncthreads();
-  if (threadIdx.x == 0) a.queue[kSlowCount] = n_slow;
+// The piece descriptor list of (b, h) = bh for list 0 (every tile of the launch's chunks) or
+// list 1 + p (part p of a split tile: tiles [T p / parts, T (p + 1) / parts) of the T).
+__device__ void write_piece_list(const AttnArgs& a, int64_t bh, int list) {
+  const int64_t T = a.call_tiles;
+  const int64_t v0 = list > 0 ? T * (list - 1) / a.parts : 0;
+  const int64_t v1 = list > 0 ? T * list / a.parts : T;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const auto chunk = [&](int c) {
+    const ChunkDesc& ch = a.ch[c];
+    return PieceSrc{(uint64_t)(uintptr_t)ch.k + (uint64_t)(2 * (b * ch.k_sb + h * ch.k_sh)),
+                    (uint64_t)(uintptr_t)ch.v + (uint64_t)(2 * (b * ch.v_sb + h * ch.v_sh)), ch.k_ss, ch.v_ss,
+                    ch.len};
+  };
+  build_piece_list(a.ptable + (bh * kPieceLists + list) * kPieceSlots * kPieceWords, chunk, a.n_chunks, v0, v1);
+}
+
+// Before each launch.  Block 0 clears the queue counters and lists the slow whole tiles (in
+// no particular order: each tile's result does not depend on when it runs); the other
+// blocks write the piece descriptor lists, one per thread.
+__global__ __launch_bounds__(256) void prep_kernel(AttnArgs a, int64_t lists) {
+  if (blockIdx.x == 0) {
+    __shared__ unsigned int n_slow;
+    if (threadIdx.x == 0) n_slow = 0;
+    if (threadIdx.x <= kSlowTaken) a.queue[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < a.n_whole; t += blockDim.x)
+      if (tile_is_slow(a, t)) a.slow_list[atomicAdd(&n_slow, 1u)] = (int32_t)t;
+    __syncthreads();
+    if (threadIdx.x == 0) a.queue[kSlowCount] = n_slow;
+    return;
+  }
+  const int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  if (i >= lists) return;
+  const int per_bh = a.parts > 1 ? 1 + a.parts : 1;
+  write_piece_list(a, i / per_bh, (int)(i % per_bh));
 }
 
 }  // namespace
@@ -896,7 +754,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int64_t items = a.n_whole + (tiles - a.n_whole) * a.parts;
   const int cus = device_cus();
   const int64_t grid = items < cus || cus <= 0 ? items : cus;
-  queue_prep_kernel<<<1, 1024, 0, s>>>(a);
+  const int64_t lists = (int64_t)a.B * a.H * (a.parts > 1 ? 1 + a.parts : 1);
+  prep_kernel<<<(unsigned)(1 + (lists + 255) / 256), 256, 0, s>>>(a, lists);
   attn_bf16_d128_kernel<<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }

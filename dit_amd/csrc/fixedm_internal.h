@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "../../include/fixedm.h"
+#include "pieces.h"
 
 namespace fixedm {
 
@@ -12,8 +13,12 @@ constexpr int kMaxBoundsChunks = 32;     // chunks one fixedm_bounds call accept
 constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (LDS staging)
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
 constexpr int kMaxParts = 4;             // key-range parts of a split tail tile (bf16 kernel)
+constexpr int kPieceWords = kPieceDescWords;   // dwords of one chunk-piece descriptor (bf16 kernel)
+constexpr int kPieceSlots = kMaxChunksPerLaunch + 1;   // descriptors of a list, terminator included
+constexpr int kPieceLists = 1 + kMaxParts;            // lists per (b, h): whole tiles, then each part
 constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
 constexpr int64_t kMaxKeys = (int64_t)1 << 38;   // most keys of a problem (and of a chunk)
+constexpr int64_t kMaxKeysBf16 = (int64_t)1 << 35;   // most keys of a bf16 problem
 constexpr int64_t kMaxRowStrideBf16 = (int64_t)1 << 26;   // largest sequence stride of a bf16 tensor
 
 // Grid-tail split of the bf16 attention launch.  The tiles fill whole rounds of one
@@ -96,7 +101,7 @@ bool bounds_layout(const fixedm_problem& p, BoundsLayout* out);
 // room for kMaxSplitTail tiles), and the work-queue counters of its launches.
 struct WorkspaceLayout {
   int64_t n_qtiles, sq_pad;
-  size_t acc, l, r, acc_x, l_x, r_x, queue, slow_list, total;
+  size_t acc, l, r, acc_x, l_x, r_x, queue, slow_list, ptable, total;
 };
 bool workspace_layout(const fixedm_problem& p, WorkspaceLayout* out);
 
@@ -135,7 +140,8 @@ struct AttnArgs {
   int64_t q_sb, q_ss, q_sh;
   ChunkDesc ch[kMaxChunksPerLaunch];
   int32_t n_chunks;
-  int64_t call_len;    // keys of all chunks of this launch (their concatenation is split)
+  int64_t call_len;    // keys of all chunks of this launch
+  int64_t call_tiles;  // their 32-key tiles (the sum over chunks of ceil(len / 32))
   int32_t B, H, D;
   int32_t Sq, n_qtiles, sq_pad;
   int32_t q_block, nqb;
@@ -154,6 +160,8 @@ struct AttnArgs {
   unsigned long long* queue;   // bf16 kernel: 8 work-queue counters, the slow-list length and
                                // take counter (set up before each launch)
   int32_t* slow_list;          // bf16 kernel: whole tiles taken first (room for every tile)
+  uint32_t* ptable;            // bf16 kernel: chunk-piece descriptor lists [B*H][kPieceLists]
+                               // [kPieceSlots][kPieceWords] (written before each launch)
   float* acc_x;                // parts 1.. of split tiles: [(tile - n_whole) * (parts - 1) + part - 1]
   float* l_x;
   float* r_x;

@@ -81,12 +81,22 @@ DMA_WAIT = (AHEAD - 2) * 4
 O_BASE, Q_BASE, K_BASE, V0_ABASE = 0, 128, 192, 224
 S_BASE, P_BASE, SHIFT_BASE, V1_VBASE = 0, 64, 96, 128
 LSUM, NSHIFT, KOFF, VOFF, DMA = 160, 162, 164, 172, 176
-S_KT, S_VT, S_KTILE, S_VTILE, S_LDS, S_CNT, S_TCNT = 60, 62, 64, 66, 68, 70, 71
-S_KLAST, S_VLAST, S_J, S_NFULL, S_LOPART, S_LO, S_TMP = 72, 74, 76, 77, 78, 79, 80
-S_KT6, S_VT6, S_LO1 = 82, 84, 86      # tile 6's addresses (the priming step's DMA); tile 1's first real row
-KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask temporary
+# The DMA cursor, s[64:79], is loaded whole from a piece descriptor (one s_load_dwordx16):
+S_D = 64
+S_KT, S_VT, S_KTILE, S_VTILE, S_KLAST, S_VLAST = 64, 66, 68, 70, 72, 74
+S_DREM, S_KSS, S_VSS, S_RSH = 76, 77, 78, 79
+# The mask cursor, s[80:83], from the descriptor's mask fields (one s_load_dwordx4):
+S_M = 80
+S_MREM, S_LOLAST, S_LOBASE = 80, 81, 82
+S_DPTR, S_MPTR, S_TMP = 84, 86, 88    # descriptor addresses of the two cursors; temporaries
+S_TCNT, S_CNT, S_LO, S_LOPREV, S_FLAG, S_LDS = 90, 91, 92, 93, 94, 95
+PIECE_BYTES = 128                     # one piece descriptor (32 dwords)
+MASK_OFF = 64                         # byte offset of its mask fields
+KB4, NEG_INF, MASK_X = 188, 189, 190      # 4 (lane / 32); -inf; mask / lane-offset temporary
 ALPHA = 180                           # v180: alpha (fp32), the logit factor of the fp32a variant
 LSUM_HI = 186                         # v186-v187: row sums of the high halves
+ROW, CK, CV = 181, 183, (185, 191)    # this lane's tile rows (DMA instructions 0, 1) and the
+                                      # byte offsets of its K and V chunks in those rows
 
 
 def areg(base, n=1):
@@ -145,11 +155,6 @@ EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it 
 BARRIER_AFTER = 2                     # PV MFMAs issued before a step's vmcnt wait and barrier
 DMA_WITH_KREAD = True                 # a K fragment read between each M0 write and its DMA
                                       # (DMAs first with s_nop 0, K reads after: same speed)
-ROWSUM = os.environ.get("FIXEDM_ROWSUM", "f32add")   # how the row sums add a word of P:
-                                      # "f32add": the two fp32 probabilities (two adds);
-                                      # "dot2": the word's two bf16 values, v_dot2_f32_bf16
-                                      # against (1, 1) (one op; the sum the PV product sees)
-ONES = 191                            # v191: bf16 pair (1.0, 1.0) for the dot2 row sums
 V_TR_PER_SLOT, V_TR_FIRST = 2, 0      # V^T transpose reads per S MFMA slot, from this slot on
                                       # (one per slot over all 16, or two per slot in the second
                                       # half, measured 0.5-0.6% slower)
@@ -186,11 +191,6 @@ def softmax_plan(buf):
         x = s_first(buf, n) + 2 * i
         pw = p_first(buf, n) + i
         cvt = add(f"v_cvt_pk_bf16_f32 v{pw}, v{x}, v{x + 1}", True, word_exps[w])
-        if ROWSUM == "dot2":
-            acc = (LSUM if i % 2 == 0 else LSUM_HI) + n
-            d2 = add(f"v_dot2_f32_bf16 v{acc}, v{pw}, v{ONES}, v{acc}", False, [cvt], acc=acc)
-            plain += [cvt, d2]
-            continue
         a_lo = add(f"v_add_f32 v{LSUM + n}, v{LSUM + n}, v{x}", True, [word_exps[w][0]], acc=LSUM + n)
         a_hi = add(f"v_add_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{x + 1}", True, [word_exps[w][1]],
                    acc=LSUM_HI + n)
@@ -243,7 +243,12 @@ def softmax_plan(buf):
 
 
 class Emitter:
-    """Collects the instruction lines and pads VALU reads of MFMA-written score registers."""
+    """Collects the instruction lines and pads VALU reads of MFMA-written score registers.
+
+    Forward branches (branch() to a label placed later with label()) merge the hazard state:
+    at the label each score buffer counts as written as recently as on any path that reaches
+    it.  A loop head (loop_head()) is reached by a back edge, so the tracking restarts there
+    as if an MFMA had just written both buffers."""
 
     MIN_WAIT = 16
 
@@ -251,6 +256,8 @@ class Emitter:
         self.lines = []
         self.count = 0                          # instructions emitted (each >= 1 wait state)
         self.s_written = {0: -10**9, 1: -10**9}  # index of the last MFMA writing each S buffer
+        self.pending = {}                       # forward label -> wait-state distances at branches
+        self.n_labels = 0
 
     def emit(self, text, reads_sbuf=None, writes_sbuf=None):
         if reads_sbuf is not None:
@@ -263,15 +270,129 @@ class Emitter:
             self.s_written[writes_sbuf] = self.count
         self.count += 1
 
+    def new_label(self):
+        self.n_labels += 1
+        return f"L_fixedm_f{self.n_labels}_%="
 
-def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = False):
-    """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).  A tail step clamps its
-    DMA to the chunk's last 32-key window and masks the keys of the next tile that are not
-    real, so steps past the chunk's end (and the partial last tile) run the same code.
+    def branch(self, op, label):
+        self.emit(f"{op} {label}")
+        self.pending.setdefault(label, []).append({b: self.count - w for b, w in self.s_written.items()})
 
-    first: the priming step t = 0 of a chunk (S(0) already issued): no PV product (there is
-    no tile -1), the DMA of tile 6 from s[S_KT6], S(1) masked from row s[S_LO1] on (tile 1
-    is the partial last tile when the chunk has 33..63 keys)."""
+    def label(self, label):
+        for dist in self.pending.pop(label, []):
+            for b in (0, 1):
+                self.s_written[b] = max(self.s_written[b], self.count - dist[b])
+        self.lines.append(f"{label}:")
+
+    def loop_head(self, label):
+        self.lines.append(f"{label}:")
+        self.s_written = {0: self.count - 1, 1: self.count - 1}
+
+    def seq(self, items):
+        """Emits a list of instructions, ("branch", op, label) and ("label", label) items."""
+        for it in items:
+            if isinstance(it, tuple):
+                if it[0] == "branch":
+                    self.branch(it[1], it[2])
+                else:
+                    self.label(it[1])
+            else:
+                self.emit(it)
+
+
+def lane_offsets():
+    """The DMA lane offsets of the DMA cursor's piece: row = max(row_i - rshift, 0) (rshift > 0
+    only for a chunk shorter than a tile, whose keys then fill the tile's last rows), offset
+    = row x row stride + this lane's 16-byte chunk in the row."""
+    out = []
+    for i in range(2):
+        out += [f"v_subrev_u32 v{MASK_X}, s{S_RSH}, v{ROW + i}",
+                f"v_max_i32 v{MASK_X}, 0, v{MASK_X}",
+                f"v_mul_lo_u32 v{DMA + i}, v{MASK_X}, s{S_KSS}",
+                f"v_add_u32 v{DMA + i}, v{DMA + i}, v{CK + i}",
+                f"v_mul_lo_u32 v{DMA + 2 + i}, v{MASK_X}, s{S_VSS}",
+                f"v_add_u32 v{DMA + 2 + i}, v{DMA + 2 + i}, v{CV[i]}"]
+    return out
+
+
+def stale_offsets(e):
+    """Recomputes the lane offsets if the DMA cursor has moved to another piece since they
+    were formed (s[S_FLAG] set; the descriptor load has been waited for)."""
+    lab = e.new_label()
+    return ([f"s_cmp_eq_u32 s{S_FLAG}, 0", ("branch", "s_cbranch_scc1", lab)] + lane_offsets()
+            + [f"s_mov_b32 s{S_FLAG}, 0", ("label", lab)])
+
+
+def dma_issue(stage):
+    """The four DMA instructions of this wave's share of a tile into LDS stage `stage`, each
+    after its M0 write (an instruction goes between them: the wait state M0 needs)."""
+    out = []
+    for i in range(2):
+        for base, vreg_i, sreg in ((stage * TILE_BYTES, DMA + i, S_KT),
+                                    (V_RING + stage * TILE_BYTES, DMA + 2 + i, S_VT)):
+            out.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", None,
+                        f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
+    return out
+
+
+ADVANCE = [[f"s_add_u32 s{S_KT}, s{S_KT}, s{S_KTILE}", f"s_addc_u32 s{S_KT + 1}, s{S_KT + 1}, s{S_KTILE + 1}"],
+           [f"s_add_u32 s{S_VT}, s{S_VT}, s{S_VTILE}", f"s_addc_u32 s{S_VT + 1}, s{S_VT + 1}, s{S_VTILE + 1}"]]
+LAST_WINDOW = [f"s_cselect_b64 s[{S_KT}:{S_KT + 1}], s[{S_KLAST}:{S_KLAST + 1}], s[{S_KT}:{S_KT + 1}]",
+               f"s_cselect_b64 s[{S_VT}:{S_VT + 1}], s[{S_VLAST}:{S_VLAST + 1}], s[{S_VT}:{S_VT + 1}]"]
+
+
+def dma_advance(e):
+    """After a DMA in a step that may reach a piece's end: the next tile's addresses, the
+    piece's last window for its last tile, and at the piece's end the next descriptor (its
+    values are used from the next step on, after that step's lgkmcnt wait)."""
+    lab = e.new_label()
+    return [list(ADVANCE[0]), list(ADVANCE[1]),
+            [f"s_sub_u32 s{S_DREM}, s{S_DREM}, 1", f"s_cmp_eq_u32 s{S_DREM}, 1"] + LAST_WINDOW,
+            [f"s_cmp_lg_u32 s{S_DREM}, 0", ("branch", "s_cbranch_scc1", lab),
+             f"s_add_u32 s{S_DPTR}, s{S_DPTR}, {PIECE_BYTES}", f"s_addc_u32 s{S_DPTR + 1}, s{S_DPTR + 1}, 0",
+             f"s_load_dwordx16 s[{S_D}:{S_D + 15}], s[{S_DPTR}:{S_DPTR + 1}], 0x0",
+             f"s_mov_b32 s{S_FLAG}, 1", ("label", lab)]]
+
+
+def mask_step(e: Emitter, fp32a: bool):
+    """The initial accumulator of the next S tile: -(m + c_i) (0 in fp32a) for its real keys and
+    -inf for the rest.  Real keys sit in rows >= lo: lo = the piece's lo_last for its last tile
+    (32 - rem for a partial last tile), lo_base for the others (0; 32 past the last piece).  The
+    32 initial-value registers are rewritten only when lo changes."""
+    l_next, l_same = e.new_label(), e.new_label()
+    e.emit(f"s_cmp_eq_u32 s{S_MREM}, 1")
+    e.emit(f"s_cselect_b32 s{S_LO}, s{S_LOLAST}, s{S_LOBASE}")
+    e.emit(f"s_sub_u32 s{S_MREM}, s{S_MREM}, 1")
+    e.emit(f"s_cmp_lg_u32 s{S_MREM}, 0")
+    e.branch("s_cbranch_scc1", l_next)
+    e.emit(f"s_add_u32 s{S_MPTR}, s{S_MPTR}, {PIECE_BYTES}")
+    e.emit(f"s_addc_u32 s{S_MPTR + 1}, s{S_MPTR + 1}, 0")
+    e.emit(f"s_load_dwordx4 s[{S_M}:{S_M + 3}], s[{S_MPTR}:{S_MPTR + 1}], {MASK_OFF}")
+    e.label(l_next)
+    e.emit(f"s_cmp_eq_u32 s{S_LO}, s{S_LOPREV}")
+    e.branch("s_cbranch_scc1", l_same)
+    e.emit(f"s_mov_b32 s{S_LOPREV}, s{S_LO}")
+    e.emit(f"v_sub_u32 v{MASK_X}, s{S_LO}, v{KB4}")         # lo - 4 (lane / 32)
+    for r in range(16):
+        key = 8 * (r >> 2) + (r & 3)                          # row of register r, lane half 0
+        e.emit(f"v_cmp_lt_i32_e32 vcc, {key}, v{MASK_X}")
+        for n in range(2):
+            init = "0" if fp32a else f"v{NSHIFT + n}"
+            e.emit(f"v_cndmask_b32_e32 v{SHIFT_BASE + 16 * n + r}, {init}, v{NEG_INF}, vcc")
+    e.emit("s_nop 1")
+    e.label(l_same)
+
+
+def step(e: Emitter, jj: int, mode: str, fp32a: bool = False):
+    """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).
+
+    mode "fast": every tile the step loads and scores lies inside one piece, not its last
+    tile, so the DMA address just advances and the keys are all real (the group's entry check
+    ensures it).  "slow": the DMA cursor may reach a piece's end (last window, next
+    descriptor) and the S tile's mask is formed.  "first": the priming step t = 0 (S(0)
+    already issued): no PV product (there is no tile -1), otherwise slow."""
+    first = mode == "first"
+    slow = mode != "fast"
     t_mod = 0 if first else 1 + jj
     cur = t_mod % 2            # parity of t: S(t), P(t), V(t) buffers
     prv = 1 - cur              # parity of t-1 (= parity of t+1)
@@ -279,7 +400,6 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
     stage_next = (t_mod + 1) % STAGES
     stage_dma = (t_mod + AHEAD) % STAGES
 
-    dma_offsets = [AHEAD]
     early = 0 if first else BARRIER_AFTER
     if early == 0:
         e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
@@ -302,36 +422,13 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
         # overwrite: let them take their operands first
         e.emit("s_nop 7")
         e.emit("s_nop 7")
-    # tail steps: a tile to load may be the partial last tile or lie past the end: its address
-    # is clamped to the start of the chunk's last 32-key window before the DMA reads it
-    clamp = []
-    for ptr, last in ((S_KT, S_KLAST), (S_VT, S_VLAST)):
-        clamp += [f"s_sub_u32 s{S_TMP}, s{last}, s{ptr}", f"s_subb_u32 s{S_TMP + 1}, s{last + 1}, s{ptr + 1}",
-                  f"s_cselect_b64 s[{ptr}:{ptr + 1}], s[{last}:{last + 1}], s[{ptr}:{ptr + 1}]"]
-    advance = [[f"s_add_u32 s{ptr}, s{ptr}, s{stride}", f"s_addc_u32 s{ptr + 1}, s{ptr + 1}, s{stride + 1}"]
-               for ptr, stride in ((S_KT, S_KTILE), (S_VT, S_VTILE))]
-    for di, off in enumerate(dma_offsets):
-        stage_dma = (t_mod + off) % STAGES
-        # the priming step loads tile 6 from its own registers (dead after it, clamped already)
-        from_t6 = first and off == AHEAD
-        kt_reg, vt_reg = (S_KT6, S_VT6) if from_t6 else (S_KT, S_VT)
-        if tail and not from_t6:
-            if di == 0:
-                for ins in clamp:
-                    e.emit(ins)
-            else:
-                extra.append(list(clamp))
-        for i in range(2):
-            for base, vreg_i, sreg in ((stage_dma * TILE_BYTES, DMA + i, kt_reg),
-                                        (V_RING + stage_dma * TILE_BYTES, DMA + 2 + i, vt_reg)):
-                between = kreads.pop(0) if DMA_WITH_KREAD and kreads else "s_nop 0"
-                extra.append([f"s_add_u32 m0, s{S_LDS}, {base + 1024 * i}", between,
-                              f"global_load_lds_dwordx4 v{vreg_i}, s[{sreg}:{sreg + 1}]"])
-        if not from_t6 and di + 1 < len(dma_offsets):     # the next tile to load
-            extra += [list(a) for a in advance]
+    if slow:
+        extra.append(stale_offsets(e))
+    for grp in dma_issue(stage_dma):
+        grp[1] = kreads.pop(0) if DMA_WITH_KREAD and kreads else "s_nop 0"
+        extra.append(grp)
     extra += [[kr] for kr in kreads]
-    if dma_offsets and not (first and len(dma_offsets) == 1):
-        extra += [list(a) for a in advance]
+    extra += dma_advance(e) if slow else [list(a) for a in ADVANCE]
 
     plan = softmax_plan(cur)
     slot = 0
@@ -361,31 +458,12 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
                     e.emit(f"s_waitcnt vmcnt({DMA_WAIT})")
                     e.emit("s_barrier")
                 if extra and i_mfma >= early:
-                    for ins in extra.pop(0):
-                        e.emit(ins)
+                    e.seq(extra.pop(0))
                 valu_slot()
                 i_mfma += 1
     assert not extra
-    if tail or first:
-        # Initial accumulator of S(t+1): -(m + c_i) for the real keys of tile j = t+1, -inf for
-        # the others.  Real keys of tile j sit in rows >= lo: lo = 0 for a full tile, 32 - rem
-        # for the partial last tile (loaded as the chunk's last 32-key window), 32 past the end.
-        if first:
-            e.emit(f"s_mov_b32 s{S_LO}, s{S_LO1}")
-        else:
-            e.emit(f"s_cmp_eq_u32 s{S_J}, s{S_NFULL}")
-            e.emit(f"s_cselect_b32 s{S_LO}, s{S_LOPART}, 32")
-            e.emit(f"s_cmp_lt_u32 s{S_J}, s{S_NFULL}")
-            e.emit(f"s_cselect_b32 s{S_LO}, 0, s{S_LO}")
-            e.emit(f"s_add_u32 s{S_J}, s{S_J}, 1")
-        e.emit(f"v_sub_u32 v{MASK_X}, s{S_LO}, v{KB4}")         # lo - 4 (lane / 32)
-        for r in range(16):
-            key = 8 * (r >> 2) + (r & 3)                          # row of register r, lane half 0
-            e.emit(f"v_cmp_lt_i32_e32 vcc, {key}, v{MASK_X}")
-            for n in range(2):
-                init = "0" if fp32a else f"v{NSHIFT + n}"
-                e.emit(f"v_cndmask_b32_e32 v{SHIFT_BASE + 16 * n + r}, {init}, v{NEG_INF}, vcc")
-        e.emit("s_nop 1")
+    if slow:
+        mask_step(e, fp32a)
     # S(t+1) = K(t+1) Q^T - (m + c), with the V(t) transpose reads in the first half
     e.emit("s_waitcnt lgkmcnt(0)")
     tr = [(st, m, h) for st in range(2) for m in range(4) for h in range(2)]
@@ -407,6 +485,24 @@ def step(e: Emitter, jj: int, tail: bool, first: bool = False, fp32a: bool = Fal
     assert slot == 32 and ti == 16
 
 
+def fast_check(e: Emitter):
+    """At a group boundary: the number of fast groups that can follow (the DMA cursor and the
+    mask cursor each keep >= 1 tile of their piece beyond them, the mask registers hold an
+    all-real tile and the cursors are not past the last piece), then into the fast loop if
+    any.  Lane offsets left stale by a descriptor switch are formed first."""
+    e.emit("s_waitcnt lgkmcnt(0)")
+    e.seq(stale_offsets(e))
+    e.emit(f"s_sub_u32 s{S_TMP}, s{S_DREM}, 1")
+    e.emit(f"s_sub_u32 s{S_TMP + 1}, s{S_MREM}, 1")
+    e.emit(f"s_min_u32 s{S_TMP}, s{S_TMP}, s{S_TMP + 1}")
+    e.emit(f"s_lshr_b32 s{S_CNT}, s{S_TMP}, 3")
+    e.emit(f"s_or_b32 s{S_TMP + 1}, s{S_LOPREV}, s{S_LOBASE}")
+    e.emit(f"s_cmp_eq_u32 s{S_TMP + 1}, 0")
+    e.emit(f"s_cselect_b32 s{S_CNT}, s{S_CNT}, 0")
+    e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
+    e.emit("s_cbranch_scc1 L_fixedm_fast_%=")
+
+
 def generate_variant(fp32a: bool) -> str:
     """One assembly function: the bf16(alpha q) loop, or (fp32a) the loop that applies alpha
     in fp32 with an FMA per score."""
@@ -417,10 +513,27 @@ def generate_variant(fp32a: bool) -> str:
     e.emit(f"v_mov_b32 v{NEG_INF}, 0xff800000")
     e.emit(f"v_mov_b32 v{LSUM_HI}, 0")
     e.emit(f"v_mov_b32 v{LSUM_HI + 1}, 0")
+    e.emit(f"s_load_dwordx16 s[{S_D}:{S_D + 15}], s[{S_DPTR}:{S_DPTR + 1}], 0x0")
+    e.emit(f"s_load_dwordx4 s[{S_M}:{S_M + 3}], s[{S_DPTR}:{S_DPTR + 1}], {MASK_OFF}")
+    e.emit(f"s_mov_b64 s[{S_MPTR}:{S_MPTR + 1}], s[{S_DPTR}:{S_DPTR + 1}]")
+    e.emit(f"s_mov_b32 s{S_LOPREV}, 0")
+    e.emit(f"s_mov_b32 s{S_FLAG}, 1")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
-    # Priming: S(0) from stage 0 (tile 0 is whole whenever this block runs), then step t = 0
-    # (P(0), the row sums of tile 0, S(1), V(0)'s fragments, the DMA of tile 6).
+    # Prologue: tiles 0 .. 5 into stages 0 .. 5, then tile 0 waited for and met at a barrier.
+    for tile in range(AHEAD):
+        e.emit("s_waitcnt lgkmcnt(0)")
+        e.seq(stale_offsets(e))
+        for grp in dma_issue(tile):
+            grp[1] = "s_nop 0"
+            e.seq(grp)
+        for grp in dma_advance(e):
+            e.seq(grp)
+    e.emit(f"s_waitcnt vmcnt({(AHEAD - 1) * 4})")
+    e.emit("s_barrier")
+    # S(0) from stage 0 with tile 0's mask, then the priming step t = 0 (P(0), the row sums of
+    # tile 0, S(1), V(0)'s fragments, the DMA of tile 6).
+    mask_step(e, fp32a)
     for kk in range(8):
         e.emit(f"ds_read_b128 {k_reg(0, kk)}, v{KOFF + kk} offset:0")
     e.emit("s_waitcnt lgkmcnt(0)")
@@ -430,30 +543,34 @@ def generate_variant(fp32a: bool) -> str:
             src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
             e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(0, kk)}, {q_reg(n, kk)}, {src_c}",
                    writes_sbuf=0)
-    step(e, 0, tail=False, first=True, fp32a=fp32a)
-    e.emit(f"s_cmp_eq_u32 s{S_CNT}, 0")
-    e.emit("s_cbranch_scc1 L_fixedm_tail_%=")
-    # fast groups: every tile they prefetch and every S tile they compute is a full one
-    e.lines.append("L_fixedm_group_%=:")
-    # the loop's back edge: the previous group's last S MFMAs may be a few instructions away
-    e.s_written = {0: e.count - 1, 1: e.count - 1}
+    step(e, 0, "first", fp32a=fp32a)
+    fast_check(e)
+    # slow groups: steps t = 1 .. n_tiles, one at a time, leaving after step t = n_tiles (the PV
+    # product of the last tile); at each group boundary the fast check
+    e.loop_head("L_fixedm_slow_%=")
     for jj in range(STAGES):
-        step(e, jj, tail=False, fp32a=fp32a)
-    e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
-    e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
-    e.emit("s_cbranch_scc1 L_fixedm_group_%=")
-    # tail steps: clamped DMA and masked keys, through step t = n_tiles (the PV product of the
-    # chunk's last tile): s[S_TCNT] counts the steps left, and the loop leaves after the step
-    # that brings it to 0, wherever that falls in the unrolled group of 8
-    e.lines.append("L_fixedm_tail_%=:")
-    e.s_written = {0: e.count - 1, 1: e.count - 1}
-    for jj in range(STAGES):
-        step(e, jj, tail=True, fp32a=fp32a)
+        step(e, jj, "slow", fp32a=fp32a)
         e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
         e.emit(f"s_cmp_eq_u32 s{S_TCNT}, 0")
         e.emit("s_cbranch_scc1 L_fixedm_end_%=")
-    e.emit("s_branch L_fixedm_tail_%=")
-    e.lines.append("L_fixedm_end_%=:")
+    fast_check(e)
+    e.emit("s_branch L_fixedm_slow_%=")
+    # fast groups of 8 steps
+    e.loop_head("L_fixedm_fast_%=")
+    for jj in range(STAGES):
+        step(e, jj, "fast", fp32a=fp32a)
+    e.emit(f"s_sub_u32 s{S_DREM}, s{S_DREM}, 8")
+    e.emit(f"s_sub_u32 s{S_MREM}, s{S_MREM}, 8")
+    e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 8")
+    e.emit(f"s_sub_u32 s{S_CNT}, s{S_CNT}, 1")
+    e.emit(f"s_cmp_lg_u32 s{S_CNT}, 0")
+    e.emit("s_cbranch_scc1 L_fixedm_fast_%=")
+    e.emit(f"s_cmp_eq_u32 s{S_DREM}, 1")
+    for ins in LAST_WINDOW:
+        e.emit(ins)
+    e.emit("s_branch L_fixedm_slow_%=")
+    e.loop_head("L_fixedm_end_%=")
+    assert not e.pending
     e.emit(f"v_add_f32 v{LSUM}, v{LSUM}, v{LSUM_HI}")
     e.emit(f"v_add_f32 v{LSUM + 1}, v{LSUM + 1}, v{LSUM_HI + 1}")
     e.emit("s_waitcnt lgkmcnt(0)")
@@ -466,8 +583,7 @@ def generate_variant(fp32a: bool) -> str:
         for m in range(4):
             outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
-             f'"+{{s[{S_KT}:{S_KT + 1}]}}"(kt)', f'"+{{s[{S_VT}:{S_VT + 1}]}}"(vt)',
-             f'"+{{s{S_CNT}}}"(groups)', f'"+{{s{S_TCNT}}}"(tail_steps)', f'"+{{s{S_J}}}"(next_tile)']
+             f'"+{{s[{S_DPTR}:{S_DPTR + 1}]}}"(pieces)', f'"+{{s{S_TCNT}}}"(n_tiles)']
     ins = []
     for n in range(2):
         for kk in range(8):
@@ -475,22 +591,21 @@ def generate_variant(fp32a: bool) -> str:
     ins += [f'"{{v{NSHIFT}}}"(nshift[0])', f'"{{v{NSHIFT + 1}}}"(nshift[1])']
     ins += [f'"{{v{KOFF + kk}}}"(koff[{kk}])' for kk in range(8)]
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
-    ins += [f'"{{v{DMA + i}}}"(dma[{i}])' for i in range(4)]
+    ins += [f'"{{v{ROW + i}}}"(lane[{i}])' for i in range(2)]
+    ins += [f'"{{v{CK + i}}}"(lane[{2 + i}])' for i in range(2)]
+    ins += [f'"{{v{CV[i]}}}"(lane[{4 + i}])' for i in range(2)]
     ins += [f'"{{v{KB4}}}"(kb4)']
     if fp32a:
         ins += [f'"{{v{ALPHA}}}"(alpha)']
-    if ROWSUM == "dot2":
-        ins += [f'"{{v{ONES}}}"(0x3f803f80u)']
-    ins += [f'"{{s[{S_KT6}:{S_KT6 + 1}]}}"(kt6)', f'"{{s[{S_VT6}:{S_VT6 + 1}]}}"(vt6)', f'"{{s{S_LO1}}}"(lo1)']
-    ins += [f'"{{s[{S_KTILE}:{S_KTILE + 1}]}}"(ktile)', f'"{{s[{S_VTILE}:{S_VTILE + 1}]}}"(vtile)',
-            f'"{{s{S_LDS}}}"(lds_wave)', f'"{{s[{S_KLAST}:{S_KLAST + 1}]}}"(k_last)',
-            f'"{{s[{S_VLAST}:{S_VLAST + 1}]}}"(v_last)', f'"{{s{S_NFULL}}}"(n_full)', f'"{{s{S_LOPART}}}"(lo_part)']
+    ins += [f'"{{s{S_LDS}}}"(lds_wave)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 64)] + [f"v{i}" for i in range(P_BASE, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
-            + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
+            + [f"v{DMA + i}" for i in range(4)] + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
             + [f"v{NEG_INF}", f"v{MASK_X}"]
             + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
-            + [f"s{S_LO}", f"s{S_TMP}", f"s{S_TMP + 1}", "vcc", "scc", "memory"])
+            + [f"s{i}" for i in range(S_D, S_M + 4)] + [f"s{i}" for i in range(S_MPTR, S_TMP + 2)]
+            + [f"s{i}" for i in (S_CNT, S_LO, S_LOPREV, S_FLAG)]
+            + ["m0", "vcc", "scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
     def join(items):
@@ -502,22 +617,18 @@ def generate_variant(fp32a: bool) -> str:
             "the query fragments are bf16(alpha q) and the S chain starts from -(m + c_i), so S is "
             "the exponent")
     return f"""// {what}.
-// The fixed-m pass over a chunk of >= 2 tiles: the priming step (S(0), then step t = 0: P(0),
-// S(1), V(0)'s fragments, the DMA of tile 6), `groups` fast groups of 8 pipelined 32-key
-// steps, then `tail_steps` (>= 1) tail steps, so steps t = 1 .. 8 groups + tail_steps run;
-// step t turns S(t) into P(t), adds V(t-1) P(t-1) to O and computes S(t+1).  On entry: tiles
-// 0 .. 5 issued and tile 0 in LDS (waited and met at a barrier), kt6 / vt6 = the addresses of
-// tile 6 and kt / vt those of tile 7 (each clamped to the chunk's last 32-key window), lo1 =
-// tile 1's first real row, next_tile = 8 groups + 2 (the tile whose S the first tail step
-// computes).  Keys past the chunk's last tile are masked (p = 0); with tail_steps = n_tiles -
-// 8 groups the last step completes the PV product of the last tile.  On exit every LDS read
-// has completed.
+// The whole fixed-m pass of one work item over its n_tiles (>= 1) tiles of 32 keys, the
+// tiles of its chunk pieces in order (the piece descriptor list at `pieces`, ended by a
+// terminator): the prologue (tiles 0 .. 5 loaded, tile 0 waited for and met at a barrier),
+// S(0), the priming step t = 0, then steps t = 1 .. n_tiles in groups of 8, each turning S(t)
+// into P(t), adding V(t-1) P(t-1) to O and computing S(t+1); the last step completes the PV
+// product of the last tile.  Keys past the last tile are masked (p = 0).  The LDS ring and
+// its barriers continue across piece boundaries.  On exit every LDS read has completed;
+// DMAs of tiles past the end may still be in flight.
 __device__ __attribute__((always_inline)) inline void {name}(
-    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8],
-    float (&lsum)[2], const float (&nshift)[2], const uint32_t (&koff)[8], const uint32_t (&voff)[4],
-    const uint32_t (&dma)[4], uint32_t kb4, uint64_t kt6, uint64_t vt6, uint32_t lo1, uint64_t kt, uint64_t vt,
-    uint64_t ktile, uint64_t vtile, uint32_t lds_wave, uint64_t k_last, uint64_t v_last, uint32_t n_full,
-    uint32_t lo_part, uint32_t groups, uint32_t tail_steps, uint32_t next_tile{", float alpha" if fp32a else ""}) {{
+    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], float (&lsum)[2], const float (&nshift)[2],
+    const uint32_t (&koff)[8], const uint32_t (&voff)[4], const uint32_t (&lane)[6], uint32_t kb4,
+    uint64_t pieces, uint32_t n_tiles, uint32_t lds_wave{", float alpha" if fp32a else ""}) {{
   asm volatile(
 {body}
       : {join(outs)}

@@ -100,7 +100,7 @@ typedef struct {
   int64_t heads;         /* H >= 1; MHA only (K/V have the same H as Q) */
   int64_t head_dim;      /* D: 128 (bf16 and fp32) or 64 (fp32 only) */
   int64_t sq;            /* resident query rows, 1 .. 2^30; B x H x ceil(sq / 256) < 2^31 */
-  int64_t sk_total;      /* N: real keys over all chunks, 1 .. 2^38 (unpadded, [UR] Summary) */
+  int64_t sk_total;      /* N: real keys over all chunks, 1 .. 2^38 (bf16: 2^35), unpadded ([UR] Summary) */
   int64_t q_block;       /* rows per shift/eligibility block: positive multiple of 64 */
   float softmax_scale;   /* s; 0 selects fp32(1/sqrt(D)) ([CM] Interface table) */
   int32_t center;        /* fixedm_center */

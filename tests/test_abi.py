@@ -61,6 +61,8 @@ def test_sizes_of_valid_problems():
     assert r.scratch - r.u_row >= 40 * 18900 * 8 and all(o % 256 == 0 for o in (r.m_row, r.q2_row, r.u_row))
     assert F.workspace_bytes(_p(shift="row")) == ws
     assert F.bounds_bytes(_p(batch=3, heads=21845, sq=1, sk_total=2, q_block=64)) > 0   # the most heads
+    assert F.bounds_bytes(_p(sk_total=2**35)) > 0
+    assert F.bounds_bytes(_p(dtype="fp32", head_dim=64, center="none", sk_total=2**38)) > 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,6 +85,7 @@ def test_sizes_of_valid_problems():
     (dict(batch=1, heads=65536), -3),         # batch x heads above 65,535
     (dict(batch=2**40, heads=2**40), -3),     # no overflow in the product check
     (dict(sk_total=2**38 + 1), -3),
+    (dict(sk_total=2**35 + 1), -3),           # bf16: a launch's key tiles are counted in 32 bits
 ])
 def test_invalid_problems(kw, code):
     p = _p(**kw)

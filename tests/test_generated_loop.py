@@ -65,16 +65,29 @@ def test_exp_readers_sit_behind_their_exp(gen):
 
 def test_mfma_results_are_waited_for(gen):
     """Every VALU read of a score register comes >= 16 wait states (an instruction is one, s_nop N is N+1)
-    after the MFMA that last wrote that score buffer; at a label the tracking restarts as if an MFMA
-    had just written both buffers, as the generator assumes."""
+    after the MFMA that last wrote that score buffer.  A forward-branch target (L_fixedm_fN) takes the
+    closest write over the paths that reach it; at any other label (a loop head) the tracking restarts
+    as if an MFMA had just written both buffers, as the generator assumes."""
     lines = _body(gen.generate())
     written = {}
     count = 0
+    pending = {}
     s_regs = {0: set(range(gen.s_first(0, 0), gen.s_first(0, 0) + 32)),
               1: set(range(gen.s_first(1, 0), gen.s_first(1, 0) + 32))}
     for ln in lines:
-        if ln.endswith(":"):            # a label: the generator restarts its tracking conservatively
-            written = {b: count - 1 for b in (0, 1)}
+        if ln.endswith(":"):
+            lab = ln[:-1]
+            if re.match(r"L_fixedm_f\d+_%=$", lab):
+                for dist in pending.pop(lab, []):
+                    for b, d in dist.items():
+                        written[b] = max(written.get(b, -10**9), count - d)
+            else:
+                written = {b: count - 1 for b in (0, 1)}
+            continue
+        m = re.match(r"s_c?branch\S* (L_fixedm_f\d+_%=)$", ln)
+        if m:
+            count += 1
+            pending.setdefault(m.group(1), []).append({b: count - w for b, w in written.items()})
             continue
         if ln.startswith("v_mfma") and re.match(r"v_mfma\S* v\[(\d+):", ln):
             lo = int(re.match(r"v_mfma\S* v\[(\d+):", ln).group(1))
@@ -87,3 +100,4 @@ def test_mfma_results_are_waited_for(gen):
                     if r in regs and b in written:
                         assert count - written[b] - 1 >= 16, ln
         count += int(ln.split()[1]) + 1 if ln.startswith("s_nop") else 1
+    assert not pending
