@@ -46,15 +46,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str, fused: bool, fallback: str, q_block_default: bool):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None
-    when the kernel source has changed since the counters were taken."""
+    when this run is not the launch the counters were taken on (another workload, the
+    per-chunk calls, a fallback mode, another q_block) or the kernel source has changed
+    since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if not (fused and fallback == "none" and q_block_default
+            and str(t.get("workload", "")).split(" ")[0] == workload):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -300,14 +305,14 @@ def main():
             "sq": wl.sq, "sk": wl.sk, "chunks": list(wl.chunks), "ring_order": order,
             "q_block": q_block, "centering": wl.center, "eligible_fraction": elig_frac,
             "fallback": args.fallback, "loud_qblocks": loud_blocks,
-            "step": ("bounds + attn_fwd_final over the 4 ring chunks (bf16 out written by the "
-                     "attention launch)" if fused else
-                     "bounds + 4 x attn_fwd (one per ring chunk) + finalize(bf16 out)"),
+            "step": (f"bounds + attn_fwd_final over the {len(ks)} ring chunks (output written by "
+                     "the attention launch)" if fused else
+                     f"bounds + {len(ks)} x attn_fwd (one per ring chunk) + finalize"),
         },
         "roofline": {
             "kernel": "attn_bf16_d128_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, fused, args.fallback, q_block == wl.q_block),
             "launch_ms": round(attn_avg, 4), "launches_per_step": n_attn,
             "flops_per_launch": per_launch_flops,
             "timed_call": ("fixedm_attn_fwd_final: the attention launch plus the finalize of "

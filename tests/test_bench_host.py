@@ -24,13 +24,27 @@ def test_more_than_one_gpu_exits_with_a_message(argv, env):
 def test_traffic_follows_the_kernel_source_hash(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic() is None                              # no file
+    run = ("wan720p-rank-share-bf16", True, "none", True)
+    assert bench.measured_traffic(*run) is None                          # no file
     f.write_text("not json")
-    assert bench.measured_traffic() is None
-    f.write_text(json.dumps({"kernel_source_sha256_16": "0" * 16, "hbm_bytes_per_launch": 123}))
-    assert bench.measured_traffic() is None                              # counters of another kernel
-    f.write_text(json.dumps({"kernel_source_sha256_16": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123}))
-    assert bench.measured_traffic() == 123
+    assert bench.measured_traffic(*run) is None
+    rec = {"workload": "wan720p-rank-share-bf16 (B=1, ...)", "hbm_bytes_per_launch": 123}
+    f.write_text(json.dumps(dict(rec, kernel_source_sha256_16="0" * 16)))
+    assert bench.measured_traffic(*run) is None                          # counters of another kernel
+    f.write_text(json.dumps(dict(rec, kernel_source_sha256_16=bench.kernel_source_hash())))
+    assert bench.measured_traffic(*run) == 123
+
+
+def test_traffic_only_for_the_profiled_launch(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(json.dumps({"workload": "wan720p-rank-share-bf16 (B=1, ...)", "hbm_bytes_per_launch": 123,
+                             "kernel_source_sha256_16": bench.kernel_source_hash()}))
+    assert bench.measured_traffic("wan720p-rank-share-bf16", True, "none", True) == 123
+    assert bench.measured_traffic("wan-block-bf16", True, "none", True) is None      # another workload
+    assert bench.measured_traffic("wan720p-rank-share-bf16", False, "none", True) is None   # per-chunk calls
+    assert bench.measured_traffic("wan720p-rank-share-bf16", True, "all", True) is None     # fallback mode
+    assert bench.measured_traffic("wan720p-rank-share-bf16", True, "none", False) is None   # other q_block
 
 
 def test_committed_traffic_record_is_well_formed():
