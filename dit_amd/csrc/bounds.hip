@@ -357,20 +357,22 @@ __device__ inline const T* key_row(const BoundsArgs& a, int b, int h, int64_t j,
   return p;
 }
 
-// |x| <= 256 for every element of a 16-byte piece (NaN fails).
+// |x| <= 256 for every element of a 16-byte piece (NaN fails).  Branch free: a short-circuit
+// test branches on divergent lanes.
 __device__ inline bool piece_ok(uint4 w, const uint16_t*) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-  bool ok = true;
+  uint32_t big = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ok = ok && (u[i] & 0x7fffu) <= 0x4380u && ((u[i] >> 16) & 0x7fffu) <= 0x4380u;
-  return ok;
+  for (int i = 0; i < 4; ++i)
+    big |= (uint32_t)((u[i] & 0x7fffu) > 0x4380u) | (uint32_t)(((u[i] >> 16) & 0x7fffu) > 0x4380u);
+  return big == 0;
 }
 __device__ inline bool piece_ok(uint4 w, const float*) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-  bool ok = true;
+  uint32_t big = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ok = ok && (u[i] & 0x7fffffffu) <= 0x43800000u;
-  return ok;
+  for (int i = 0; i < 4; ++i) big |= (uint32_t)((u[i] & 0x7fffffffu) > 0x43800000u);
+  return big == 0;
 }
 
 __device__ inline unsigned long long wave_max_u64(unsigned long long v) {
@@ -462,6 +464,112 @@ __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
   }
 }
 
+// bf16 K2 and V check (D = 128), one persistent workgroup per compute unit.  Each wave takes a
+// contiguous range of work items (b, h, block of up to 64 keys of one chunk; ordered by (b, h),
+// so a wave keeps its head and its k_mean for many items).  The K rows of an item arrive in
+// the wave's LDS stage by direct global->LDS loads, four whole 256-byte rows per instruction
+// (lane L of instruction i: row 4 i + L / 16, the 16-byte chunk (L mod 16) ^ (row mod 16) so
+// that each lane reads its own row back bank-conflict free); the V rows come the same way
+// into registers and are checked where they land.  Two stages per wave: the loads of item k+1
+// are issued before the fp64 sums of item k.  (One key per lane reading its own rows from
+// HBM was bound by its load pattern: each instruction touched 64 rows a key stride apart.)
+__global__ __launch_bounds__(256, 1) void knorm_vcheck_lds_kernel(BoundsArgs a) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) uint4 kst[4][2][64 * 16];
+  __shared__ double kmd[4][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t n_kb = 0;
+  for (int c = 0; c < a.n_chunks; ++c) n_kb += (a.ch[c].len + 63) / 64;
+  const int64_t n_items = (int64_t)a.B * a.H * n_kb;
+  const int64_t G = (int64_t)gridDim.x * 4, g = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t i0 = n_items * g / G, i1 = n_items * (g + 1) / G;
+  if (i0 >= i1) return;
+  // item -> (b, h), chunk, block of the chunk, rows
+  struct Item {
+    int64_t bh;
+    const uint16_t* k0;
+    const uint16_t* v0;
+    int64_t kss, vss;
+    int nrows;
+  };
+  const auto locate = [&](int64_t item) {
+    Item it;
+    it.bh = item / n_kb;
+    int64_t kb = item % n_kb;
+    int c = 0;
+    while (kb >= (a.ch[c].len + 63) / 64) {
+      kb -= (a.ch[c].len + 63) / 64;
+      ++c;
+    }
+    const ChunkDesc& cd = a.ch[c];
+    const int64_t b = it.bh / a.H, h = it.bh % a.H;
+    it.k0 = reinterpret_cast<const uint16_t*>(cd.k) + b * cd.k_sb + kb * 64 * cd.k_ss + h * cd.k_sh;
+    it.v0 = reinterpret_cast<const uint16_t*>(cd.v) + b * cd.v_sb + kb * 64 * cd.v_ss + h * cd.v_sh;
+    it.kss = cd.k_ss;
+    it.vss = cd.v_ss;
+    it.nrows = cd.len - kb * 64 < 64 ? (int)(cd.len - kb * 64) : 64;
+    return it;
+  };
+  // issues item `it`'s K rows into stage `st` and its V rows into vv (rows past nrows repeat
+  // row nrows - 1: every load is in bounds)
+  const auto issue = [&](const Item& it, int st, uint4 (&vv)[16]) {
+    const int q = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int r = 4 * i + q;
+      r = r < it.nrows ? r : it.nrows - 1;
+      const uint16_t* src = it.k0 + r * it.kss + 8 * (pc ^ ((4 * i + q) & 15));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&kst[wave][st][64 * i], 16, 0,
+                                       0);
+      vv[i] = *reinterpret_cast<const uint4*>(it.v0 + r * it.vss + 8 * pc);
+    }
+  };
+  int bad = 0;
+  int64_t cur_bh = -1;
+  unsigned long long best = 0ull;
+  uint4 vv[16];
+  Item it = locate(i0);
+  issue(it, 0, vv);
+  for (int64_t item = i0; item < i1; ++item) {
+    const int st = (int)((item - i0) & 1);
+    if (it.bh != cur_bh) {   // a new head: flush the previous head's max, stage this one's k_mean
+      if (cur_bh >= 0) {
+        const unsigned long long m = wave_max_u64(best);
+        if (lane == 0) atomicMax(a.k2 + cur_bh, m);
+      }
+      best = 0ull;
+      cur_bh = it.bh;
+      for (int d = lane; d < D; d += 64) kmd[wave][d] = (double)a.k_mean[cur_bh * D + d];
+    }
+    // this item's loads have landed (the compiler waits for them before the LDS reads below)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bad |= (int)!piece_ok(vv[i], (const uint16_t*)nullptr);
+    RowRegs<uint16_t> kr;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) kr.p[p] = kst[wave][st][lane * 16 + (p ^ (lane & 15))];
+    const int nrows = it.nrows;
+    if (item + 1 < i1) {       // the next item's loads, in flight during this item's sums
+      it = locate(item + 1);
+      issue(it, st ^ 1, vv);
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int gq = 0; gq < D / 32; ++gq) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double t = (double)kr.elem(32 * gq + i) - kmd[wave][32 * gq + i];
+        ss = ss + t * t;
+      }
+    }
+    const unsigned long long v = lane < nrows ? (unsigned long long)__double_as_longlong(ss) : 0ull;
+    best = v > best ? v : best;
+  }
+  const unsigned long long m = wave_max_u64(best);
+  if (lane == 0) atomicMax(a.k2 + cur_bh, m);
+  if (__any(bad) && lane == 0) atomicOr(a.v_bad, 1);
+}
+
 // Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2: work item (block of 64
 // positions, head group), as in the K kernel; 64 positions lie in one q-block (q_block is
 // a multiple of 64).
@@ -544,7 +652,12 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
   const int64_t qitems = (a.Sq + 63) / 64 * n_hq;
   const int64_t cap = (int64_t)1 << 20;    // grid-stride loops beyond this many workgroups
   const dim3 gq((unsigned)(qitems < cap ? qitems : cap), (unsigned)a.B);
-  knorm_vcheck_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), (unsigned)(a.B * a.H)), 256, 0, s>>>(a);
+  if constexpr (sizeof(T) == 2) {
+    const int cus = device_cus();
+    knorm_vcheck_lds_kernel<<<(unsigned)(cus > 0 ? cus : 256), 256, 0, s>>>(a);
+  } else {
+    knorm_vcheck_kernel<T><<<dim3((unsigned)((a.N + 255) / 256), (unsigned)(a.B * a.H)), 256, 0, s>>>(a);
+  }
   if constexpr (sizeof(T) == 4) {            // fp32: D = 64 (16 pieces a row) or 128 (32)
     if (a.D == 128) {
       qnorm_kernel<T, 32><<<gq, 64 * W, 0, s>>>(a);
