@@ -453,6 +453,8 @@ AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspa
   a.elig = reinterpret_cast<const uint8_t*>(bbase + lay.elig);
   a.u = reinterpret_cast<const double*>(bbase + lay.u);
   a.k_mean = reinterpret_cast<const float*>(bbase + lay.k_mean);
+  a.v_bad = reinterpret_cast<const int32_t*>(bbase + lay.v_bad);
+  a.log2_n = bounds->log2_n;
   a.alpha = bounds->alpha;
   a.alpha64 = (double)p.softmax_scale * kLog2e;
   a.acc = reinterpret_cast<float*>(wbase + wl.acc);

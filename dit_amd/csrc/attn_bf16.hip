@@ -14,33 +14,31 @@
 //
 // Design (MI355X):
 //   * Workgroup = 4 waves x 64 query rows = 256 rows of one (b, h).  Each wave keeps its 64
-//     query rows resident in VGPRs as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16).
+//     query rows resident (in AGPRs) as the B operand of S^T = K Q^T
+//     (v_mfma_f32_32x32x16_bf16).
 //   * In the 32x32 accumulator layout each lane owns ONE query column and 16 keys, so the
-//     fixed-m exponent e = alpha*S - (m + c_i) is one FMA with a per-lane constant, the
-//     row sum is a per-lane running fp32 sum of the fp32 probabilities, and the exp2'd
-//     scores, packed to bf16, are
-//     already the B operand of O^T += V^T P^T with no transpose (the K-stationary layout of
-//     [CM]).  The matching key order on the V^T operand comes from the gfx950 LDS transpose
-//     read ds_read_b64_tr_b16.
+//     per-query shift is a per-lane constant, the row sum is a per-lane running fp32 sum of
+//     the fp32 probabilities, and the exp2'd scores, packed to bf16, are already the B operand
+//     of O^T += V^T P^T with no transpose (the K-stationary layout of [CM]).  The matching key
+//     order on the V^T operand comes from the gfx950 LDS transpose read ds_read_b64_tr_b16.
 //   * K/V tiles of 32 keys stream through an 8-stage LDS ring (K ring in the first 64 KB,
 //     V ring in the next 64 KB) with direct global->LDS loads (global_load_lds_dwordx4)
 //     issued six tiles ahead; no VGPR staging.  Tiles are XOR-swizzled so both the K row
-//     reads and the V transpose reads are bank-conflict free.  The main loop is unrolled
-//     over the 8 stages, so every LDS address is a per-lane base plus an immediate.
-//   * Fixed-m body, software-pipelined per 32-key tile t: the MFMAs of O += V(t-1) P(t-1)
-//     are independent of the VALU work exp2(alpha S(t) - shift), so the matrix cores and
-//     the vector ALUs overlap within one wave.
+//     reads and the V transpose reads are bank-conflict free.
+//   * A work item (a query tile, or part of a split one) runs all the 32-key tiles of its
+//     chunk pieces as one pipeline, in one generated assembly block: the matrix cores and
+//     the vector ALUs overlap within one wave, and the ring, its barriers and the
+//     accumulators continue across chunk boundaries.
 //   * The body is chosen per wave from its q-block's eligibility byte and bound U: the
-//     fixed-m assembly loop on bf16(alpha q) (U <= kR17MaxU), the fixed-m assembly loop that
-//     applies alpha in fp32 (eligible, U above it), or online softmax (ineligible).  A
-//     wave-uniform branch.
-//   * One launch folds one K/V chunk (one ring step) into the workspace.
-//   * Ragged KV tails: rows past a chunk's end are clamped to its last row on load and
-//     their probabilities forced to zero; no padding copies.  Query rows past Sq are
+//     fixed-m loop on bf16(alpha q) (U <= kR17MaxU), the fixed-m loop that applies alpha in
+//     fp32 (eligible, U above it), or the online-softmax loop (ineligible).  All three take
+//     the same loads and barriers, so the waves of a workgroup may run different bodies.
+//   * Ragged KV tails: a chunk's partial last tile is loaded as its last 32-key window and
+//     the keys already counted are masked; no padding copies.  Query rows past Sq are
 //     clamped on load and land in padded workspace rows that finalize never reads.
-//   * Persistent workgroups (one per compute unit) take query tiles from per-XCD queues:
+//   * Persistent workgroups (one per compute unit) take work items from per-XCD queues:
 //     each XCD works through consecutive tiles of the same heads (sharing the K/V stream in
-//     its L2) and, once its queue is empty, takes work from the back of the others.
+//     its L2) and, once its queue is empty, takes work from the others.
 #include <math.h>
 
 #include "fixedm_internal.h"
@@ -49,12 +47,10 @@ namespace fixedm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kD = 128;
 constexpr int kKT = 32;                        // keys per pipeline tile
@@ -62,7 +58,6 @@ constexpr int kRowBytes = kD * 2;              // 256 bytes per key row
 constexpr int kTileBytes = kKT * kRowBytes;    // 8 KB: K (or V) of one tile
 constexpr int kStages = 8;                     // LDS ring depth in tiles
 constexpr int kAhead = kStages - 2;            // tiles in flight ahead of the current one
-constexpr int kLoadsPerTile = 4;               // global->LDS instructions per wave per tile
 constexpr int kVRing = kStages * kTileBytes;   // the V ring starts after the K ring
 constexpr int kLdsBytes = 2 * kStages * kTileBytes;   // 128 KB
 // Largest block bound U for which the fixed-m body takes its logits from bf16(alpha q).  The
@@ -88,32 +83,7 @@ __device__ inline void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One 16-byte-per-lane global->LDS load of a tile row's chunk: lane L's 16 bytes come from
-// sbase + max(row - rsh, 0) * stride + chunk and land at LDS byte lds + 16 L.  Written as
-// inline asm so the compiler's wait-count pass does not treat every later LDS read as
-// aliasing an in-flight load (it would insert vmcnt(0) and drain the ring); the ring's vmcnt
-// waits are explicit instead.  The lane offset is formed inside the block from loop-invariant
-// inputs: the compiler takes a register an asm load reads as busy until the load completes,
-// so rewriting a register that holds an offset would make it wait on the vector memory
-// counter (which also counts the ring's loads) and drain the ring.  The destination is passed
-// as an LDS pointer (with a memory clobber) so the compiler knows the asm writes the shared
-// buffer.  M0 carries the wave-uniform LDS address; no compiler-generated instruction here
-// reads M0.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-__device__ inline void dma16_row(uint32_t row, uint32_t chunk, uint32_t rsh, uint32_t stride, uint64_t sbase,
-                                 lds_u8* lds) {
-  uint32_t off;
-  asm volatile(
-      "v_subrev_u32 %0, %3, %1\n\t"
-      "v_max_i32 %0, 0, %0\n\t"
-      "v_mul_lo_u32 %0, %0, %4\n\t"
-      "v_add_u32 %0, %0, %2\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "global_load_lds_dwordx4 %0, %6"
-      : "=&v"(off)
-      : "v"(row), "v"(chunk), "s"(rsh), "s"(stride), "s"(lds), "s"(sbase)
-      : "memory");
-}
 
 __device__ inline uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -160,225 +130,33 @@ __device__ inline DmaLane dma_lane(int wave, int lane) {
   return d;
 }
 
-// The key tiles of one work item are the 32-key tiles of its chunk pieces in order, read
-// from a piece descriptor list (pieces.h) that the prep kernel writes before each launch.
-// The lists are read through the constant address space, so the reads are scalar loads:
-// a vector load here would make the compiler wait on the vector memory counter, which also
-// counts the ring's loads in flight, and drain the ring.
-typedef __attribute__((address_space(4))) const uint32_t desc_word;
-__device__ inline uint32_t desc_at(const uint32_t* d, int i) { return ((const desc_word*)d)[i]; }
-__device__ inline uint64_t desc_u64(const uint32_t* d, int i) {
-  return ((uint64_t)desc_at(d, i + 1) << 32) | desc_at(d, i);
-}
-
-// Load side of the ring as the compiled body runs it (the assembly loop keeps the same
-// cursor in SGPRs): the next tile's addresses, the tiles left in the piece, this lane's
-// offsets into the piece's rows.
-struct DmaCursor {
-  const uint32_t* d;
-  uint64_t kt, vt, ktile, vtile, klast, vlast;
-  uint32_t rem, kss, vss, rsh;
-};
-__device__ inline void dma_load(DmaCursor& c) {
-  const uint32_t* d = c.d;
-  c.kt = desc_u64(d, 0);
-  c.vt = desc_u64(d, 2);
-  c.ktile = desc_u64(d, 4);
-  c.vtile = desc_u64(d, 6);
-  c.klast = desc_u64(d, 8);
-  c.vlast = desc_u64(d, 10);
-  c.rem = desc_at(d, 12);
-  c.kss = desc_at(d, 13);
-  c.vss = desc_at(d, 14);
-  c.rsh = desc_at(d, 15);
-}
-// Issues this wave's share of the next tile (2 KB of K rows, 2 KB of V rows) into LDS stage
-// `stage`, then advances: the piece's last tile is its last window, and past the piece's
-// end the cursor moves to the next descriptor.
-__device__ __attribute__((always_inline)) void dma_next(uint8_t* smem, DmaCursor& c, const DmaLane& ln, int wave,
-                                                        int stage) {
-  lds_u8* kl = (lds_u8*)(smem + stage * kTileBytes);
-  lds_u8* vl = (lds_u8*)(smem + kVRing + stage * kTileBytes);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = __builtin_amdgcn_readfirstlane(1024 * (2 * wave + i));
-    dma16_row(ln.row[i], ln.ck[i], c.rsh, c.kss, c.kt, kl + blk);
-    dma16_row(ln.row[i], ln.cv[i], c.rsh, c.vss, c.vt, vl + blk);
-  }
-  c.kt += c.ktile;
-  c.vt += c.vtile;
-  if (--c.rem == 1) {
-    c.kt = c.klast;
-    c.vt = c.vlast;
-  } else if (c.rem == 0) {
-    c.d += kPieceWords;
-    dma_load(c);
-  }
-}
-
-// Score side: the first real row of each tile in turn.
-struct MaskCursor {
-  const uint32_t* d;
-  uint32_t rem, lo_last, lo_base;
-};
-__device__ inline void mask_load(MaskCursor& m) {
-  m.rem = desc_at(m.d, 16);
-  m.lo_last = desc_at(m.d, 17);
-  m.lo_base = desc_at(m.d, 18);
-}
-__device__ inline int mask_next(MaskCursor& m) {
-  const int lo = (int)(m.rem == 1 ? m.lo_last : m.lo_base);
-  if (--m.rem == 0) {
-    m.d += kPieceWords;
-    mask_load(m);
-  }
-  return lo;
-}
-
-// Key index within the tile held by accumulator register r of this lane.
-__device__ inline int tile_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
-
-// S^T(tile) = K(tile) Q^T for one 32-key tile and two 32-query tiles: 16 MFMAs.  Rows of the
-// tile before `lo` (keys that are not real) start from -inf (p = 0), the others from 0.
-__device__ __attribute__((always_inline)) void compute_s(const uint8_t* smem, const LdsOff& g, int stage,
-                                                         const bf16x8 (&qf)[2][8], f32x16 (&s)[2], int lo,
-                                                         int hh) {
-  const uint8_t* ks = smem + stage * kTileBytes;
-  bf16x8 kf[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(ks + g.koff[kk]);
-  f32x16 c;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) c[r] = tile_key(r, hh) >= lo ? 0.0f : -INFINITY;
-  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0][0], c, 0, 0, 0);
-  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[1][0], c, 0, 0, 0);
-#pragma unroll
-  for (int kk = 1; kk < 8; ++kk) {
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], s[1], 0, 0, 0);
-  }
-}
-
-// O^T += V(tile)^T P(tile)^T: four 32-dim tiles x two 16-key steps x two query tiles.  For
-// each 16-key step st and 32-dim tile m a lane holds one dim and 8 keys in the P register
-// order, from two LDS transpose reads (each 4 keys x 16 dims to a 16-lane group).
-__device__ __attribute__((always_inline)) void compute_pv(const uint8_t* smem, const LdsOff& g, int stage,
-                                                          const bf16x8 (&p)[2][2], f32x16 (&o)[2][4]) {
-  const uint8_t* vs = smem + stage * kTileBytes;
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint8_t* a0 = vs + g.voff[m] + 4096 * st;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 2048));
-      const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[0][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[0][st], o[0][m], 0, 0, 0);
-      o[1][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[1][st], o[1][m], 0, 0, 0);
-    }
-  }
-}
-
-// The fixed-m pass of a work item, written out instruction by instruction (generated).
+// The three passes of a work item over its key tiles, written out instruction by instruction
+// (generated): fixed_loop_asm, fixed_loop_fp32a_asm and online_loop_asm.
 #include "fixed_loop.inc"
 
-// Packs 8 probabilities to bf16 (round to nearest even; the B operand of the PV product)
-// and adds the fp32 probabilities to the row sum, key by key.
-__device__ __attribute__((always_inline)) bf16x8 pack8_sum(const f32x16& e, int base, float& lsum) {
-  bf16x2 w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[i] = __builtin_convertvector((f32x2){e[base + 2 * i], e[base + 2 * i + 1]}, bf16x2);
-    lsum += e[base + 2 * i];
-    lsum += e[base + 2 * i + 1];
-  }
-  bf16x8 r;
-  __builtin_memcpy(&r, w, 16);
-  return r;
+// How far (base 2) the online body lets a row's maximum run ahead of its reference before it
+// raises the reference (word 19 of every piece descriptor): s = clamp(127 - ceil(log2 N) - ceil(log2 max|v|), 0, 8), so that
+// N 2^s max|v| <= 2^127 and the accumulators stay finite wherever those of exact online
+// softmax (s = 0) do.  max|v| is 256 when the V check passed, else the largest |v| it
+// recorded (non-finite: s = 0; the output is then not finite anyway).
+__device__ inline float online_slack(const AttnArgs& a) {
+  const uint32_t vb = (uint32_t)__builtin_amdgcn_readfirstlane(*a.v_bad);
+  if (vb >= 0x7f800000u) return 0.0f;
+  const int log2_v = vb == 0 ? 8 : (int)(vb >> 23) - 127 + ((vb & 0x7fffffu) != 0 ? 1 : 0);
+  const int s = 127 - a.log2_n - log2_v;
+  return (float)(s < 0 ? 0 : s > 8 ? 8 : s);
 }
 
-// Online-softmax probabilities of one tile (the fallback body).  The running reference r of
-// each query row (base 2) is raised to the row's max only when some row of the wave's query
-// tile exceeds its r by more than kRescaleSlack; the accumulator and the row sum are then
-// rescaled by 2^(r_old - r_new) (one wave-uniform branch).  Between raises the probabilities
-// 2^(alpha s - r) stay below 2^kRescaleSlack, well inside the bf16 and fp32 ranges, and O / l
-// does not depend on which r was used, so most tiles skip the 64 accumulator multiplies.
-// Masked rows arrive as -inf scores (every tile this body visits has at least one real key).
-constexpr float kRescaleSlack = 8.0f;
-__device__ __attribute__((always_inline)) void softmax_online(const f32x16 (&s)[2], bf16x8 (&p)[2][2],
-                                                              float (&lsum)[2], float (&rmax)[2],
-                                                              f32x16 (&o)[2][4], float alpha) {
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float am = alpha * mx;
-    if (__builtin_amdgcn_ballot_w64(am > rmax[n] + kRescaleSlack) != 0) {
-      const float rn = fmaxf(rmax[n], am);
-      const float f = __builtin_amdgcn_exp2f(rmax[n] - rn);
-      rmax[n] = rn;
-      lsum[n] *= f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) o[n][m] *= f;
-    }
-    f32x16 e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(alpha, s[n][r], -rmax[n]));
-    p[n][0] = pack8_sum(e, 0, lsum[n]);
-    p[n][1] = pack8_sum(e, 8, lsum[n]);
-  }
-}
+// A work item's pass over its key tiles, in the assembly block of its body: fixed-m with
+// bf16(alpha q) fragments (kFixedR17), fixed-m with the logit factor applied in fp32
+// (kFixedF32), or online softmax (kOnline; shift[] returns each query row's reference r,
+// -inf before the first key).  Every body takes the same loads and barriers.
+enum Body { kFixedR17, kFixedF32, kOnline };
 
-// The online-softmax pass of a work item (the fallback body), on the same ring as the
-// assembly loop: the prologue's six tile loads and barrier, then per tile t a barrier
-// (tile t+1 landed, stage t-2 free), the load of tile t+6, and the tile's scores,
-// probabilities and PV product; then one more barrier and load for the assembly loop's
-// step t = n_tiles.  The waves of a workgroup thus meet at the same barriers and load the
-// same tiles whichever body each runs.
-__device__ __attribute__((always_inline)) void run_online(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
-                                                          int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
-                                                          float (&lsum)[2], float (&rmax)[2], int wave, int lane) {
-  const int hh = lane >> 5;
-  const LdsOff g = lds_offsets(lane);
-  const DmaLane ln = dma_lane(wave, lane);
-  // The compiler does not count the ring's loads (inline asm): a vector memory access of its
-  // own still in flight when the loop starts (a spill reload, say) would make it wait on the
-  // counter inside the loop, every iteration, and drain the ring.  Waiting here, before the
-  // first ring load, leaves it nothing to wait for.
-  wait_vmcnt<0>();
-  DmaCursor dc;
-  dc.d = pieces;
-  dma_load(dc);
-  MaskCursor mc;
-  mc.d = pieces;
-  mask_load(mc);
-#pragma unroll 1
-  for (int t = 0; t < kAhead; ++t) dma_next(smem, dc, ln, wave, t);
-  wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();   // tile 0 has landed (this wave's part)
-  barrier();
-#pragma unroll 1
-  for (int t = 0; t <= n_tiles; ++t) {
-    wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
-    barrier();
-    dma_next(smem, dc, ln, wave, (t + kAhead) % kStages);
-    if (t == n_tiles) break;
-    const int stage = t % kStages;
-    f32x16 s[2];
-    bf16x8 p[2][2];
-    compute_s(smem, g, stage, qf, s, mask_next(mc), hh);
-    softmax_online(s, p, lsum, rmax, o, a.alpha);
-    compute_pv(smem, g, stage, p, o);
-  }
-}
-
-// The fixed-m pass of a work item: the assembly loop, with bf16(alpha q) fragments (r17) or
-// with the logit factor applied in fp32.
-__device__ __attribute__((always_inline)) void run_fixed(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
-                                                         int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
-                                                         float (&lsum)[2], const float (&shift)[2], bool r17,
-                                                         int wave, int lane) {
+__device__ __attribute__((always_inline)) void run_pass(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
+                                                        int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
+                                                        float (&lsum)[2], float (&shift)[2], Body body, int wave,
+                                                        int lane) {
   // The lane's offsets are formed from an id the compiler cannot hoist above the assembly
   // block, so they are not kept live (and spilled) around it.
   int tid = wave * 64 + lane;
@@ -394,14 +172,21 @@ __device__ __attribute__((always_inline)) void run_fixed(const AttnArgs& a, uint
   for (int m = 0; m < 4; ++m) voff[m] = lds0 + g.voff[m];
   const uint32_t lane6[6] = {ln.row[0], ln.row[1], ln.ck[0], ln.ck[1], ln.cv[0], ln.cv[1]};
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds0 + 2048 * w);
-  const float nshift[2] = {-shift[0], -shift[1]};
   const uint64_t list = uniform_u64((uint64_t)(uintptr_t)pieces);
   const uint32_t nt = __builtin_amdgcn_readfirstlane((uint32_t)n_tiles);
-  if (r17)
-    fixed_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, (uint32_t)(4 * (l >> 5)), list, nt, lds_wave);
+  const uint32_t kb4 = (uint32_t)(4 * (l >> 5));
+  if (body == kOnline) {
+    float nshift[2] = {INFINITY, INFINITY};
+    online_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha);
+    shift[0] = -nshift[0];
+    shift[1] = -nshift[1];
+    return;
+  }
+  const float nshift[2] = {-shift[0], -shift[1]};
+  if (body == kFixedR17)
+    fixed_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave);
   else
-    fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, lane6, (uint32_t)(4 * (l >> 5)), list, nt, lds_wave,
-                         a.alpha);
+    fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha);
 }
 
 // One work item: a whole query tile (all tiles of the launch's chunks), or part p of a split
@@ -500,8 +285,8 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   }
   if (n_tiles > 0) {
     const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
-    if (fixed) run_fixed(a, smem, pieces, n_tiles, qf, o, lsum, shift, r17, wave, lane);
-    else run_online(a, smem, pieces, n_tiles, qf, o, lsum, shift, wave, lane);
+    run_pass(a, smem, pieces, n_tiles, qf, o, lsum, shift, fixed ? (r17 ? kFixedR17 : kFixedF32) : kOnline, wave,
+             lane);
     wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is reused
     barrier();
   }
@@ -723,7 +508,8 @@ __device__ void write_piece_list(const AttnArgs& a, int64_t bh, int list) {
                     (uint64_t)(uintptr_t)ch.v + (uint64_t)(2 * (b * ch.v_sb + h * ch.v_sh)), ch.k_ss, ch.v_ss,
                     ch.len};
   };
-  build_piece_list(a.ptable + (bh * kPieceLists + list) * kPieceSlots * kPieceWords, chunk, a.n_chunks, v0, v1);
+  build_piece_list(a.ptable + (bh * kPieceLists + list) * kPieceSlots * kPieceWords, chunk, a.n_chunks, v0, v1,
+                   __float_as_uint(online_slack(a)));
 }
 
 // Before each launch.  Block 0 clears the queue counters and lists the slow whole tiles (in

@@ -357,22 +357,38 @@ __device__ inline const T* key_row(const BoundsArgs& a, int b, int h, int64_t j,
   return p;
 }
 
-// |x| <= 256 for every element of a 16-byte piece (NaN fails).  Branch free: a short-circuit
-// test branches on divergent lanes.
-__device__ inline bool piece_ok(uint4 w, const uint16_t*) {
+// The largest |x| of a 16-byte piece as fp32 bits: the magnitude bits order finite values by
+// size and put inf and NaN above them all.  Branch free (a short-circuit test branches on
+// divergent lanes).  Every |x| <= 256 exactly when the result is <= kV256Bits.
+constexpr uint32_t kV256Bits = 0x43800000u;   // 256.0f
+__device__ inline uint32_t piece_maxabs(uint4 w, const uint16_t*) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-  uint32_t big = 0;
+  uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    big |= (uint32_t)((u[i] & 0x7fffu) > 0x4380u) | (uint32_t)(((u[i] >> 16) & 0x7fffu) > 0x4380u);
-  return big == 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = u[i] & 0x7fffu, hi = (u[i] >> 16) & 0x7fffu;
+    m = max(m, max(lo, hi));
+  }
+  return m << 16;
 }
-__device__ inline bool piece_ok(uint4 w, const float*) {
+__device__ inline uint32_t piece_maxabs(uint4 w, const float*) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-  uint32_t big = 0;
+  uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) big |= (uint32_t)((u[i] & 0x7fffffffu) > 0x43800000u);
-  return big == 0;
+  for (int i = 0; i < 4; ++i) m = max(m, u[i] & 0x7fffffffu);
+  return m;
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Records a V magnitude over the bound: v_bad keeps the fp32 bits of the largest |v| seen
+// (positive as an int32), so it is nonzero exactly when some |v| > 256 or is not a number.
+__device__ inline void note_v_max(const BoundsArgs& a, uint32_t wave_max) {
+  if (wave_max > kV256Bits) atomicMax(a.v_bad, (int32_t)wave_max);
 }
 
 __device__ inline unsigned long long wave_max_u64(unsigned long long v) {
@@ -424,14 +440,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
   __shared__ double km[128];
   __shared__ unsigned long long wmax[4];
-  __shared__ int wbad[4];
+  __shared__ uint32_t wvmax[4];
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
   const int64_t j = (int64_t)blockIdx.x * 256 + tid;
   if (tid < a.D) km[tid] = (double)a.k_mean[(int64_t)bh * a.D + tid];
   __syncthreads();
   unsigned long long best = 0ull;
-  int bad = 0;
+  uint32_t vmax = 0;
   if (j < a.N) {
     const int c = find_chunk(a, j);
     RowRegs<T> kr, vr;
@@ -448,19 +464,19 @@ __global__ __launch_bounds__(256) void knorm_vcheck_kernel(BoundsArgs a) {
     best = (unsigned long long)__double_as_longlong(s);
 #pragma unroll
     for (int i = 0; i < RowRegs<T>::kPieces; ++i)
-      if (i < a.D * (int)sizeof(T) / 16) bad |= !piece_ok(vr.p[i], (const T*)nullptr);
+      if (i < a.D * (int)sizeof(T) / 16) vmax = max(vmax, piece_maxabs(vr.p[i], (const T*)nullptr));
   }
   best = wave_max_u64(best);
-  const int any_bad = __any(bad) ? 1 : 0;
+  vmax = wave_max_u32(vmax);
   const int w = tid >> 6;
-  if ((tid & 63) == 0) { wmax[w] = best; wbad[w] = any_bad; }
+  if ((tid & 63) == 0) { wmax[w] = best; wvmax[w] = vmax; }
   __syncthreads();
   if (tid == 0) {
     unsigned long long m = wmax[0];
-    int vb = wbad[0];
-    for (int i = 1; i < 4; ++i) { m = wmax[i] > m ? wmax[i] : m; vb |= wbad[i]; }
+    uint32_t vm = wvmax[0];
+    for (int i = 1; i < 4; ++i) { m = wmax[i] > m ? wmax[i] : m; vm = max(vm, wvmax[i]); }
     atomicMax(a.k2 + bh, m);
-    if (vb) atomicOr(a.v_bad, 1);
+    note_v_max(a, vm);
   }
 }
 
@@ -524,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void knorm_vcheck_lds_kernel(BoundsArgs a) 
       vv[i] = *reinterpret_cast<const uint4*>(it.v0 + r * it.vss + 8 * pc);
     }
   };
-  int bad = 0;
+  uint32_t vmax = 0;
   int64_t cur_bh = -1;
   unsigned long long best = 0ull;
   uint4 vv[16];
@@ -543,7 +559,7 @@ __global__ __launch_bounds__(256, 1) void knorm_vcheck_lds_kernel(BoundsArgs a) 
     }
     // this item's loads have landed (the compiler waits for them before the LDS reads below)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bad |= (int)!piece_ok(vv[i], (const uint16_t*)nullptr);
+    for (int i = 0; i < 16; ++i) vmax = max(vmax, piece_maxabs(vv[i], (const uint16_t*)nullptr));
     RowRegs<uint16_t> kr;
 #pragma unroll
     for (int p = 0; p < 16; ++p) kr.p[p] = kst[wave][st][lane * 16 + (p ^ (lane & 15))];
@@ -567,7 +583,8 @@ __global__ __launch_bounds__(256, 1) void knorm_vcheck_lds_kernel(BoundsArgs a) 
   }
   const unsigned long long m = wave_max_u64(best);
   if (lane == 0) atomicMax(a.k2 + cur_bh, m);
-  if (__any(bad) && lane == 0) atomicOr(a.v_bad, 1);
+  vmax = wave_max_u32(vmax);
+  if (lane == 0) note_v_max(a, vmax);
 }
 
 // Q2[b,h,beta] = max over the block's real rows of sum_d q_d^2: work item (block of 64

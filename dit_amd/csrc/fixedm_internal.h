@@ -150,6 +150,8 @@ struct AttnArgs {
   const uint8_t* elig;
   const double* u;        // per-block bound U [B, H, nQB]
   const float* k_mean;
+  const int32_t* v_bad;   // 0, or the fp32 bits of the largest |v| when some |v| > 256
+  int32_t log2_n;         // ceil(log2 N), N the keys of the whole run
   float alpha;       // fp32(scale * log2 e)
   double alpha64;    // fp64 scale * log2 e (fp32 path)
   float* acc;

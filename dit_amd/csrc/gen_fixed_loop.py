@@ -97,6 +97,12 @@ ALPHA = 180                           # v180: alpha (fp32), the logit factor of 
 LSUM_HI = 186                         # v186-v187: row sums of the high halves
 ROW, CK, CV = 181, 183, (185, 191)    # this lane's tile rows (DMA instructions 0, 1) and the
                                       # byte offsets of its K and V chunks in those rows
+# online variant: per query tile n a row-max / rescale-factor register A and a scratch B,
+# the two tiles' growth masks (s96:97) and the accumulator-rescale flag (s98)
+OA, OB = (192, 194), (193, 195)
+S_GROW, S_RESC = 96, 98
+S_SLACK = S_M + 3                     # s83, descriptor word 19: the running reference is raised
+                                      # when a row max exceeds it by more than this (fp32, base 2)
 
 
 def areg(base, n=1):
@@ -150,6 +156,12 @@ def shift_reg(n):
 #    larger elsewhere; the last slot takes what is left.
 EXP_QUOTA = [1] * 20 + [2] + [1] * 10 + [0]
 SIMPLE_CAP = [1, 1, 1, 1, 3, 3, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 2, 2, 2, 2, 0, 2, 2, 2, 4, 4, 4, 4, 4, 4, 4, 4]
+# online variant: the first ONLINE_PRE slots hold the row maxima and the rescale test, so the 32
+# exps go to the slots after them (two in five of those slots)
+ONLINE_PRE = 4
+ONLINE_EXP_QUOTA = [0] * ONLINE_PRE + [2 if s in (10, 14, 20, 25, 29) else 1 for s in range(ONLINE_PRE, 31)] + [0]
+ONLINE_SIMPLE_CAP = [0] * ONLINE_PRE + [1, 1, 1, 1, 1, 1, 3, 3, 3, 3, 0, 3, 3, 3, 0, 3, 2, 2, 2, 2, 0, 2, 2,
+                                         2, 2, 0, 4, 4]
 DEP_DIST = 2                          # a plain VALU op sits >= 2 instructions after its producer
 EXP_GAP = 2                           # ... and >= 2 MFMA slots after an exp it reads
 BARRIER_AFTER = 2                     # PV MFMAs issued before a step's vmcnt wait and barrier
@@ -160,7 +172,7 @@ V_TR_PER_SLOT, V_TR_FIRST = 2, 0      # V^T transpose reads per S MFMA slot, fro
                                       # half, measured 0.5-0.6% slower)
 
 
-def softmax_plan(buf):
+def softmax_plan(buf, online=False):
     """The 80 VALU instructions that turn S(t) (scores buffer `buf`) into P(t) and the row
     sums, placed into the 32 MFMA slots of a step.  Returns 32 lists of (text, whether the
     instruction reads the scores buffer).
@@ -200,12 +212,14 @@ def softmax_plan(buf):
     last_acc = {}
     plan = [[] for _ in range(32)]
     ei, pending = 0, list(plain)
+    quota, caps = (ONLINE_EXP_QUOTA, ONLINE_SIMPLE_CAP) if online else (EXP_QUOTA, SIMPLE_CAP)
+    assert len(quota) == 32 and len(caps) == 32 and sum(quota) == 32
     for s in range(32):
-        for _ in range(EXP_QUOTA[s]):
+        for _ in range(quota[s]):
             pos[exps[ei]] = (s, len(plan[s]))
             plan[s].append(exps[ei])
             ei += 1
-        cap = SIMPLE_CAP[s] if s < 31 else len(pending)
+        cap = caps[s] if s < 31 else len(pending)
         dist = DEP_DIST if s < 31 else 1
         took = 0
         while took < cap:
@@ -258,6 +272,7 @@ class Emitter:
         self.s_written = {0: -10**9, 1: -10**9}  # index of the last MFMA writing each S buffer
         self.pending = {}                       # forward label -> wait-state distances at branches
         self.n_labels = 0
+        self.deferred = []                      # out-of-line blocks, emitted after the epilogue
 
     def emit(self, text, reads_sbuf=None, writes_sbuf=None):
         if reads_sbuf is not None:
@@ -355,6 +370,7 @@ def dma_advance(e):
 
 
 def mask_step(e: Emitter, fp32a: bool):
+    # fp32a: the S chain starts from 0 (the fp32-factor and online variants)
     """The initial accumulator of the next S tile: -(m + c_i) (0 in fp32a) for its real keys and
     -inf for the rest.  Real keys sit in rows >= lo: lo = the piece's lo_last for its last tile
     (32 - rem for a partial last tile), lo_base for the others (0; 32 past the last piece).  The
@@ -383,14 +399,84 @@ def mask_step(e: Emitter, fp32a: bool):
     e.label(l_same)
 
 
-def step(e: Emitter, jj: int, mode: str, fp32a: bool = False):
+def online_pre(cur):
+    """Online variant, per query tile n: the row maximum of S(t) over the tile's 32 keys (16 in
+    this lane, 16 in lane ^ 32, exchanged by v_permlane32_swap), scaled by alpha, and the test
+    alpha max > r + slack (r = -NSHIFT, the running reference; slack in s[S_SLACK]); the two tiles' tests
+    are or-ed into s[S_GROW].  Four lists, one per leading MFMA slot; each entry is (text,
+    whether it reads the scores buffer)."""
+    groups = []
+    for n in range(2):
+        x, a, b = s_first(cur, n), OA[n], OB[n]
+        chain = [(f"v_max3_f32 v{a}, v{x}, v{x + 1}, v{x + 2}", True)]
+        for i in range(3, 15, 2):
+            chain.append((f"v_max3_f32 v{a}, v{a}, v{x + i}, v{x + i + 1}", True))
+        chain.append((f"v_max_f32 v{a}, v{a}, v{x + 15}", True))
+        tail = [(f"v_mov_b32 v{b}, v{a}", False), ("s_nop 1", False),
+                (f"v_permlane32_swap_b32 v{a}, v{b}", False), ("s_nop 1", False),
+                (f"v_max_f32 v{a}, v{a}, v{b}", False),
+                (f"v_mul_f32 v{a}, v{a}, v{ALPHA}", False),
+                (f"v_add_f32 v{b}, v{a}, v{NSHIFT + n}", False),
+                (f"v_cmp_lt_f32_e32 vcc, s{S_SLACK}, v{b}", False)]
+        tail.append((f"s_mov_b64 s[{S_GROW}:{S_GROW + 1}], vcc", False) if n == 0 else
+                    (f"s_or_b64 s[{S_GROW}:{S_GROW + 1}], s[{S_GROW}:{S_GROW + 1}], vcc", False))
+        groups += [chain, tail]
+    return groups
+
+
+def online_raise(e: Emitter):
+    """Online variant, after the tests: if some row grew, raise every row's reference to
+    max(r, alpha max), rescale its row sums by f = 2^(r_old - r_new) now and, through s[S_RESC],
+    its accumulators at the end of the step (after this step's PV products, made with the old
+    reference).  OA[n] keeps f until then.  With r = -inf (NSHIFT = +inf) f is 0."""
+    lab = e.new_label()
+    e.branch("s_cbranch_scc0", lab)
+    for n in range(2):
+        a, b = OA[n], OB[n]
+        e.emit(f"v_min_f32 v{b}, v{NSHIFT + n}, -v{a}")
+        e.emit(f"v_sub_f32 v{a}, v{b}, v{NSHIFT + n}")
+        e.emit(f"v_exp_f32 v{a}, v{a}")
+        e.emit(f"v_mov_b32 v{NSHIFT + n}, v{b}")
+        e.emit("s_nop 1")
+        e.emit(f"v_mul_f32 v{LSUM + n}, v{LSUM + n}, v{a}")
+        e.emit(f"v_mul_f32 v{LSUM_HI + n}, v{LSUM_HI + n}, v{a}")
+    e.emit(f"s_mov_b32 s{S_RESC}, 1")
+    e.label(lab)
+
+
+def online_rescale_acc(e: Emitter):
+    """Online variant, end of a step: when s[S_RESC] is set, multiplies the accumulators of
+    query tile n by OA[n] (the PV MFMAs of this step have long completed: the 16 score MFMAs
+    came after them).  The rare block is out of line, after the epilogue, so the loop's code
+    stays contiguous; it branches back to the step's end.  It touches no score register, so
+    the hazard state after it is the state at the branch."""
+    block, back = e.new_label(), e.new_label()
+    e.emit(f"s_cmp_lg_u32 s{S_RESC}, 0")
+    e.emit(f"s_cbranch_scc1 {block}")
+    e.lines.append(f"{back}:")
+    body = ["s_nop 7", "s_nop 7"]
+    tmp = (MASK_X, OB[0])
+    k = 0
+    for n in range(2):
+        for i in range(64):
+            reg = O_BASE + 64 * n + i
+            t = tmp[k % 2]
+            body += [f"v_accvgpr_read_b32 v{t}, a{reg}", f"v_mul_f32 v{t}, v{t}, v{OA[n]}",
+                     f"v_accvgpr_write_b32 a{reg}, v{t}"]
+            k += 1
+    body += [f"s_mov_b32 s{S_RESC}, 0", "s_nop 2", f"s_branch {back}"]
+    e.deferred.append((block, body))
+
+
+def step(e: Emitter, jj: int, mode: str, fp32a: bool = False, online: bool = False):
     """Step jj of an unrolled group: tile t with t = 1 + jj (mod 8).
 
     mode "fast": every tile the step loads and scores lies inside one piece, not its last
     tile, so the DMA address just advances and the keys are all real (the group's entry check
     ensures it).  "slow": the DMA cursor may reach a piece's end (last window, next
     descriptor) and the S tile's mask is formed.  "first": the priming step t = 0 (S(0)
-    already issued): no PV product (there is no tile -1), otherwise slow."""
+    already issued): no PV product (there is no tile -1), otherwise slow.  online: the
+    online-softmax variant (fp32a arithmetic with a running reference, see online_pre)."""
     first = mode == "first"
     slow = mode != "fast"
     t_mod = 0 if first else 1 + jj
@@ -430,13 +516,19 @@ def step(e: Emitter, jj: int, mode: str, fp32a: bool = False):
     extra += [[kr] for kr in kreads]
     extra += dma_advance(e) if slow else [list(a) for a in ADVANCE]
 
-    plan = softmax_plan(cur)
+    plan = softmax_plan(cur, online=online)
+    pre = online_pre(cur) if online else []
     slot = 0
 
     def valu_slot():
         nonlocal slot
+        if slot < len(pre):
+            for text, reads in pre[slot]:
+                e.emit(text, reads_sbuf=cur if reads else None)
+            if slot == len(pre) - 1:
+                online_raise(e)
         for text, reads in plan[slot]:
-            if fp32a and text.startswith("v_exp_f32"):
+            if (fp32a or online) and text.startswith("v_exp_f32"):
                 # fp32a: the exponent is alpha S - (m + c_i), one FMA right before the exp
                 r = int(text.split()[1].rstrip(",")[1:])
                 n = (r - s_first(cur, 0)) // 16
@@ -463,7 +555,7 @@ def step(e: Emitter, jj: int, mode: str, fp32a: bool = False):
                 i_mfma += 1
     assert not extra
     if slow:
-        mask_step(e, fp32a)
+        mask_step(e, fp32a or online)
     # S(t+1) = K(t+1) Q^T - (m + c), with the V(t) transpose reads in the first half
     e.emit("s_waitcnt lgkmcnt(0)")
     tr = [(st, m, h) for st in range(2) for m in range(4) for h in range(2)]
@@ -483,6 +575,8 @@ def step(e: Emitter, jj: int, mode: str, fp32a: bool = False):
                     ti += 1
             valu_slot()
     assert slot == 32 and ti == 16
+    if online:
+        online_rescale_acc(e)
 
 
 def fast_check(e: Emitter):
@@ -503,13 +597,16 @@ def fast_check(e: Emitter):
     e.emit("s_cbranch_scc1 L_fixedm_fast_%=")
 
 
-def generate_variant(fp32a: bool) -> str:
-    """One assembly function: the bf16(alpha q) loop, or (fp32a) the loop that applies alpha
-    in fp32 with an FMA per score."""
+def generate_variant(variant: str) -> str:
+    """One assembly function: "r17", the fixed-m loop on bf16(alpha q); "fp32a", the fixed-m
+    loop that applies alpha in fp32 with an FMA per score; "online", the online-softmax loop
+    (fp32a arithmetic against a running reference raised lazily, see online_pre)."""
+    fp32a = variant == "fp32a"
+    online = variant == "online"
     e = Emitter()
     for n in range(2):
         for i in range(16):
-            e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, {'0' if fp32a else f'v{NSHIFT + n}'}")
+            e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, {'0' if fp32a or online else f'v{NSHIFT + n}'}")
     e.emit(f"v_mov_b32 v{NEG_INF}, 0xff800000")
     e.emit(f"v_mov_b32 v{LSUM_HI}, 0")
     e.emit(f"v_mov_b32 v{LSUM_HI + 1}, 0")
@@ -518,6 +615,8 @@ def generate_variant(fp32a: bool) -> str:
     e.emit(f"s_mov_b64 s[{S_MPTR}:{S_MPTR + 1}], s[{S_DPTR}:{S_DPTR + 1}]")
     e.emit(f"s_mov_b32 s{S_LOPREV}, 0")
     e.emit(f"s_mov_b32 s{S_FLAG}, 1")
+    if online:
+        e.emit(f"s_mov_b32 s{S_RESC}, 0")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
     # Prologue: tiles 0 .. 5 into stages 0 .. 5, then tile 0 waited for and met at a barrier.
@@ -533,7 +632,7 @@ def generate_variant(fp32a: bool) -> str:
     e.emit("s_barrier")
     # S(0) from stage 0 with tile 0's mask, then the priming step t = 0 (P(0), the row sums of
     # tile 0, S(1), V(0)'s fragments, the DMA of tile 6).
-    mask_step(e, fp32a)
+    mask_step(e, fp32a or online)
     for kk in range(8):
         e.emit(f"ds_read_b128 {k_reg(0, kk)}, v{KOFF + kk} offset:0")
     e.emit("s_waitcnt lgkmcnt(0)")
@@ -543,13 +642,13 @@ def generate_variant(fp32a: bool) -> str:
             src_c = shift_reg(n) if kk == 0 else vreg(s0, 16)
             e.emit(f"v_mfma_f32_32x32x16_bf16 {vreg(s0, 16)}, {k_reg(0, kk)}, {q_reg(n, kk)}, {src_c}",
                    writes_sbuf=0)
-    step(e, 0, "first", fp32a=fp32a)
+    step(e, 0, "first", fp32a=fp32a, online=online)
     fast_check(e)
     # slow groups: steps t = 1 .. n_tiles, one at a time, leaving after step t = n_tiles (the PV
     # product of the last tile); at each group boundary the fast check
     e.loop_head("L_fixedm_slow_%=")
     for jj in range(STAGES):
-        step(e, jj, "slow", fp32a=fp32a)
+        step(e, jj, "slow", fp32a=fp32a, online=online)
         e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 1")
         e.emit(f"s_cmp_eq_u32 s{S_TCNT}, 0")
         e.emit("s_cbranch_scc1 L_fixedm_end_%=")
@@ -558,7 +657,7 @@ def generate_variant(fp32a: bool) -> str:
     # fast groups of 8 steps
     e.loop_head("L_fixedm_fast_%=")
     for jj in range(STAGES):
-        step(e, jj, "fast", fp32a=fp32a)
+        step(e, jj, "fast", fp32a=fp32a, online=online)
     e.emit(f"s_sub_u32 s{S_DREM}, s{S_DREM}, 8")
     e.emit(f"s_sub_u32 s{S_MREM}, s{S_MREM}, 8")
     e.emit(f"s_sub_u32 s{S_TCNT}, s{S_TCNT}, 8")
@@ -576,6 +675,13 @@ def generate_variant(fp32a: bool) -> str:
     e.emit("s_waitcnt lgkmcnt(0)")
     e.emit("s_nop 7")
     e.emit("s_nop 7")
+    if e.deferred:
+        e.emit("s_branch L_fixedm_done_%=")
+        for block, body in e.deferred:
+            e.lines.append(f"{block}:")
+            for ins in body:
+                e.emit(ins)
+        e.lines.append("L_fixedm_done_%=:")
     body = "\n".join(f'      "{l}\\n"' for l in e.lines)
 
     outs = []
@@ -584,18 +690,21 @@ def generate_variant(fp32a: bool) -> str:
             outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_DPTR}:{S_DPTR + 1}]}}"(pieces)', f'"+{{s{S_TCNT}}}"(n_tiles)']
+    if online:
+        outs += [f'"+{{v{NSHIFT}}}"(nshift[0])', f'"+{{v{NSHIFT + 1}}}"(nshift[1])']
     ins = []
     for n in range(2):
         for kk in range(8):
             ins.append(f'"{{{q_reg(n, kk)}}}"(qf[{n}][{kk}])')
-    ins += [f'"{{v{NSHIFT}}}"(nshift[0])', f'"{{v{NSHIFT + 1}}}"(nshift[1])']
+    if not online:
+        ins += [f'"{{v{NSHIFT}}}"(nshift[0])', f'"{{v{NSHIFT + 1}}}"(nshift[1])']
     ins += [f'"{{v{KOFF + kk}}}"(koff[{kk}])' for kk in range(8)]
     ins += [f'"{{v{VOFF + m}}}"(voff[{m}])' for m in range(4)]
     ins += [f'"{{v{ROW + i}}}"(lane[{i}])' for i in range(2)]
     ins += [f'"{{v{CK + i}}}"(lane[{2 + i}])' for i in range(2)]
     ins += [f'"{{v{CV[i]}}}"(lane[{4 + i}])' for i in range(2)]
     ins += [f'"{{v{KB4}}}"(kb4)']
-    if fp32a:
+    if fp32a or online:
         ins += [f'"{{v{ALPHA}}}"(alpha)']
     ins += [f'"{{s{S_LDS}}}"(lds_wave)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 64)] + [f"v{i}" for i in range(P_BASE, P_BASE + 32)]
@@ -605,17 +714,24 @@ def generate_variant(fp32a: bool) -> str:
             + [f"a{i}" for i in range(K_BASE, K_BASE + 64)]
             + [f"s{i}" for i in range(S_D, S_M + 4)] + [f"s{i}" for i in range(S_MPTR, S_TMP + 2)]
             + [f"s{i}" for i in (S_CNT, S_LO, S_LOPREV, S_FLAG)]
-            + ["m0", "vcc", "scc", "memory"])
+            + ([f"v{r}" for r in OA + OB] + [f"s{i}" for i in (S_GROW, S_GROW + 1, S_RESC)] if online else [])
+            + ["vcc", "scc", "memory"])
     clob_text = ",\n        ".join(", ".join(f'"{c}"' for c in clob[i:i + 12]) for i in range(0, len(clob), 12))
 
     def join(items):
         return ",\n        ".join(items)
 
-    name = "fixed_loop_fp32a_asm" if fp32a else "fixed_loop_asm"
-    what = ("the query fragments are bf16(q) and each exponent is alpha S - (m + c_i) (one FMA "
-            "before its exp; the S chain starts from 0)" if fp32a else
-            "the query fragments are bf16(alpha q) and the S chain starts from -(m + c_i), so S is "
-            "the exponent")
+    name = {"r17": "fixed_loop_asm", "fp32a": "fixed_loop_fp32a_asm", "online": "online_loop_asm"}[variant]
+    what = {"fp32a": "the query fragments are bf16(q) and each exponent is alpha S - (m + c_i) (one FMA "
+                     "before its exp; the S chain starts from 0)",
+            "r17": "the query fragments are bf16(alpha q) and the S chain starts from -(m + c_i), so S is "
+                   "the exponent",
+            "online": "online softmax: the query fragments are bf16(q) and each exponent is alpha S - r_i, "
+                      "with r_i = -nshift[n] the running reference of query row i, raised to the row's "
+                      "maximum only when that exceeds it by more than the slack s of the piece "
+                      "descriptors (base 2; the row sums and accumulators then rescaled, so every "
+                      "probability is at most 2^s); on entry r_i = -inf (nshift = +inf), on exit "
+                      "nshift = -r_i"}[variant]
     return f"""// {what}.
 // The whole fixed-m pass of one work item over its n_tiles (>= 1) tiles of 32 keys, the
 // tiles of its chunk pieces in order (the piece descriptor list at `pieces`, ended by a
@@ -626,9 +742,9 @@ def generate_variant(fp32a: bool) -> str:
 // its barriers continue across piece boundaries.  On exit every LDS read has completed;
 // DMAs of tiles past the end may still be in flight.
 __device__ __attribute__((always_inline)) inline void {name}(
-    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], float (&lsum)[2], const float (&nshift)[2],
+    f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], float (&lsum)[2], {"float" if online else "const float"} (&nshift)[2],
     const uint32_t (&koff)[8], const uint32_t (&voff)[4], const uint32_t (&lane)[6], uint32_t kb4,
-    uint64_t pieces, uint32_t n_tiles, uint32_t lds_wave{", float alpha" if fp32a else ""}) {{
+    uint64_t pieces, uint32_t n_tiles, uint32_t lds_wave{", float alpha" if fp32a or online else ""}) {{
   asm volatile(
 {body}
       : {join(outs)}
@@ -639,8 +755,10 @@ __device__ __attribute__((always_inline)) inline void {name}(
 
 
 def generate() -> str:
-    head = "// Generated by gen_fixed_loop.py; do not edit by hand.\n\n"
-    return head + generate_variant(False) + "\n" + generate_variant(True)
+    head = ("// Generated by gen_fixed_loop.py; do not edit by hand.\n\n"
+            f"static_assert(kStages == {STAGES} && kAhead == {AHEAD} && kTileBytes == {TILE_BYTES},\n"
+            "              \"the generated loop assumes this LDS ring geometry\");\n\n")
+    return head + generate_variant("r17") + "\n" + generate_variant("fp32a") + "\n" + generate_variant("online")
 
 
 def main(out_path=None):

@@ -10,7 +10,9 @@
 //   12  tiles to load                           13, 14  K, V row strides in bytes
 //   15  rows the lane rows shift down (32 - len for a chunk shorter than a tile, else 0)
 //   16  tiles to score                          17  first real row of the last tile
-//   18  first real row of the other tiles       19-31 zero
+//   18  first real row of the other tiles       19  `extra`, the same in every descriptor
+//   20-31 zero
+// (The online-softmax loop takes its rescale slack, fp32 bits, from word 19.)
 // Tile j of a chunk of len >= 32 keys holds the 32 keys from min(32 j, len - 32): the partial
 // last tile is loaded as the chunk's last 32-key window, and its rows before 32 - rem (keys
 // of the previous tile) are masked.  A chunk shorter than a tile is loaded with its keys in
@@ -47,7 +49,8 @@ FIXEDM_PHD inline void piece_put_u64(uint32_t* d, int i, uint64_t x) {
 // each chunk's ceil(len / 32) tiles) to `out`; returns the number of pieces (0: an empty
 // range, nothing written).  chunk(c) gives chunk c as a PieceSrc.
 template <class ChunkAt>
-FIXEDM_PHD inline int build_piece_list(uint32_t* out, ChunkAt chunk, int n_chunks, int64_t v0, int64_t v1) {
+FIXEDM_PHD inline int build_piece_list(uint32_t* out, ChunkAt chunk, int n_chunks, int64_t v0, int64_t v1,
+                                       uint32_t extra) {
   constexpr int64_t kT = 32;
   int np = 0;
   int64_t vbase = 0;
@@ -77,6 +80,7 @@ FIXEDM_PHD inline int build_piece_list(uint32_t* out, ChunkAt chunk, int n_chunk
     d[16] = (uint32_t)(j1 - j0);
     d[17] = j1 - 1 == n_full && rem > 0 ? (uint32_t)(kT - rem) : 0u;
     d[18] = 0;
+    d[19] = extra;
     for (int i = 0; i < kPieceDescWords; ++i) out[np * kPieceDescWords + i] = d[i];
     ++np;
   }

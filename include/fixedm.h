@@ -135,7 +135,8 @@ typedef struct {
  * m: int32 [B, H, nQB]; elig: uint8 [B, H, nQB] (1 = fixed-m body); u: fp64 [B, H, nQB];
  * q2: fp64 [B, H, nQB] (max of sum_d q^2 over the block's real rows); k2: fp64 [B, H]
  * (max of sum_d (k - k_mean)^2 over all keys); k_mean: fp32 [B, H, D]; v_bad: int32
- * (nonzero when some V element has !(|v| <= 256); v_ok = (v_bad == 0)).  With
+ * (0 when every V element has |v| <= 256, else the fp32 bit pattern of the largest |v|,
+ * inf and NaN included; v_ok = (v_bad == 0)).  With
  * shift == FIXEDM_SHIFT_ROW also m_row: int32 [B, H, sq] (m_i = ceil(u_i) - C), q2_row:
  * fp64 [B, H, sq] (sum_d q_id^2) and u_row: fp64 [B, H, sq] (alpha64 * sqrt(q2_i * k2));
  * in BLOCK mode these three arrays are empty (their offsets equal the next one's). */

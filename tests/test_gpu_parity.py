@@ -648,6 +648,46 @@ def test_row_shift_edges(F, name, args, kw):
 
 
 # ------------------------------------------------------------------ degenerate inputs -
+@pytest.mark.parametrize("mode", ["fused", "per_chunk"])
+def test_online_fallback_with_huge_values_stays_finite(F, mode):
+    """V elements of 2^110 (beyond the V bound: every block takes the online body) over 4096
+    keys, whose scores are 0 in the first 32-key tile and about 7 (base 2) after it.  Exact
+    online softmax keeps every probability <= 1 and sums to about 2^122; a reference allowed
+    to lag 8 behind the row maximum would sum 2^7 per key and overflow fp32.  The V check
+    records max|v| bit for bit, the body lets the reference lag at most
+    127 - ceil(log2 N) - ceil(log2 max|v|) = 5, and the output is 2^110 as softmax's is."""
+    import torch
+    say(f"degenerate: |v| = 2^110 on the online body ({mode})")
+    B, H, D, Sq, chunks = 1, 2, 128, 200, (2048, 2048)
+    inp = WL.generic_inputs(57, "bf16", B, H, D, Sq, chunks, q_block=64)
+    scale = O.default_scale(D)
+    qf = np.zeros_like(inp.q)
+    qf[..., 0] = 1.0
+    ks, vs = [], []
+    for c, n in enumerate(chunks):
+        k = np.zeros((B, n, H, D), np.float32)
+        k[:, 32 if c == 0 else 0:, :, 0] = 55.0            # alpha 55 = 7.01 with the default scale
+        ks.append(k)
+        vs.append(np.full((B, n, H, D), 2.0 ** 110, np.float32))
+    inp.q_store = WL.bf16_bits_from_f32(qf)
+    inp.k_store = [WL.bf16_bits_from_f32(k) for k in ks]
+    inp.v_store = [WL.bf16_bits_from_f32(v) for v in vs]
+    q, kd, vd, _ = device_inputs(inp)
+    kw = FUSED if mode == "fused" else {}
+    out, _, desc, buf = F.forward(q, kd, vd, q_block=64, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    gb = gpu_bounds_dict(desc, buf)
+    assert int(gb["v_bad"][0]) == int(np.float32(2.0 ** 110).view(np.int32))
+    assert not gb["elig"].any()
+    ref, _ = O.attention(qf, np.concatenate(ks, 1), np.concatenate(vs, 1), scale)
+    assert np.allclose(ref, 2.0 ** 110, rtol=1e-12)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all(), "the online body overflowed"
+    rel = np.abs(got / 2.0 ** 110 - 1.0).max()
+    say(f"  max relative error {rel:.3e}")
+    assert rel <= 1e-2
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_nonfinite_query_takes_fallback(F, dtype):
     """An infinite query element makes its block's bound non-finite: the block is ineligible

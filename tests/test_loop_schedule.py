@@ -20,6 +20,7 @@ CSRC = os.path.join(ROOT, "dit_amd", "csrc")
 M32 = 0xffffffff
 TBL = 0x7000_0000_0000
 KT = 32
+SLACK_BITS = 0x40e00000                # 7.0f: the descriptors' word 19 in these cases
 
 
 @pytest.fixture(scope="module")
@@ -50,7 +51,7 @@ def build_list(lib, chunks, v0, v1):
     kss, vss, ln = arr("k_ss", np.int64), arr("v_ss", np.int64), arr("len", np.int64)
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     np_ = lib.build_piece_list_host(p(out), p(kb), p(vb), p(kss), p(vss), p(ln), n, ctypes.c_int64(v0),
-                                    ctypes.c_int64(v1))
+                                    ctypes.c_int64(v1), ctypes.c_uint32(SLACK_BITS))
     return np_, out
 
 
@@ -66,8 +67,11 @@ class Machine:
     """Executes the scalar, branch, lane-offset, mask and load instructions of the loop; the
     matrix, LDS-read and exp work is skipped (it does not steer the control flow)."""
 
-    def __init__(self, lines, mem, wave, n_tiles, lds0=0):
+    def __init__(self, lines, mem, wave, n_tiles, lds0=0, seed=0):
         self.lines = lines
+        self.rng = np.random.default_rng(seed)
+        self.vcc_bit = 0                                 # the online growth test (data dependent)
+        self.rescales = 0
         self.labels = {l[:-1]: i for i, l in enumerate(lines) if l.endswith(":")}
         self.mem = mem
         self.s = {}
@@ -171,7 +175,13 @@ class Machine:
             return
         if op.startswith("s_"):
             # the reads come first, so a pending destination register is caught by wset
-            if op in ("s_add_u32", "s_addc_u32", "s_sub_u32"):
+            if op == "s_mov_b64" and ops[1] == "vcc":
+                self.wpair(ops[0], self.vcc_bit)
+            elif op == "s_or_b64" and ops[2] == "vcc":
+                r = self.spair(ops[1]) | self.vcc_bit
+                self.scc = int(r != 0)
+                self.wpair(ops[0], r)
+            elif op in ("s_add_u32", "s_addc_u32", "s_sub_u32"):
                 a, b = self.sreg(ops[1]), self.sreg(ops[2])
                 if op == "s_add_u32":
                     r = a + b
@@ -189,6 +199,8 @@ class Machine:
             elif op in ("s_cmp_eq_u32", "s_cmp_lg_u32"):
                 a, b = self.sreg(ops[0]), self.sreg(ops[1])
                 self.scc = int((a == b) == (op == "s_cmp_eq_u32"))
+                if op == "s_cmp_lg_u32" and ops[0] == "s98" and self.scc:
+                    self.rescales += 1
             elif op == "s_cselect_b32":
                 self.wset(int(ops[0][1:]), self.sreg(ops[1]) if self.scc else self.sreg(ops[2]))
             elif op == "s_cselect_b64":
@@ -231,6 +243,10 @@ class Machine:
             self.v[int(ops[0][1:])] = (self.vreg(ops[1]) + self.vreg(ops[2])) & M32
         elif op == "v_sub_u32":
             self.v[int(ops[0][1:])] = (self.sreg(ops[1]) - self.vreg(ops[2])) & M32
+        elif op == "v_cmp_lt_f32_e32":       # the online growth test: either outcome
+            if self.sreg(ops[1]) != SLACK_BITS:
+                raise Fault(f"growth test against {ops[1]}, not the descriptors' slack word")
+            self.vcc_bit = int(self.rng.integers(0, 2))
         elif op == "v_cmp_lt_i32_e32":
             x = self.vreg(ops[2]).astype(np.uint32).astype(np.int32)
             self.vcc = int(ops[1]) < x
@@ -249,7 +265,7 @@ class Machine:
                 self.s_tiles.append((n, self.mask[:, 16 * n:16 * n + 16].copy()))
         elif op.startswith(("v_", "ds_")):
             m = re.match(r"v(\d+)$", ops[0]) if ops else None
-            if m and int(m.group(1)) in (176, 177, 178, 179, 181, 182, 183, 184, 185, 188, 190, 191):
+            if m and int(m.group(1)) in (176, 177, 178, 179, 181, 182, 183, 184, 185, 188, 191):
                 raise Fault(f"unmodelled write of a tracked register: {ln}")
         else:
             raise Fault(f"unmodelled instruction: {ln}")
@@ -278,7 +294,7 @@ def _chunks(lens, strides):
     return out
 
 
-def run_case(gen, lib, lens, strides, parts=1, part=None, waves=(0, 3), variants=(False, True)):
+def run_case(gen, lib, lens, strides, parts=1, part=None, waves=(0, 3), variants=("r17", "fp32a", "online")):
     chunks = _chunks(lens, strides)
     seq = _tiles(chunks)
     T = len(seq)
@@ -290,11 +306,13 @@ def run_case(gen, lib, lens, strides, parts=1, part=None, waves=(0, 3), variants
         return
     mem = {TBL + 4 * i: int(w) for i, w in enumerate(table[:(n_pieces + 1) * 32])}
     items = seq[v0:v1]
-    for fp32a in variants:
-        lines = _body(gen.generate_variant(fp32a))
+    for variant in variants:
+        lines = _body(gen.generate_variant(variant))
         for wave in waves:
-            m = Machine(lines, mem, wave, n_tiles)
+            m = Machine(lines, mem, wave, n_tiles, seed=wave + 7 * n_tiles)
             m.run()
+            if variant == "online" and n_tiles >= 4:
+                assert m.rescales > 0       # the out-of-line accumulator rescale ran
             assert m.barriers == n_tiles + 2
             # loads: tiles 0 .. n_tiles + 6, four instructions each, in the ring's stages
             assert len(m.dmas) == 4 * (n_tiles + 7), (len(m.dmas), n_tiles)
@@ -364,7 +382,7 @@ def test_split_parts(gen, lib, parts):
     lens = [290, 7, 610, 64, 33]
     for part in range(parts):
         run_case(gen, lib, lens, [(128, 128), (128, 256), (5120, 5120), (128, 128), (256, 128)], parts, part,
-                 waves=(2,), variants=(False,))
+                 waves=(2,), variants=("r17",))
 
 
 def test_random_sequences(gen, lib):
@@ -375,7 +393,8 @@ def test_random_sequences(gen, lib):
         strides = [(int(rng.choice([128, 640, 5120])), int(rng.choice([128, 640, 5120]))) for _ in range(n)]
         parts = int(rng.integers(1, 5))
         part = None if parts == 1 else int(rng.integers(0, parts))
-        run_case(gen, lib, lens, strides, parts, part, waves=(int(rng.integers(0, 4)),), variants=(bool(rng.integers(0, 2)),))
+        run_case(gen, lib, lens, strides, parts, part, waves=(int(rng.integers(0, 4)),),
+                 variants=(("r17", "fp32a", "online")[int(rng.integers(0, 3))],))
 
 
 def test_empty_part_writes_no_list(gen, lib):
