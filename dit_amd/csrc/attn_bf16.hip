@@ -293,10 +293,21 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
 
   if (a.final_out && !split) {
     // The run ends with this launch: merge the workspace's earlier keys (if any), normalise
-    // once ([CM] "Accumulate, then normalize once") and write O, and lse, straight from the
-    // accumulator registers.  The arithmetic is the finalize kernel's: O = acc / l (IEEE
-    // division), bf16 by round-to-nearest-even, lse = ln 2 (r + log2 l).
+    // once ([CM] "Accumulate, then normalize once") and write O, and lse, from the accumulator
+    // registers.  The arithmetic is the finalize kernel's: O = acc / l (IEEE division), bf16 by
+    // round-to-nearest-even, lse = ln 2 (r + log2 l).  A lane holds pieces of 4 elements of one
+    // query row, rows 10 KB apart across a wave in the usual layout: stored directly, each
+    // instruction would touch 64 rows.  So each wave stages its 64 rows in its own 32 KB of the
+    // (now idle) ring, 32 pieces a row at piece p ^ (row mod 32), and stores whole rows: lane L
+    // of instruction i writes piece L mod 32 of row 2 i + L / 32 (8 bytes bf16, 16 bytes fp32).
     const int64_t tb = (int64_t)tile * (kQTile * kD);
+    const bool f32out = a.out_dtype == FIXEDM_F32;
+    const uint32_t pbytes = f32out ? 16u : 8u;
+    // staging offsets from an id the compiler cannot hoist above the assembly block
+    int sid = threadIdx.x;
+    asm volatile("" : "+v"(sid));
+    const int s_lane = sid & 63, s_lq = s_lane & 31, s_hh = s_lane >> 5;
+    uint8_t* stage = smem + (sid >> 6) * 32768;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const float other = __shfl_xor(lsum[n], 32, 64);
@@ -327,22 +338,35 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
             if (fixed) v = prev + v;
             else v = prev * fw + v * fo;
           }
-          if (q < a.Sq) {
-            const int64_t off = b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + 32 * m + 8 * jj + 4 * hh;
-            const float x0 = __fdiv_rn(v[0], lnew), x1 = __fdiv_rn(v[1], lnew);
-            const float x2 = __fdiv_rn(v[2], lnew), x3 = __fdiv_rn(v[3], lnew);
-            if (a.out_dtype == FIXEDM_F32) {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{x0, x1, x2, x3};
-            } else {
-              uint2 w;
-              w.x = bf16_rne(x0) | (bf16_rne(x1) << 16);
-              w.y = bf16_rne(x2) | (bf16_rne(x3) << 16);
-              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w;
-            }
+          const float x0 = __fdiv_rn(v[0], lnew), x1 = __fdiv_rn(v[1], lnew);
+          const float x2 = __fdiv_rn(v[2], lnew), x3 = __fdiv_rn(v[3], lnew);
+          const int r = 32 * n + s_lq, pc = 8 * m + 2 * jj + s_hh;
+          uint8_t* dst = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
+          if (f32out) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{x0, x1, x2, x3};
+          } else {
+            uint2 w;
+            w.x = bf16_rne(x0) | (bf16_rne(x1) << 16);
+            w.y = bf16_rne(x2) | (bf16_rne(x3) << 16);
+            *reinterpret_cast<uint2*>(dst) = w;
           }
         }
       }
       if (a.lse != nullptr && hh == 0 && q < a.Sq) a.lse[(int64_t)bh * a.Sq + q] = lse_of(rnew, lnew);
+    }
+    // the wave's own rows only: its LDS writes complete before its reads of them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int r = 2 * i + s_hh, pc = s_lq, q = q0 + r;
+      const uint8_t* src = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
+      if (q < a.Sq) {
+        const int64_t off = b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + 4 * pc;
+        if (f32out)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = *reinterpret_cast<const f32x4*>(src);
+        else
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = *reinterpret_cast<const uint2*>(src);
+      }
     }
     return;
   }
