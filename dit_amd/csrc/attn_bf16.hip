@@ -205,47 +205,66 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   const int qlast = q0 < a.Sq ? q0 : a.Sq - 1;
   const int beta = qlast / a.q_block;
   const int64_t bq = (int64_t)bh * a.nqb + beta;
+  // Every load of the set-up is issued before any of its results is used (the item's
+  // set-up then costs one memory round trip): the block's flags, shift and bound, the query
+  // rows and k_mean.
+  const uint32_t elig_raw = a.elig[bq];
+  const int m_raw = a.m[bq];
+  const double u_raw = a.u[bq];
+  const float* km = a.k_mean + (int64_t)bh * kD;
+  uint4 qw[2][8];
+  f32x4 kmv[8][2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    int row = q0 + 32 * n + lq;
+    if (row >= a.Sq) row = a.Sq - 1;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)row * a.q_ss + h * a.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qw[n][kk] = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * hh);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kmv[kk][i] = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * hh + 4 * i);
   // The body is chosen per wave: make the choice visibly wave-uniform (a scalar branch), so
   // no wave steps through the other body's code with an empty exec mask (that code holds
   // barriers and assembly that keeps its state in fixed registers).
-  const bool fixed = __builtin_amdgcn_readfirstlane((int)a.elig[bq]) != 0;
-  const int mshift = __builtin_amdgcn_readfirstlane(a.m[bq]);
+  const bool fixed = __builtin_amdgcn_readfirstlane((int)elig_raw) != 0;
+  const int mshift = __builtin_amdgcn_readfirstlane(m_raw);
   // Eligible blocks with a bound above kR17MaxU take the fixed-m body with the logit factor
   // applied in fp32: the rounding of bf16(alpha q) moves a base-2 logit by up to 2^-8 U.
-  const bool r17 = fixed && __builtin_amdgcn_readfirstlane((int)(a.u[bq] <= kR17MaxU)) != 0;
+  const bool r17 = fixed && __builtin_amdgcn_readfirstlane((int)(u_raw <= kR17MaxU)) != 0;
 
   // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean.
   // The fixed-m assembly body takes its logits in base 2 straight from the MFMA: its query
   // fragments are bf16(alpha q) (fp32 product, one rounding: the base-2 rescale of Q that the
   // TPU path folds into Q's producer, [FM] Summary "Relayout optimization", bit-identical
   // there by the [UR] review thread) and c_i = (alpha q_i) . k_mean.  The other two bodies
-  // keep q and scale their scores by alpha in fp32 (c_i = alpha (q_i . k_mean)).
+  // keep q and scale their scores by alpha in fp32 (c_i = alpha (q_i . k_mean)).  The
+  // scaling is a select, not a branch, so no load waits behind the choice.
   bf16x8 qf[2][8];
   float cdot[2];
-  const float* km = a.k_mean + (int64_t)bh * kD;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    int row = q0 + 32 * n + lq;
-    if (row >= a.Sq) row = a.Sq - 1;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)row * a.q_ss + h * a.q_sh;
     float dot = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * hh);
+      const uint4 w = qw[n][kk];
       uint32_t u[4] = {w.x, w.y, w.z, w.w};
-      if (r17) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x2 x = {__uint_as_float(u[i] << 16) * a.alpha, __uint_as_float(u[i] & 0xffff0000u) * a.alpha};
-          const bf16x2 y = __builtin_convertvector(x, bf16x2);
-          __builtin_memcpy(&u[i], &y, 4);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 x = {__uint_as_float(u[i] << 16) * a.alpha, __uint_as_float(u[i] & 0xffff0000u) * a.alpha};
+        const bf16x2 y = __builtin_convertvector(x, bf16x2);
+        uint32_t sc;
+        __builtin_memcpy(&sc, &y, 4);
+        u[i] = r17 ? sc : u[i];
       }
       __builtin_memcpy(&qf[n][kk], u, 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dot = __builtin_fmaf(__uint_as_float(u[i] << 16), km[16 * kk + 8 * hh + 2 * i], dot);
-        dot = __builtin_fmaf(__uint_as_float(u[i] & 0xffff0000u), km[16 * kk + 8 * hh + 2 * i + 1], dot);
+        const f32x4 kv = kmv[kk][i >> 1];
+        dot = __builtin_fmaf(__uint_as_float(u[i] << 16), kv[2 * (i & 1)], dot);
+        dot = __builtin_fmaf(__uint_as_float(u[i] & 0xffff0000u), kv[2 * (i & 1) + 1], dot);
       }
     }
     // q . k_mean: this half's dims plus the other half's, low half first on both lanes; the
