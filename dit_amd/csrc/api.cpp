@@ -337,7 +337,7 @@ fixedm_status bounds_impl(const fixedm_problem* p, fixedm_tensor q, const fixedm
   a.k_mean = reinterpret_cast<float*>(base + lay.k_mean);
   a.v_bad = reinterpret_cast<int32_t*>(base + lay.v_bad);
   a.kpart = reinterpret_cast<double*>(scratch_base + sc.kpart);
-  a.kflag = reinterpret_cast<int32_t*>(scratch_base + sc.kflag);
+  a.kflag = reinterpret_cast<uint8_t*>(scratch_base + sc.kflag);
   a.kslabs = sc.slabs;
   if (p->shift == FIXEDM_SHIFT_ROW) {
     a.m_row = reinterpret_cast<int32_t*>(base + lay.m_row);
@@ -375,9 +375,8 @@ fixedm_status fixedm_bounds_static(const fixedm_problem* p, fixedm_tensor q, con
   bounds_layout(*p, &lay);
   // as few key slabs as the static array needs: its size bounds the partial sums
   const size_t el = (size_t)(p->batch * p->heads) * (size_t)p->head_dim;
-  const size_t flags = (el * 4 + 255) & ~(size_t)255;
-  if (kStaticScratchBytes < flags + el * 8) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
-  const BoundsScratch sc = bounds_scratch(*p, (int64_t)((kStaticScratchBytes - flags - 255) / (el * 8)));
+  if (kStaticScratchBytes < el * 9 + 512) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
+  const BoundsScratch sc = bounds_scratch(*p, (int64_t)((kStaticScratchBytes - 512) / (el * 9)));
   if (sc.total > kStaticScratchBytes) return FIXEDM_ERR_UNSUPPORTED_SHAPE;
   return bounds_impl(p, q, k_chunks, v_chunks, chunk_len, n_chunks, k_mean_in, bounds_dev, bounds_dev_bytes,
                      lay.scratch, nullptr, sc, out, stream);

@@ -70,7 +70,6 @@ __global__ void bounds_init_kernel(BoundsArgs a) {
     if (i < nkm) {
       if (a.center == FIXEDM_CENTER_NONE) a.k_mean[i] = 0.0f;
       else if (a.center == FIXEDM_CENTER_SUPPLIED) a.k_mean[i] = a.k_mean_in[i];
-      else a.kflag[i] = 0;
     }
     if (i == 0) *a.v_bad = 0;
   }
@@ -135,6 +134,17 @@ struct MagRange<float> {
 
 template <typename T>
 __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
+  // This pass runs first: it clears what the later passes reduce into (the Q and K norm
+  // maxima and the V record), so no separate initialising launch is needed.
+  {
+    const int64_t nth = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    const int64_t t0 = (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x +
+                       threadIdx.x;
+    const int64_t nqb_all = (int64_t)a.B * a.H * a.nqb;
+    for (int64_t t = t0; t < nqb_all; t += nth) a.q2[t] = 0ull;
+    for (int64_t t = t0; t < (int64_t)a.B * a.H; t += nth) a.k2[t] = 0ull;
+    if (t0 == 0) *a.v_bad = 0;
+  }
   const int per = a.D / 8;
   const int hl = threadIdx.x / per, c = threadIdx.x % per;
   const int b = blockIdx.y, h = blockIdx.z * kBoundsHeads + hl;
@@ -145,14 +155,13 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   int64_t count = 0;                             // keys this thread adds
   int ci = 0;                                    // chunk of the current key (uniform)
   const int64_t stride = (int64_t)a.kslabs * 8;
-  // bf16: two of the workgroup's blocks per pass (16 keys in flight a thread), kept as raw
-  // 16-byte words until they are added in key order.
-  constexpr int kRows = sizeof(T) == 2 ? 16 : 8, kW = (int)sizeof(T) / 2;
-  for (int64_t j = (int64_t)blockIdx.x * 8; j < a.N; j += (kRows / 8) * stride) {
-    uint4 raw[kRows][kW];
+  // The workgroup's blocks of 8 keys, software-pipelined: the next block's loads are in flight
+  // while the current one is added (raw 16-byte words until then), keys in order.
+  constexpr int kW = (int)sizeof(T) / 2;
+  const auto load_block = [&](int64_t j, uint4 (&raw)[8][kW]) {
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      const int64_t jj = j + (u < 8 ? u : stride + u - 8);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t jj = j + u;
       if (jj < a.N) {
         while (ci + 1 < a.n_chunks && jj >= a.ch[ci + 1].start) ++ci;
         const ChunkDesc& cd = a.ch[ci];
@@ -162,13 +171,19 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
         for (int w = 0; w < kW; ++w) raw[u][w] = src[w];
       }
     }
+  };
+  uint4 cur[8][kW], nxt[8][kW];
+  int64_t j = (int64_t)blockIdx.x * 8;
+  if (j < a.N) load_block(j, cur);
+  for (; j < a.N; j += stride) {
+    if (j + stride < a.N) load_block(j + stride, nxt);
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      if (j + (u < 8 ? u : stride + u - 8) < a.N) {
+    for (int u = 0; u < 8; ++u) {
+      if (j + u < a.N) {
         float f[8];
         ++count;
         if constexpr (sizeof(T) == 2) {
-          const uint32_t x[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
+          const uint32_t x[4] = {cur[u][0].x, cur[u][0].y, cur[u][0].z, cur[u][0].w};
           mag.add(x);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -176,8 +191,8 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
             f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
           }
         } else {
-          const uint32_t x[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
-                                 raw[u][kW - 1].x, raw[u][kW - 1].y, raw[u][kW - 1].z, raw[u][kW - 1].w};
+          const uint32_t x[8] = {cur[u][0].x, cur[u][0].y, cur[u][0].z, cur[u][0].w,
+                                 cur[u][kW - 1].x, cur[u][kW - 1].y, cur[u][kW - 1].z, cur[u][kW - 1].w};
           mag.add(x);
 #pragma unroll
           for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(x[i]);
@@ -186,52 +201,82 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
         for (int i = 0; i < 8; ++i) acc[i] = acc[i] + (double)f[i];
       }
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int w = 0; w < kW; ++w) cur[u][w] = nxt[u][w];
   }
   // ceil(log2 count): partial sums stay below 2^lc max|x|
   int lc = 0;
   while (((int64_t)1 << lc) < count) ++lc;
   const int64_t el = ((int64_t)b * a.H + h) * a.D + 8 * c;
-  double* dst = a.kpart + (int64_t)blockIdx.x * a.B * a.H * a.D + el;
+  const int64_t slab = (int64_t)blockIdx.x * a.B * a.H * a.D;
+  double* dst = a.kpart + slab + el;
+  uint8_t* flag = a.kflag + slab + el;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     dst[i] = acc[i];
     const uint32_t lo1 = mag.lo1(i), hi = mag.hi(i);
-    if (lo1 == MagRange<T>::kNone) continue;                 // no nonzero key: the sum is 0
-    const int emax = MagRange<T>::exp_field(hi), emin = MagRange<T>::exp_field(lo1 + 1);
-    // |x| < 2^(max(emax,1) - 126) and x a multiple of 2^(max(emin,1) - 127 - mant):
-    // exact while max(emax,1) - 126 + lc <= max(emin,1) - 127 - mant + 53
-    const bool nonfinite = emax == 255;
-    const int top = (emax > 1 ? emax : 1) + lc, room = (emin > 1 ? emin : 1) + 52 - MagRange<T>::kMant;
-    if (nonfinite || top > room) atomicOr(a.kflag + el + i, 1);
+    bool inexact = false;                                    // no nonzero key: the sum is 0
+    if (lo1 != MagRange<T>::kNone) {
+      const int emax = MagRange<T>::exp_field(hi), emin = MagRange<T>::exp_field(lo1 + 1);
+      // |x| < 2^(max(emax,1) - 126) and x a multiple of 2^(max(emin,1) - 127 - mant):
+      // exact while max(emax,1) - 126 + lc <= max(emin,1) - 127 - mant + 53
+      const bool nonfinite = emax == 255;
+      const int top = (emax > 1 ? emax : 1) + lc, room = (emin > 1 ? emin : 1) + 52 - MagRange<T>::kMant;
+      inexact = nonfinite || top > room;
+    }
+    flag[i] = inexact ? 1 : 0;
   }
 }
 
-// k_mean[b,h,d] = fp32(fl64(exact key sum) / N) for the elements whose slab partial sums are
-// all exact (kflag clear): thread (g, e) of a 256-thread workgroup adds partials g, g + 8, ...
-// of element e into its own fixed-point accumulator in LDS (exact, so no order enters); the
-// 8 accumulators of the element are then added and rounded once.  Flagged elements are left
-// to kmean_exact_kernel.
+// k_mean[b,h,d] = fp32(fl64(exact key sum) / N).  Workgroup of 256 threads = 8 groups x 32
+// elements: thread (g, e) adds the partials of slabs g, g + 8, ... of element e into its own
+// fixed-point accumulator in LDS (exact, so no order enters; a partial whose slab flagged it
+// is skipped: it may not be exact, or even finite).  When no slab flagged the element, its 8
+// accumulators are added and rounded once.  Otherwise (a slab sum that was not exact, or a
+// non-finite key) the element's keys are re-summed one by one: thread (g, e) takes the keys
+// g, g + 8, ... of every chunk (the 32 elements of a workgroup are adjacent dims, so each key
+// is one contiguous read).  A NaN, or both infinities, give NaN; otherwise an infinity gives
+// itself.
+template <typename T>
 __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
   __shared__ int64_t lim[8][32][kLimbs];
+  __shared__ uint32_t st[8][32];
   const int64_t n = (int64_t)a.B * a.H * a.D;
   const int g = threadIdx.x >> 5, el = threadIdx.x & 31;
   const int64_t i = (int64_t)blockIdx.x * 32 + el;
-  const bool mine = i < n && a.kflag[i] == 0;
+  const bool valid = i < n;
   int64_t* acc = lim[g][el];
   for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
-  if (mine) {
+  uint32_t flagged = 0;
+  if (valid) {
     int sl = g;
     for (; sl + 56 < a.kslabs; sl += 64) {      // eight partials in flight
       double x[8];
+      uint32_t f[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = a.kpart[(int64_t)(sl + 8 * u) * n + i];
+      for (int u = 0; u < 8; ++u) {
+        x[u] = a.kpart[(int64_t)(sl + 8 * u) * n + i];
+        f[u] = a.kflag[(int64_t)(sl + 8 * u) * n + i];
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) exact_add(acc, x[u]);
+      for (int u = 0; u < 8; ++u) {
+        flagged |= f[u];
+        if (f[u] == 0) exact_add(acc, x[u]);
+      }
     }
-    for (; sl < a.kslabs; sl += 8) exact_add(acc, a.kpart[(int64_t)sl * n + i]);
+    for (; sl < a.kslabs; sl += 8) {
+      const uint32_t f = a.kflag[(int64_t)sl * n + i];
+      flagged |= f;
+      if (f == 0) exact_add(acc, a.kpart[(int64_t)sl * n + i]);
+    }
   }
-  __syncthreads();
-  if (g == 0 && mine) {
+  st[g][el] = flagged;
+  const bool any_in_group = __syncthreads_or(flagged != 0) != 0;
+  uint32_t mine = 0;                               // some slab flagged this thread's element
+  for (int gg = 0; gg < 8; ++gg) mine |= st[gg][el];
+  if (g == 0 && valid && mine == 0) {
     int64_t tot[kLimbs];
     for (int k = 0; k < kLimbs; ++k) {
       int64_t t = 0;
@@ -240,45 +285,46 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
     }
     a.k_mean[i] = (float)(exact_round(tot) / (double)a.N);
   }
-}
-
-// k_mean for the flagged elements (a slab partial sum that was not exact, or a non-finite
-// key): one workgroup per (b, h), thread d re-sums dim d over every key of every chunk in
-// the fixed-point accumulator (key rows are read coalesced across the threads).  A NaN, or
-// both infinities, give NaN; otherwise an infinity gives itself.  Elements with kflag clear
-// return at once, so the launch costs a few microseconds when nothing is flagged.
-template <typename T>
-__global__ __launch_bounds__(128) void kmean_exact_kernel(BoundsArgs a) {
-  __shared__ int64_t lim[128][kLimbs];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-  const int d = threadIdx.x;
-  if (d >= a.D) return;
-  const int64_t i = (int64_t)bh * a.D + d;
-  if (a.kflag[i] == 0) return;
-  int64_t* acc = lim[d];
-  for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
-  bool nan = false, pinf = false, ninf = false;
-  int64_t since = 0;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const ChunkDesc& cd = a.ch[c];
-    const T* col = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + h * cd.k_sh + d;
-    for (int64_t j = 0; j < cd.len; ++j) {
-      const double x = (double)load_elem(col + j * cd.k_ss);
-      if (isnan(x)) nan = true;
-      else if (isinf(x)) (x > 0 ? pinf : ninf) = true;
-      else exact_add(acc, x);
-      if (++since == ((int64_t)1 << 28)) {
-        exact_normalize(acc);
-        since = 0;
+  if (!any_in_group) return;                       // the whole workgroup: nothing flagged
+  __syncthreads();                                 // every read of st and lim above is done
+  uint32_t bits = 0;                               // 1: NaN, 2: +inf, 4: -inf
+  if (valid && mine != 0) {
+    for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
+    const int64_t bh = i / a.D, d = i % a.D, b = bh / a.H, h = bh % a.H;
+    int64_t since = 0;
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const ChunkDesc& cd = a.ch[c];
+      const T* col = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + h * cd.k_sh + d;
+      for (int64_t j = g; j < cd.len; j += 8) {
+        const double x = (double)load_elem(col + j * cd.k_ss);
+        if (isnan(x)) bits |= 1u;
+        else if (isinf(x)) bits |= x > 0 ? 2u : 4u;
+        else exact_add(acc, x);
+        if (++since == ((int64_t)1 << 28)) {
+          exact_normalize(acc);
+          since = 0;
+        }
       }
     }
   }
-  double sum;
-  if (nan || (pinf && ninf)) sum = __longlong_as_double(0x7ff8000000000000ll);
-  else if (pinf) sum = __longlong_as_double(0x7ff0000000000000ll);
-  else if (ninf) sum = -__longlong_as_double(0x7ff0000000000000ll);
-  else sum = exact_round(acc);
-  a.k_mean[i] = (float)(sum / (double)a.N);
+  st[g][el] = bits;
+  __syncthreads();
+  if (g == 0 && valid && mine != 0) {
+    uint32_t all = 0;
+    int64_t tot[kLimbs];
+    for (int k = 0; k < kLimbs; ++k) tot[k] = 0;
+    for (int gg = 0; gg < 8; ++gg) {
+      all |= st[gg][el];
+      exact_normalize(lim[gg][el]);                // each group's limbs into digits first
+      for (int k = 0; k < kLimbs; ++k) tot[k] += lim[gg][el][k];
+    }
+    double sum;
+    if ((all & 1u) || (all & 6u) == 6u) sum = __longlong_as_double(0x7ff8000000000000ll);
+    else if (all & 2u) sum = __longlong_as_double(0x7ff0000000000000ll);
+    else if (all & 4u) sum = -__longlong_as_double(0x7ff0000000000000ll);
+    else sum = exact_round(tot);
+    a.k_mean[i] = (float)(sum / (double)a.N);
+  }
 }
 
 // One row per thread in the norm kernels: every 16-byte piece of the row is loaded before
@@ -661,8 +707,7 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
     const int hpg = a.H < kBoundsHeads ? a.H : kBoundsHeads;
     kmean_partial_kernel<T><<<dim3((unsigned)a.kslabs, (unsigned)a.B, groups), hpg * (a.D / 8), 0, s>>>(a);
     const int64_t n = (int64_t)a.B * a.H * a.D;
-    kmean_final_kernel<<<(unsigned)((n + 31) / 32), 256, 0, s>>>(a);
-    kmean_exact_kernel<T><<<(unsigned)(a.B * a.H), 128, 0, s>>>(a);
+    kmean_final_kernel<T><<<(unsigned)((n + 31) / 32), 256, 0, s>>>(a);
   }
   constexpr int W = NormGeom<T>::kWaves;
   const int64_t n_hq = (a.H + W - 1) / W;
@@ -710,7 +755,8 @@ hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s) {
   const int64_t nkm = (int64_t)a.B * a.H * a.D;
   const int64_t init_n = nqb_all > nkm ? nqb_all : nkm;
   const unsigned init_blocks = (unsigned)((init_n + 255) / 256 < 4096 ? (init_n + 255) / 256 : 4096);
-  bounds_init_kernel<<<init_blocks, 256, 0, s>>>(a);
+  // (with the key mean computed, its first pass does the clearing)
+  if (a.center != FIXEDM_CENTER_COMPUTE) bounds_init_kernel<<<init_blocks, 256, 0, s>>>(a);
   if (a.dtype == FIXEDM_BF16) launch_typed<uint16_t>(a, s);
   else launch_typed<float>(a, s);
   gate_kernel<<<(unsigned)((nqb_all + 255) / 256), 256, 0, s>>>(a);

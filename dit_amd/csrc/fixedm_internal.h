@@ -44,12 +44,13 @@ inline SplitPlan split_plan(int64_t tiles, int cus) {
   return sp;
 }
 
-// Key slabs of the k_mean reduction: enough workgroups to fill the chip (about 512 with
-// B x head groups), at most one slab per 16 keys, and at most max_slabs.  The key sum is
+// Key slabs of the k_mean reduction: about 256 workgroups of B x head groups (with 640-thread
+// workgroups that fills the chip; more slabs only lengthen the final reduction), at most one
+// slab per 16 keys, and at most max_slabs.  The key sum is
 // exact, so the slab count changes the speed only, never a bit of the result.
 inline int kmean_slabs(int64_t B, int64_t H, int64_t N, int64_t max_slabs = 1 << 30) {
   const int64_t groups = B * ((H + kBoundsHeads - 1) / kBoundsHeads);
-  int64_t s = (512 + groups - 1) / groups;
+  int64_t s = (256 + groups - 1) / groups;
   if (s > N / 16) s = N / 16;
   if (s > max_slabs) s = max_slabs;
   if (s < 1) s = 1;
@@ -57,7 +58,7 @@ inline int kmean_slabs(int64_t B, int64_t H, int64_t N, int64_t max_slabs = 1 <<
 }
 
 // Scratch of one bounds call in COMPUTE centring: the key-mean partial sums
-// [slabs][B*H][D] fp64, then their exactness flags [B*H][D] int32 (byte offsets from the
+// [slabs][B*H][D] fp64, then their exactness flags [slabs][B*H][D] uint8 (byte offsets from the
 // scratch base, 256-byte aligned).  Empty for the other centring modes.
 struct BoundsScratch {
   int32_t slabs;
@@ -69,7 +70,7 @@ inline BoundsScratch bounds_scratch(const fixedm_problem& p, int64_t max_slabs =
   const size_t el = (size_t)(p.batch * p.heads) * (size_t)p.head_dim;
   s.slabs = kmean_slabs(p.batch, p.heads, p.sk_total, max_slabs);
   s.kflag = ((size_t)s.slabs * el * 8 + 255) & ~(size_t)255;
-  s.total = (s.kflag + el * 4 + 255) & ~(size_t)255;
+  s.total = (s.kflag + (size_t)s.slabs * el + 255) & ~(size_t)255;
   return s;
 }
 
@@ -126,7 +127,8 @@ struct BoundsArgs {
   float* k_mean;
   int32_t* v_bad;
   double* kpart;            // [kslabs][B*H][D] partial key sums
-  int32_t* kflag;           // [B*H][D]: nonzero when a partial sum of that element rounded
+  uint8_t* kflag;           // [kslabs][B*H][D]: 1 when that slab's partial sum of the element
+                            // may not be exact (or a key is not finite)
   int32_t kslabs;
   // per-row shifts (shift == FIXEDM_SHIFT_ROW; null otherwise): [B, H, Sq]
   int32_t* m_row;
