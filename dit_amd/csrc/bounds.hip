@@ -230,35 +230,36 @@ __global__ __launch_bounds__(1024) void kmean_partial_kernel(BoundsArgs a) {
   }
 }
 
-// k_mean[b,h,d] = fp32(fl64(exact key sum) / N).  Workgroup of 256 threads = 8 groups x 32
-// elements: thread (g, e) adds the partials of slabs g, g + 8, ... of element e into its own
+// k_mean[b,h,d] = fp32(fl64(exact key sum) / N).  Workgroup of 256 threads = kFinG groups x
+// kFinE elements: thread (g, e) adds the partials of slabs g, g + kFinG, ... of element e into its own
 // fixed-point accumulator in LDS (exact, so no order enters; a partial whose slab flagged it
-// is skipped: it may not be exact, or even finite).  When no slab flagged the element, its 8
-// accumulators are added and rounded once.  Otherwise (a slab sum that was not exact, or a
+// is skipped: it may not be exact, or even finite).  When no slab flagged the element, its
+// kFinG accumulators are added and rounded once.  Otherwise (a slab sum that was not exact, or a
 // non-finite key) the element's keys are re-summed one by one: thread (g, e) takes the keys
-// g, g + 8, ... of every chunk (the 32 elements of a workgroup are adjacent dims, so each key
+// g, g + kFinG, ... of every chunk (the elements of a workgroup are adjacent dims, so each key
 // is one contiguous read).  A NaN, or both infinities, give NaN; otherwise an infinity gives
 // itself.
+constexpr int kFinG = 16, kFinE = 256 / kFinG;
 template <typename T>
 __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
-  __shared__ int64_t lim[8][32][kLimbs];
-  __shared__ uint32_t st[8][32];
+  __shared__ int64_t lim[kFinG][kFinE][kLimbs];
+  __shared__ uint32_t st[kFinG][kFinE];
   const int64_t n = (int64_t)a.B * a.H * a.D;
-  const int g = threadIdx.x >> 5, el = threadIdx.x & 31;
-  const int64_t i = (int64_t)blockIdx.x * 32 + el;
+  const int g = threadIdx.x / kFinE, el = threadIdx.x % kFinE;
+  const int64_t i = (int64_t)blockIdx.x * kFinE + el;
   const bool valid = i < n;
   int64_t* acc = lim[g][el];
   for (int k = 0; k < kLimbs; ++k) acc[k] = 0;
   uint32_t flagged = 0;
   if (valid) {
     int sl = g;
-    for (; sl + 56 < a.kslabs; sl += 64) {      // eight partials in flight
+    for (; sl + 7 * kFinG < a.kslabs; sl += 8 * kFinG) {      // eight partials in flight
       double x[8];
       uint32_t f[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        x[u] = a.kpart[(int64_t)(sl + 8 * u) * n + i];
-        f[u] = a.kflag[(int64_t)(sl + 8 * u) * n + i];
+        x[u] = a.kpart[(int64_t)(sl + kFinG * u) * n + i];
+        f[u] = a.kflag[(int64_t)(sl + kFinG * u) * n + i];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
         if (f[u] == 0) exact_add(acc, x[u]);
       }
     }
-    for (; sl < a.kslabs; sl += 8) {
+    for (; sl < a.kslabs; sl += kFinG) {
       const uint32_t f = a.kflag[(int64_t)sl * n + i];
       flagged |= f;
       if (f == 0) exact_add(acc, a.kpart[(int64_t)sl * n + i]);
@@ -275,12 +276,12 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
   st[g][el] = flagged;
   const bool any_in_group = __syncthreads_or(flagged != 0) != 0;
   uint32_t mine = 0;                               // some slab flagged this thread's element
-  for (int gg = 0; gg < 8; ++gg) mine |= st[gg][el];
+  for (int gg = 0; gg < kFinG; ++gg) mine |= st[gg][el];
   if (g == 0 && valid && mine == 0) {
     int64_t tot[kLimbs];
     for (int k = 0; k < kLimbs; ++k) {
       int64_t t = 0;
-      for (int gg = 0; gg < 8; ++gg) t += lim[gg][el][k];
+      for (int gg = 0; gg < kFinG; ++gg) t += lim[gg][el][k];
       tot[k] = t;
     }
     a.k_mean[i] = (float)(exact_round(tot) / (double)a.N);
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
     for (int c = 0; c < a.n_chunks; ++c) {
       const ChunkDesc& cd = a.ch[c];
       const T* col = reinterpret_cast<const T*>(cd.k) + b * cd.k_sb + h * cd.k_sh + d;
-      for (int64_t j = g; j < cd.len; j += 8) {
+      for (int64_t j = g; j < cd.len; j += kFinG) {
         const double x = (double)load_elem(col + j * cd.k_ss);
         if (isnan(x)) bits |= 1u;
         else if (isinf(x)) bits |= x > 0 ? 2u : 4u;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(BoundsArgs a) {
     uint32_t all = 0;
     int64_t tot[kLimbs];
     for (int k = 0; k < kLimbs; ++k) tot[k] = 0;
-    for (int gg = 0; gg < 8; ++gg) {
+    for (int gg = 0; gg < kFinG; ++gg) {
       all |= st[gg][el];
       exact_normalize(lim[gg][el]);                // each group's limbs into digits first
       for (int k = 0; k < kLimbs; ++k) tot[k] += lim[gg][el][k];
@@ -707,7 +708,7 @@ void launch_typed(const BoundsArgs& a, hipStream_t s) {
     const int hpg = a.H < kBoundsHeads ? a.H : kBoundsHeads;
     kmean_partial_kernel<T><<<dim3((unsigned)a.kslabs, (unsigned)a.B, groups), hpg * (a.D / 8), 0, s>>>(a);
     const int64_t n = (int64_t)a.B * a.H * a.D;
-    kmean_final_kernel<T><<<(unsigned)((n + 31) / 32), 256, 0, s>>>(a);
+    kmean_final_kernel<T><<<(unsigned)((n + kFinE - 1) / kFinE), 256, 0, s>>>(a);
   }
   constexpr int W = NormGeom<T>::kWaves;
   const int64_t n_hq = (a.H + W - 1) / W;
