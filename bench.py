@@ -3,8 +3,9 @@
 One step = the whole hot path for one ring rank: fixedm_bounds, run init, then one
 fixedm_attn_fwd_final over the visiting K/V chunks in ring order 0, 3, 2, 1 (the chunks
 folded with the accumulators resident in registers, and the output written as bf16 by the
-same launch).  With --per-chunk a step is instead one fixedm_attn_fwd per chunk and a
-separate fixedm_finalize, as a ring rank receiving one chunk at a time would run it.
+same launch).  With --per-chunk a step is instead one call per chunk, as a ring rank
+receiving one chunk at a time would run it: fixedm_attn_fwd for each chunk but the last,
+and fixedm_attn_fwd_final for the last one (which writes the output).
 Inputs are seeded synthetic tensors at the Wan2.2 720p rank-share shape (40 heads,
 head_dim 128, 18,900 resident queries, 75,600 keys in 4 chunks), resident in HBM before
 the timed region starts.  Prints one JSON line.
@@ -158,8 +159,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-chunk", action="store_true",
-                    help="one fixedm_attn_fwd per ring chunk + fixedm_finalize instead of one "
-                         "fixedm_attn_fwd_final over all chunks")
+                    help="one call per ring chunk (fixedm_attn_fwd, then fixedm_attn_fwd_final for "
+                         "the last) instead of one fixedm_attn_fwd_final over all chunks")
     ap.add_argument("--fallback", default="none",
                     help="which q-blocks take the online-softmax body: 'none' (the workload as "
                          "drawn), 'all' (one V element set to 300 fails the |v| <= 256 check, so "
@@ -244,10 +245,12 @@ def main():
         for c in range(n_attn):
             if timed_idx is not None:
                 ev[timed_idx * n_attn + c][0].record(stream)
-            F.attn_fwd(desc, run, q, [ks[c]], [vs[c]], ws, stream=stream)
+            if c + 1 < n_attn:
+                F.attn_fwd(desc, run, q, [ks[c]], [vs[c]], ws, stream=stream)
+            else:
+                F.attn_fwd_final(desc, run, q, [ks[c]], [vs[c]], ws, out, None, stream=stream)
             if timed_idx is not None:
                 ev[timed_idx * n_attn + c][1].record(stream)
-        F.finalize(desc, run, ws, out, None, stream=stream)
         return desc
 
     log(f"bench: warmup {args.warmup}")
@@ -307,7 +310,7 @@ def main():
             "fallback": args.fallback, "loud_qblocks": loud_blocks,
             "step": (f"bounds + attn_fwd_final over the {len(ks)} ring chunks (output written by "
                      "the attention launch)" if fused else
-                     f"bounds + {len(ks)} x attn_fwd (one per ring chunk) + finalize"),
+                     f"bounds + {len(ks) - 1} x attn_fwd + attn_fwd_final (one call per ring chunk)"),
         },
         "roofline": {
             "kernel": "attn_bf16_d128_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",

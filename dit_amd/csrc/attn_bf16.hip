@@ -147,6 +147,189 @@ __device__ inline float online_slack(const AttnArgs& a) {
   return (float)(s < 0 ? 0 : s > 8 ? 8 : s);
 }
 
+// Sets a work item's accumulators in the registers the assembly passes keep O in, o[n][m] in
+// a[16 (4 n + m) .. + 15]: zero when `load` is 0, else the state saved in the workspace (its
+// register order: 16 bytes per lane at ((n 4 + m) 4 + j) KB + 16 lane from the wave's 32 KB),
+// loaded straight into those registers and waited for inside the block.
+__device__ __attribute__((always_inline)) inline void init_acc(f32x16 (&o)[2][4], const float* wave_base, int lane,
+                                                               uint32_t load) {
+  const uint64_t s0 = uniform_u64((uint64_t)(uintptr_t)wave_base);
+  const uint64_t s1 = s0 + 16384;
+  const uint32_t v0 = 16u * (uint32_t)lane, v1 = v0 + 4096u, v2 = v0 + 8192u, v3 = v0 + 12288u;
+  const uint32_t ld = __builtin_amdgcn_readfirstlane(load);
+  asm volatile(
+      "s_cmp_eq_u32 %[ld], 0\n"
+      "s_cbranch_scc1 L_init_acc_zero_%=\n"
+      "global_load_dwordx4 a[0:3], %[v0], %[s0] offset:0\n"
+      "global_load_dwordx4 a[4:7], %[v0], %[s0] offset:1024\n"
+      "global_load_dwordx4 a[8:11], %[v0], %[s0] offset:2048\n"
+      "global_load_dwordx4 a[12:15], %[v0], %[s0] offset:3072\n"
+      "global_load_dwordx4 a[16:19], %[v1], %[s0] offset:0\n"
+      "global_load_dwordx4 a[20:23], %[v1], %[s0] offset:1024\n"
+      "global_load_dwordx4 a[24:27], %[v1], %[s0] offset:2048\n"
+      "global_load_dwordx4 a[28:31], %[v1], %[s0] offset:3072\n"
+      "global_load_dwordx4 a[32:35], %[v2], %[s0] offset:0\n"
+      "global_load_dwordx4 a[36:39], %[v2], %[s0] offset:1024\n"
+      "global_load_dwordx4 a[40:43], %[v2], %[s0] offset:2048\n"
+      "global_load_dwordx4 a[44:47], %[v2], %[s0] offset:3072\n"
+      "global_load_dwordx4 a[48:51], %[v3], %[s0] offset:0\n"
+      "global_load_dwordx4 a[52:55], %[v3], %[s0] offset:1024\n"
+      "global_load_dwordx4 a[56:59], %[v3], %[s0] offset:2048\n"
+      "global_load_dwordx4 a[60:63], %[v3], %[s0] offset:3072\n"
+      "global_load_dwordx4 a[64:67], %[v0], %[s1] offset:0\n"
+      "global_load_dwordx4 a[68:71], %[v0], %[s1] offset:1024\n"
+      "global_load_dwordx4 a[72:75], %[v0], %[s1] offset:2048\n"
+      "global_load_dwordx4 a[76:79], %[v0], %[s1] offset:3072\n"
+      "global_load_dwordx4 a[80:83], %[v1], %[s1] offset:0\n"
+      "global_load_dwordx4 a[84:87], %[v1], %[s1] offset:1024\n"
+      "global_load_dwordx4 a[88:91], %[v1], %[s1] offset:2048\n"
+      "global_load_dwordx4 a[92:95], %[v1], %[s1] offset:3072\n"
+      "global_load_dwordx4 a[96:99], %[v2], %[s1] offset:0\n"
+      "global_load_dwordx4 a[100:103], %[v2], %[s1] offset:1024\n"
+      "global_load_dwordx4 a[104:107], %[v2], %[s1] offset:2048\n"
+      "global_load_dwordx4 a[108:111], %[v2], %[s1] offset:3072\n"
+      "global_load_dwordx4 a[112:115], %[v3], %[s1] offset:0\n"
+      "global_load_dwordx4 a[116:119], %[v3], %[s1] offset:1024\n"
+      "global_load_dwordx4 a[120:123], %[v3], %[s1] offset:2048\n"
+      "global_load_dwordx4 a[124:127], %[v3], %[s1] offset:3072\n"
+      "s_waitcnt vmcnt(0)\n"
+      "s_branch L_init_acc_done_%=\n"
+      "L_init_acc_zero_%=:\n"
+      "v_accvgpr_write_b32 a0, 0\n"
+      "v_accvgpr_write_b32 a1, 0\n"
+      "v_accvgpr_write_b32 a2, 0\n"
+      "v_accvgpr_write_b32 a3, 0\n"
+      "v_accvgpr_write_b32 a4, 0\n"
+      "v_accvgpr_write_b32 a5, 0\n"
+      "v_accvgpr_write_b32 a6, 0\n"
+      "v_accvgpr_write_b32 a7, 0\n"
+      "v_accvgpr_write_b32 a8, 0\n"
+      "v_accvgpr_write_b32 a9, 0\n"
+      "v_accvgpr_write_b32 a10, 0\n"
+      "v_accvgpr_write_b32 a11, 0\n"
+      "v_accvgpr_write_b32 a12, 0\n"
+      "v_accvgpr_write_b32 a13, 0\n"
+      "v_accvgpr_write_b32 a14, 0\n"
+      "v_accvgpr_write_b32 a15, 0\n"
+      "v_accvgpr_write_b32 a16, 0\n"
+      "v_accvgpr_write_b32 a17, 0\n"
+      "v_accvgpr_write_b32 a18, 0\n"
+      "v_accvgpr_write_b32 a19, 0\n"
+      "v_accvgpr_write_b32 a20, 0\n"
+      "v_accvgpr_write_b32 a21, 0\n"
+      "v_accvgpr_write_b32 a22, 0\n"
+      "v_accvgpr_write_b32 a23, 0\n"
+      "v_accvgpr_write_b32 a24, 0\n"
+      "v_accvgpr_write_b32 a25, 0\n"
+      "v_accvgpr_write_b32 a26, 0\n"
+      "v_accvgpr_write_b32 a27, 0\n"
+      "v_accvgpr_write_b32 a28, 0\n"
+      "v_accvgpr_write_b32 a29, 0\n"
+      "v_accvgpr_write_b32 a30, 0\n"
+      "v_accvgpr_write_b32 a31, 0\n"
+      "v_accvgpr_write_b32 a32, 0\n"
+      "v_accvgpr_write_b32 a33, 0\n"
+      "v_accvgpr_write_b32 a34, 0\n"
+      "v_accvgpr_write_b32 a35, 0\n"
+      "v_accvgpr_write_b32 a36, 0\n"
+      "v_accvgpr_write_b32 a37, 0\n"
+      "v_accvgpr_write_b32 a38, 0\n"
+      "v_accvgpr_write_b32 a39, 0\n"
+      "v_accvgpr_write_b32 a40, 0\n"
+      "v_accvgpr_write_b32 a41, 0\n"
+      "v_accvgpr_write_b32 a42, 0\n"
+      "v_accvgpr_write_b32 a43, 0\n"
+      "v_accvgpr_write_b32 a44, 0\n"
+      "v_accvgpr_write_b32 a45, 0\n"
+      "v_accvgpr_write_b32 a46, 0\n"
+      "v_accvgpr_write_b32 a47, 0\n"
+      "v_accvgpr_write_b32 a48, 0\n"
+      "v_accvgpr_write_b32 a49, 0\n"
+      "v_accvgpr_write_b32 a50, 0\n"
+      "v_accvgpr_write_b32 a51, 0\n"
+      "v_accvgpr_write_b32 a52, 0\n"
+      "v_accvgpr_write_b32 a53, 0\n"
+      "v_accvgpr_write_b32 a54, 0\n"
+      "v_accvgpr_write_b32 a55, 0\n"
+      "v_accvgpr_write_b32 a56, 0\n"
+      "v_accvgpr_write_b32 a57, 0\n"
+      "v_accvgpr_write_b32 a58, 0\n"
+      "v_accvgpr_write_b32 a59, 0\n"
+      "v_accvgpr_write_b32 a60, 0\n"
+      "v_accvgpr_write_b32 a61, 0\n"
+      "v_accvgpr_write_b32 a62, 0\n"
+      "v_accvgpr_write_b32 a63, 0\n"
+      "v_accvgpr_write_b32 a64, 0\n"
+      "v_accvgpr_write_b32 a65, 0\n"
+      "v_accvgpr_write_b32 a66, 0\n"
+      "v_accvgpr_write_b32 a67, 0\n"
+      "v_accvgpr_write_b32 a68, 0\n"
+      "v_accvgpr_write_b32 a69, 0\n"
+      "v_accvgpr_write_b32 a70, 0\n"
+      "v_accvgpr_write_b32 a71, 0\n"
+      "v_accvgpr_write_b32 a72, 0\n"
+      "v_accvgpr_write_b32 a73, 0\n"
+      "v_accvgpr_write_b32 a74, 0\n"
+      "v_accvgpr_write_b32 a75, 0\n"
+      "v_accvgpr_write_b32 a76, 0\n"
+      "v_accvgpr_write_b32 a77, 0\n"
+      "v_accvgpr_write_b32 a78, 0\n"
+      "v_accvgpr_write_b32 a79, 0\n"
+      "v_accvgpr_write_b32 a80, 0\n"
+      "v_accvgpr_write_b32 a81, 0\n"
+      "v_accvgpr_write_b32 a82, 0\n"
+      "v_accvgpr_write_b32 a83, 0\n"
+      "v_accvgpr_write_b32 a84, 0\n"
+      "v_accvgpr_write_b32 a85, 0\n"
+      "v_accvgpr_write_b32 a86, 0\n"
+      "v_accvgpr_write_b32 a87, 0\n"
+      "v_accvgpr_write_b32 a88, 0\n"
+      "v_accvgpr_write_b32 a89, 0\n"
+      "v_accvgpr_write_b32 a90, 0\n"
+      "v_accvgpr_write_b32 a91, 0\n"
+      "v_accvgpr_write_b32 a92, 0\n"
+      "v_accvgpr_write_b32 a93, 0\n"
+      "v_accvgpr_write_b32 a94, 0\n"
+      "v_accvgpr_write_b32 a95, 0\n"
+      "v_accvgpr_write_b32 a96, 0\n"
+      "v_accvgpr_write_b32 a97, 0\n"
+      "v_accvgpr_write_b32 a98, 0\n"
+      "v_accvgpr_write_b32 a99, 0\n"
+      "v_accvgpr_write_b32 a100, 0\n"
+      "v_accvgpr_write_b32 a101, 0\n"
+      "v_accvgpr_write_b32 a102, 0\n"
+      "v_accvgpr_write_b32 a103, 0\n"
+      "v_accvgpr_write_b32 a104, 0\n"
+      "v_accvgpr_write_b32 a105, 0\n"
+      "v_accvgpr_write_b32 a106, 0\n"
+      "v_accvgpr_write_b32 a107, 0\n"
+      "v_accvgpr_write_b32 a108, 0\n"
+      "v_accvgpr_write_b32 a109, 0\n"
+      "v_accvgpr_write_b32 a110, 0\n"
+      "v_accvgpr_write_b32 a111, 0\n"
+      "v_accvgpr_write_b32 a112, 0\n"
+      "v_accvgpr_write_b32 a113, 0\n"
+      "v_accvgpr_write_b32 a114, 0\n"
+      "v_accvgpr_write_b32 a115, 0\n"
+      "v_accvgpr_write_b32 a116, 0\n"
+      "v_accvgpr_write_b32 a117, 0\n"
+      "v_accvgpr_write_b32 a118, 0\n"
+      "v_accvgpr_write_b32 a119, 0\n"
+      "v_accvgpr_write_b32 a120, 0\n"
+      "v_accvgpr_write_b32 a121, 0\n"
+      "v_accvgpr_write_b32 a122, 0\n"
+      "v_accvgpr_write_b32 a123, 0\n"
+      "v_accvgpr_write_b32 a124, 0\n"
+      "v_accvgpr_write_b32 a125, 0\n"
+      "v_accvgpr_write_b32 a126, 0\n"
+      "v_accvgpr_write_b32 a127, 0\n"
+      "L_init_acc_done_%=:\n"
+      : "={a[0:15]}"(o[0][0]), "={a[16:31]}"(o[0][1]), "={a[32:47]}"(o[0][2]), "={a[48:63]}"(o[0][3]),
+        "={a[64:79]}"(o[1][0]), "={a[80:95]}"(o[1][1]), "={a[96:111]}"(o[1][2]), "={a[112:127]}"(o[1][3])
+      : [s0] "s"(s0), [s1] "s"(s1), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3), [ld] "s"(ld)
+      : "scc", "memory");
+}
+
 // A work item's pass over its key tiles, in the assembly block of its body: fixed-m with
 // bf16(alpha q) fragments (kFixedR17), fixed-m with the logit factor applied in fp32
 // (kFixedF32), or online softmax (kOnline; shift[] returns each query row's reference r,
@@ -176,7 +359,7 @@ __device__ __attribute__((always_inline)) void run_pass(const AttnArgs& a, uint8
   const uint32_t nt = __builtin_amdgcn_readfirstlane((uint32_t)n_tiles);
   const uint32_t kb4 = (uint32_t)(4 * (l >> 5));
   if (body == kOnline) {
-    float nshift[2] = {INFINITY, INFINITY};
+    float nshift[2] = {-shift[0], -shift[1]};
     online_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha);
     shift[0] = -nshift[0];
     shift[1] = -nshift[1];
@@ -205,6 +388,21 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   const int qlast = q0 < a.Sq ? q0 : a.Sq - 1;
   const int beta = qlast / a.q_block;
   const int64_t bq = (int64_t)bh * a.nqb + beta;
+  // The item's workspace slot: acc in register order (one 1 KB coalesced float4 per (wave,
+  // n, m, j)), l and r per padded query row; parts 1.. of a split tile have their own slots.
+  float* acc_t = a.acc;
+  float* l_t = a.l;
+  float* r_t = a.r;
+  int64_t tb = (int64_t)tile * (kQTile * kD);
+  int64_t row0 = (int64_t)bh * a.sq_pad + q0;
+  if (part > 0) {
+    const int64_t u = (int64_t)(tile - a.n_whole) * (a.parts - 1) + part - 1;
+    acc_t = a.acc_x;
+    l_t = a.l_x;
+    r_t = a.r_x;
+    tb = u * (kQTile * kD);
+    row0 = u * kQTile + wave * 64;
+  }
   // Every load of the set-up is issued before any of its results is used (the item's
   // set-up then costs one memory round trip): the block's flags, shift and bound, the query
   // rows and k_mean.
@@ -276,17 +474,33 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   // The query fragments are read only as MFMA B operands, which may sit in accumulation
   // registers: pin them there so the 256 architectural VGPRs hold S, P and the K/V
   // fragments of the pipeline.
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qf[n][kk]));
+  // (pinned to the exact registers the passes read them from, a[128 + 32 n + 4 kk .. + 3], so
+  // that they never sit where the accumulators are loaded)
+  asm volatile("" : "+{a[128:131]}"(qf[0][0]), "+{a[132:135]}"(qf[0][1]), "+{a[136:139]}"(qf[0][2]),
+                    "+{a[140:143]}"(qf[0][3]), "+{a[144:147]}"(qf[0][4]), "+{a[148:151]}"(qf[0][5]),
+                    "+{a[152:155]}"(qf[0][6]), "+{a[156:159]}"(qf[0][7]), "+{a[160:163]}"(qf[1][0]),
+                    "+{a[164:167]}"(qf[1][1]), "+{a[168:171]}"(qf[1][2]), "+{a[172:175]}"(qf[1][3]),
+                    "+{a[176:179]}"(qf[1][4]), "+{a[180:183]}"(qf[1][5]), "+{a[184:187]}"(qf[1][6]),
+                    "+{a[188:191]}"(qf[1][7]));
 
+  // A run that continues picks up its state where the previous call left it ([CM]
+  // "Accumulate, then normalize once": the accumulators carry across ring steps): O and the
+  // row sum from the workspace (the row sum in the low-half lanes only: the two halves'
+  // sums are added at the end), and on the online body the running reference r (a fixed-m
+  // row's shift is the same in every call).  The pass then just continues the sums.
   f32x16 o[2][4];
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) o[n][m] = f32x16{};
   float lsum[2] = {0.0f, 0.0f};
+  float rprev[2] = {-INFINITY, -INFINITY};
+  if (a.accumulate) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int64_t rowi = row0 + 32 * n + lq;
+      const float lp = l_t[rowi];
+      rprev[n] = r_t[rowi];
+      lsum[n] = hh == 0 ? lp : 0.0f;
+    }
+  }
+  init_acc(o, acc_t + tb + wave * 8192, lane, (uint32_t)a.accumulate);
   float shift[2];
   if (fixed) {
     // the fixed shift: the q-block's m, or (per-row shifts) each query row's own m
@@ -300,7 +514,8 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
       shift[n] = (float)mm + cdot[n];
     }
   } else {
-    shift[0] = shift[1] = -INFINITY;
+    shift[0] = rprev[0];
+    shift[1] = rprev[1];
   }
   if (n_tiles > 0) {
     const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
@@ -311,8 +526,8 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   }
 
   if (a.final_out && !split) {
-    // The run ends with this launch: merge the workspace's earlier keys (if any), normalise
-    // once ([CM] "Accumulate, then normalize once") and write O, and lse, from the accumulator
+    // The run ends with this launch (the accumulators already hold any earlier calls' keys):
+    // normalise once ([CM] "Accumulate, then normalize once") and write O, and lse, from the accumulator
     // registers.  The arithmetic is the finalize kernel's: O = acc / l (IEEE division), bf16 by
     // round-to-nearest-even, lse = ln 2 (r + log2 l).  A lane holds pieces of 4 elements of one
     // query row, rows 10 KB apart across a wave in the usual layout: stored directly, each
@@ -331,32 +546,13 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
     for (int n = 0; n < 2; ++n) {
       const float other = __shfl_xor(lsum[n], 32, 64);
       const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
-      const int64_t rowi = (int64_t)bh * a.sq_pad + q0 + 32 * n + lq;
-      float lnew = ltot, rnew = shift[n], fw = 0.0f, fo = 1.0f;
-      if (a.accumulate) {
-        const float lp = a.l[rowi], rp = a.r[rowi];
-        if (fixed) {
-          lnew = lp + ltot;
-          fw = 1.0f;
-        } else {
-          rnew = fmaxf(rp, shift[n]);
-          fw = rp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(rp - rnew);
-          fo = shift[n] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(shift[n] - rnew);
-          lnew = lp * fw + ltot * fo;
-        }
-      }
+      const float lnew = ltot, rnew = shift[n];
       const int q = q0 + 32 * n + lq;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
-          if (a.accumulate) {
-            const f32x4 prev =
-                *reinterpret_cast<const f32x4*>(a.acc + tb + ((((wave * 2 + n) * 4 + m) * 4 + jj) * 64 + lane) * 4);
-            if (fixed) v = prev + v;
-            else v = prev * fw + v * fo;
-          }
+          const f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
           const float x0 = __fdiv_rn(v[0], lnew), x1 = __fdiv_rn(v[1], lnew);
           const float x2 = __fdiv_rn(v[2], lnew), x3 = __fdiv_rn(v[3], lnew);
           const int r = 32 * n + s_lq, pc = 8 * m + 2 * jj + s_hh;
@@ -390,53 +586,21 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
     return;
   }
 
-  // ---- fold into the workspace: acc in register order (one 1 KB coalesced float4 store
-  // per (wave, n, m, j)), l and r per padded query row (parts 1.. of a split tile: their own
-  // slots).  The first visit of a run writes; later visits add (fixed-m: pure addition) or
-  // rescale-merge (online softmax; a part that has seen no key yet holds r = -inf, l = 0).
-  float* acc_t = a.acc;
-  float* l_t = a.l;
-  float* r_t = a.r;
-  int64_t tb = (int64_t)tile * (kQTile * kD);
-  int64_t row0 = (int64_t)bh * a.sq_pad + q0;
-  if (part > 0) {
-    const int64_t u = (int64_t)(tile - a.n_whole) * (a.parts - 1) + part - 1;
-    acc_t = a.acc_x;
-    l_t = a.l_x;
-    r_t = a.r_x;
-    tb = u * (kQTile * kD);
-    row0 = u * kQTile + wave * 64;
-  }
+  // ---- store the state into the item's workspace slot for the next call or the finalize:
+  // acc, l (the sum of both halves' row sums) and r (the shift, or the online reference; a
+  // part that has seen no key yet holds r = -inf, l = 0).
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const float other = __shfl_xor(lsum[n], 32, 64);
     const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
     const int64_t rowi = row0 + 32 * n + lq;
-    float lnew = ltot, rnew = shift[n], fw = 0.0f, fo = 1.0f;
-    if (a.accumulate) {
-      const float lp = l_t[rowi], rp = r_t[rowi];
-      if (fixed) {
-        lnew = lp + ltot;
-        fw = 1.0f;
-      } else {
-        rnew = fmaxf(rp, shift[n]);
-        fw = rp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(rp - rnew);
-        fo = shift[n] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(shift[n] - rnew);
-        lnew = lp * fw + ltot * fo;
-      }
-    }
+    const float lnew = ltot, rnew = shift[n];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         f32x4* dst = reinterpret_cast<f32x4*>(acc_t + tb + ((((wave * 2 + n) * 4 + m) * 4 + jj) * 64 + lane) * 4);
-        f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
-        if (a.accumulate) {
-          const f32x4 prev = *dst;
-          if (fixed) v = prev + v;
-          else v = prev * fw + v * fo;
-        }
-        *dst = v;
+        *dst = f32x4{o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
       }
     }
     if (hh == 0) {
