@@ -339,7 +339,7 @@ enum Body { kFixedR17, kFixedF32, kOnline };
 __device__ __attribute__((always_inline)) void run_pass(const AttnArgs& a, uint8_t* smem, const uint32_t* pieces,
                                                         int n_tiles, const bf16x8 (&qf)[2][8], f32x16 (&o)[2][4],
                                                         float (&lsum)[2], float (&shift)[2], Body body, int wave,
-                                                        int lane) {
+                                                        int lane, const float* saved) {
   // The lane's offsets are formed from an id the compiler cannot hoist above the assembly
   // block, so they are not kept live (and spilled) around it.
   int tid = wave * 64 + lane;
@@ -358,18 +358,21 @@ __device__ __attribute__((always_inline)) void run_pass(const AttnArgs& a, uint8
   const uint64_t list = uniform_u64((uint64_t)(uintptr_t)pieces);
   const uint32_t nt = __builtin_amdgcn_readfirstlane((uint32_t)n_tiles);
   const uint32_t kb4 = (uint32_t)(4 * (l >> 5));
+  // O starts from the state a previous call saved (its address), or from zero (0)
+  const uint64_t accp = uniform_u64((uint64_t)(uintptr_t)saved);
+  const uint32_t accv = 16u * (uint32_t)l;
   if (body == kOnline) {
     float nshift[2] = {-shift[0], -shift[1]};
-    online_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha);
+    online_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha, accp, accv);
     shift[0] = -nshift[0];
     shift[1] = -nshift[1];
     return;
   }
   const float nshift[2] = {-shift[0], -shift[1]};
   if (body == kFixedR17)
-    fixed_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave);
+    fixed_loop_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, accp, accv);
   else
-    fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha);
+    fixed_loop_fp32a_asm(o, qf, lsum, nshift, koff, voff, lane6, kb4, list, nt, lds_wave, a.alpha, accp, accv);
 }
 
 // One work item: a whole query tile (all tiles of the launch's chunks), or part p of a split
@@ -500,7 +503,6 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
       lsum[n] = hh == 0 ? lp : 0.0f;
     }
   }
-  init_acc(o, acc_t + tb + wave * 8192, lane, (uint32_t)a.accumulate);
   float shift[2];
   if (fixed) {
     // the fixed shift: the q-block's m, or (per-row shifts) each query row's own m
@@ -517,12 +519,17 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
     shift[0] = rprev[0];
     shift[1] = rprev[1];
   }
+  // The pass sets the accumulators itself (zero, or the saved state), so no start value is
+  // kept in registers across it; an item without tiles only takes the saved state.
+  const float* saved = a.accumulate ? acc_t + tb + wave * 8192 : nullptr;
   if (n_tiles > 0) {
     const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
     run_pass(a, smem, pieces, n_tiles, qf, o, lsum, shift, fixed ? (r17 ? kFixedR17 : kFixedF32) : kOnline, wave,
-             lane);
+             lane, saved);
     wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is reused
     barrier();
+  } else {
+    init_acc(o, saved, lane, saved != nullptr ? 1u : 0u);
   }
 
   if (a.final_out && !split) {

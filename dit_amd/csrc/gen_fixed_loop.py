@@ -597,6 +597,31 @@ def fast_check(e: Emitter):
     e.emit("s_cbranch_scc1 L_fixedm_fast_%=")
 
 
+def init_acc(e: Emitter):
+    """O's start value: zero when %[accp] is 0, else the state a previous call saved (the
+    workspace's register order: o[n][m] part j at accp + 16 lane + (16 n + 4 m + j) KB, with
+    %[accv] = 16 lane), loaded straight into O's registers.  The loads are not waited for
+    here: they precede the prologue's tile loads, whose first wait (for tile 0) covers them
+    (vector loads complete in order), and O is first read by the PV products of step 1.
+    v0-v7 (score registers, free until S(0)) hold the eight (n, m) address offsets."""
+    zero, done = e.new_label(), e.new_label()
+    e.emit("s_cmp_eq_u64 %[accp], 0")
+    e.branch("s_cbranch_scc1", zero)
+    for n in range(2):
+        for m in range(4):
+            e.emit(f"v_add_u32 v{4 * n + m}, {4096 * (4 * n + m)}, %[accv]")
+    for n in range(2):
+        for m in range(4):
+            for j in range(4):
+                e.emit(f"global_load_dwordx4 {areg(O_BASE + 16 * (4 * n + m) + 4 * j, 4)}, v{4 * n + m}, "
+                       f"%[accp] offset:{1024 * j}")
+    e.branch("s_branch", done)
+    e.label(zero)
+    for r in range(128):
+        e.emit(f"v_accvgpr_write_b32 a{O_BASE + r}, 0")
+    e.label(done)
+
+
 def generate_variant(variant: str) -> str:
     """One assembly function: "r17", the fixed-m loop on bf16(alpha q); "fp32a", the fixed-m
     loop that applies alpha in fp32 with an FMA per score; "online", the online-softmax loop
@@ -604,6 +629,7 @@ def generate_variant(variant: str) -> str:
     fp32a = variant == "fp32a"
     online = variant == "online"
     e = Emitter()
+    init_acc(e)
     for n in range(2):
         for i in range(16):
             e.emit(f"v_mov_b32 v{SHIFT_BASE + 16 * n + i}, {'0' if fp32a or online else f'v{NSHIFT + n}'}")
@@ -687,7 +713,7 @@ def generate_variant(variant: str) -> str:
     outs = []
     for n in range(2):
         for m in range(4):
-            outs.append(f'"+{{{o_reg(n, m)}}}"(o[{n}][{m}])')
+            outs.append(f'"={{{o_reg(n, m)}}}"(o[{n}][{m}])')
     outs += [f'"+{{v{LSUM}}}"(lsum[0])', f'"+{{v{LSUM + 1}}}"(lsum[1])',
              f'"+{{s[{S_DPTR}:{S_DPTR + 1}]}}"(pieces)', f'"+{{s{S_TCNT}}}"(n_tiles)']
     if online:
@@ -706,7 +732,7 @@ def generate_variant(variant: str) -> str:
     ins += [f'"{{v{KB4}}}"(kb4)']
     if fp32a or online:
         ins += [f'"{{v{ALPHA}}}"(alpha)']
-    ins += [f'"{{s{S_LDS}}}"(lds_wave)']
+    ins += [f'"{{s{S_LDS}}}"(lds_wave)', '[accp] "s"(accp)', '[accv] "v"(accv)']
     clob = ([f"v{i}" for i in range(S_BASE, S_BASE + 64)] + [f"v{i}" for i in range(P_BASE, P_BASE + 32)]
             + [f"v{i}" for i in range(SHIFT_BASE, SHIFT_BASE + 32)] + [f"v{i}" for i in range(V1_VBASE, V1_VBASE + 32)]
             + [f"v{DMA + i}" for i in range(4)] + [f"v{LSUM_HI}", f"v{LSUM_HI + 1}"]
@@ -735,7 +761,8 @@ def generate_variant(variant: str) -> str:
     return f"""// {what}.
 // The whole fixed-m pass of one work item over its n_tiles (>= 1) tiles of 32 keys, the
 // tiles of its chunk pieces in order (the piece descriptor list at `pieces`, ended by a
-// terminator): the prologue (tiles 0 .. 5 loaded, tile 0 waited for and met at a barrier),
+// terminator): O set to zero (accp = 0) or loaded from the state a previous call saved at
+// accp (accv = 16 x lane), the prologue (tiles 0 .. 5 loaded, tile 0 waited for and met at a barrier),
 // S(0), the priming step t = 0, then steps t = 1 .. n_tiles in groups of 8, each turning S(t)
 // into P(t), adding V(t-1) P(t-1) to O and computing S(t+1); the last step completes the PV
 // product of the last tile.  Keys past the last tile are masked (p = 0).  The LDS ring and
@@ -744,7 +771,8 @@ def generate_variant(variant: str) -> str:
 __device__ __attribute__((always_inline)) inline void {name}(
     f32x16 (&o)[2][4], const bf16x8 (&qf)[2][8], float (&lsum)[2], {"float" if online else "const float"} (&nshift)[2],
     const uint32_t (&koff)[8], const uint32_t (&voff)[4], const uint32_t (&lane)[6], uint32_t kb4,
-    uint64_t pieces, uint32_t n_tiles, uint32_t lds_wave{", float alpha" if fp32a or online else ""}) {{
+    uint64_t pieces, uint32_t n_tiles, uint32_t lds_wave{", float alpha" if fp32a or online else ""}, uint64_t accp,
+    uint32_t accv) {{
   asm volatile(
 {body}
       : {join(outs)}

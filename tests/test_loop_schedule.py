@@ -67,8 +67,11 @@ class Machine:
     """Executes the scalar, branch, lane-offset, mask and load instructions of the loop; the
     matrix, LDS-read and exp work is skipped (it does not steer the control flow)."""
 
-    def __init__(self, lines, mem, wave, n_tiles, lds0=0, seed=0):
+    def __init__(self, lines, mem, wave, n_tiles, lds0=0, seed=0, accp=0):
         self.lines = lines
+        self.accp = accp                                 # %[accp]: the saved state's address, or 0
+        self.acc_loads = []                              # (first AGPR, per-lane address)
+        self.acc_zeroed = []                             # AGPRs written with 0
         self.rng = np.random.default_rng(seed)
         self.vcc_bit = 0                                 # the online growth test (data dependent)
         self.rescales = 0
@@ -87,6 +90,7 @@ class Machine:
             self.v[183 + i] = 16 * ((lane & 15) ^ (row & 15))
             self.v[(185, 191)[i]] = 16 * ((lane & 15) ^ ((row & 3) << 2))
         self.v[188] = 4 * (lane >> 5)
+        self.accv = 16 * lane                            # %[accv]
         self.mask = np.zeros((64, 32), dtype=bool)     # v96..v127: True where -inf
         self.vcc = np.zeros(64, dtype=bool)
         self.s[84], self.s[85] = TBL & M32, TBL >> 32
@@ -173,9 +177,17 @@ class Machine:
                 self.pending[lo + i] = self.mem[addr + 4 * i]
                 self.poison.add(lo + i)
             return
+        if op == "global_load_dwordx4":             # O's saved state: a[lo:lo+3], vX, %[accp] offset:K
+            lo, hi = map(int, re.fullmatch(r"a\[(\d+):(\d+)\]", ops[0]).groups())
+            assert hi == lo + 3 and ops[2].startswith("%[accp] offset:")
+            self.acc_loads.append((lo, self.accp + self.vreg(ops[1]) + int(ops[2].split(":")[1])))
+            return
         if op.startswith("s_"):
             # the reads come first, so a pending destination register is caught by wset
-            if op == "s_mov_b64" and ops[1] == "vcc":
+            if op == "s_cmp_eq_u64":
+                assert ops == ["%[accp]", "0"]
+                self.scc = int(self.accp == 0)
+            elif op == "s_mov_b64" and ops[1] == "vcc":
                 self.wpair(ops[0], self.vcc_bit)
             elif op == "s_or_b64" and ops[2] == "vcc":
                 r = self.spair(ops[1]) | self.vcc_bit
@@ -239,8 +251,12 @@ class Machine:
             self.v[int(ops[0][1:])] = np.maximum(int(ops[1]), x) & M32
         elif op == "v_mul_lo_u32":
             self.v[int(ops[0][1:])] = (self.vreg(ops[1]) * self.sreg(ops[2])) & M32
+        elif op == "v_add_u32" and ops[2] == "%[accv]":
+            self.v[int(ops[0][1:])] = (int(ops[1]) + self.accv) & M32
         elif op == "v_add_u32":
             self.v[int(ops[0][1:])] = (self.vreg(ops[1]) + self.vreg(ops[2])) & M32
+        elif op == "v_accvgpr_write_b32" and ops[1] == "0":    # O's zero start (the online
+            self.acc_zeroed.append(int(ops[0][1:]))             # rescale writes registers back)
         elif op == "v_sub_u32":
             self.v[int(ops[0][1:])] = (self.sreg(ops[1]) - self.vreg(ops[2])) & M32
         elif op == "v_cmp_lt_f32_e32":       # the online growth test: either outcome
@@ -269,6 +285,23 @@ class Machine:
                 raise Fault(f"unmodelled write of a tracked register: {ln}")
         else:
             raise Fault(f"unmodelled instruction: {ln}")
+
+
+ACC_BASE = 0x5000_0000_0000
+
+
+def check_acc_init(m, accp):
+    """O's start: all 128 accumulation registers zeroed, or each 4-register group of o[n][m]
+    loaded once from its 16 bytes per lane of the saved state."""
+    lane = np.arange(64)
+    if accp == 0:
+        assert sorted(m.acc_zeroed) == list(range(128)) and not m.acc_loads
+        return
+    assert not m.acc_zeroed and len(m.acc_loads) == 32
+    for lo, addr in m.acc_loads:
+        n, m_, j = lo // 64, (lo // 16) % 4, (lo // 4) % 4
+        assert np.array_equal(addr, accp + 16 * lane + 1024 * (16 * n + 4 * m_ + j)), (lo,)
+    assert sorted(lo for lo, _ in m.acc_loads) == list(range(0, 128, 4))
 
 
 def _tiles(chunks):
@@ -309,8 +342,10 @@ def run_case(gen, lib, lens, strides, parts=1, part=None, waves=(0, 3), variants
     for variant in variants:
         lines = _body(gen.generate_variant(variant))
         for wave in waves:
-            m = Machine(lines, mem, wave, n_tiles, seed=wave + 7 * n_tiles)
+            accp = ACC_BASE if (wave + n_tiles) % 2 else 0   # both ways O starts
+            m = Machine(lines, mem, wave, n_tiles, seed=wave + 7 * n_tiles, accp=accp)
             m.run()
+            check_acc_init(m, accp)
             if variant == "online" and n_tiles >= 4:
                 assert m.rescales > 0       # the out-of-line accumulator rescale ran
             assert m.barriers == n_tiles + 2
