@@ -73,7 +73,8 @@ def to_dev(arr, dtype, torch, np):
 
 def cpu_baseline(inp, seconds: float):
     """The oracle as it stands, timed on the host on a bounded sample of the same workload:
-    whole 256-row q-blocks of successive heads against all N keys, until `seconds` pass."""
+    whole 256-row q-blocks of successive heads against all N keys, until `seconds` pass or
+    every block has been timed (then the sample is the whole workload)."""
     import numpy as np
     import oracle as O
     try:
@@ -92,7 +93,8 @@ def cpu_baseline(inp, seconds: float):
     elapsed = 0.0
     h = 0
     beta = 0
-    while elapsed < seconds:
+    n_blocks = -(-wl.sq // 256)
+    while elapsed < seconds and beta < n_blocks:
         kh = np.concatenate([f32(c[:, :, h:h + 1]) for c in K], axis=1)
         vh = np.concatenate([f32(c[:, :, h:h + 1]) for c in V], axis=1)
         qh = f32(inp.q_store[:, :, h:h + 1])

@@ -52,3 +52,13 @@ def test_committed_traffic_record_is_well_formed():
         t = json.load(fh)
     assert len(t["kernel_source_sha256_16"]) == 16
     assert t["hbm_bytes_per_launch"] > 1.99e9                            # at least the algorithmic bytes
+
+
+def test_cpu_baseline_stops_after_the_whole_workload():
+    """A workload the oracle finishes inside the time budget is timed once, whole: every
+    query row of every head exactly once, and a positive rate."""
+    from dit_amd import workloads as WL
+    inp = WL.generic_inputs(3, "bf16", 1, 2, 64, 300, (100, 50), q_block=64)
+    r = bench.cpu_baseline(inp, seconds=1000.0)
+    assert r["value"] > 0
+    assert r["sample"].startswith(f"{2 * 300} query rows (whole 256-row q-blocks over 2 heads)")
