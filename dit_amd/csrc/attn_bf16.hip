@@ -135,16 +135,22 @@ __device__ inline DmaLane dma_lane(int wave, int lane) {
 #include "fixed_loop.inc"
 
 // How far (base 2) the online body lets a row's maximum run ahead of its reference before it
-// raises the reference (word 19 of every piece descriptor): s = clamp(127 - ceil(log2 N) - ceil(log2 max|v|), 0, 8), so that
-// N 2^s max|v| <= 2^127 and the accumulators stay finite wherever those of exact online
-// softmax (s = 0) do.  max|v| is 256 when the V check passed, else the largest |v| it
-// recorded (non-finite: s = 0; the output is then not finite anyway).
+// raises the reference (word 19 of every piece descriptor): s = clamp(127 - ceil(log2 N) -
+// ceil(log2 max|v|), 0, kMaxSlack), so that N 2^s max|v| <= 2^127 and the accumulators stay
+// finite wherever those of exact online softmax (s = 0) do.  The larger s, the rarer the
+// raises (each rescales the row sums and, out of line, the accumulators), but the further a
+// sharp row's dominant keys sit above the reference: their probabilities 2^x, x fractional,
+// lose bits to the bf16 rounding of P that the fp32 row sum does not see, where a reference at
+// the row's maximum gives the top key exactly 1.  kMaxSlack = 8 keeps that small.  max|v| is
+// 256 when the V check passed, else the largest |v| it recorded (non-finite: s = 0; the output
+// is then not finite anyway).
+constexpr int kMaxSlack = 8;
 __device__ inline float online_slack(const AttnArgs& a) {
   const uint32_t vb = (uint32_t)__builtin_amdgcn_readfirstlane(*a.v_bad);
   if (vb >= 0x7f800000u) return 0.0f;
   const int log2_v = vb == 0 ? 8 : (int)(vb >> 23) - 127 + ((vb & 0x7fffffu) != 0 ? 1 : 0);
   const int s = 127 - a.log2_n - log2_v;
-  return (float)(s < 0 ? 0 : s > 8 ? 8 : s);
+  return (float)(s < 0 ? 0 : s > kMaxSlack ? kMaxSlack : s);
 }
 
 // Sets a work item's accumulators in the registers the assembly passes keep O in, o[n][m] in
