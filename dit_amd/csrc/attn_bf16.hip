@@ -656,6 +656,10 @@ __device__ inline QueueRange queue_range(const AttnArgs& a, int q) {
 // entries in slow_list), every workgroup drains that list before its queues (queue[kSlowTaken]
 // counts takes), and queue takes skip them.
 constexpr int kSlowCount = kQueues, kSlowTaken = kQueues + 1;
+// Items taken so far (every successful take adds one): a workgroup whose own queue is empty
+// reads it once and, when every item is taken, stops without trying the other queues one
+// after another (a device-wide round trip each).
+constexpr int kTakenTotal = kQueues + 2;
 
 __device__ inline bool tile_is_slow(const AttnArgs& a, int64_t tile) {
   const int64_t bh = tile / a.n_qtiles;
@@ -676,12 +680,22 @@ __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) 
     const unsigned long long n_slow = __hip_atomic_load(a.queue + kSlowCount, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long i = n_slow > 0 ? atomicAdd(a.queue + kSlowTaken, 1ull) : n_slow;
-    if (i < n_slow) return a.slow_list[i];
+    if (i < n_slow) {
+      atomicAdd(a.queue + kTakenTotal, 1ull);
+      return a.slow_list[i];
+    }
     dead |= 1u << kQueues;
   }
+  bool checked = false;
   for (int k = 0; k < kQueues; ++k) {
     const int q = (xcc + k) % kQueues;
     if ((dead >> q) & 1u) continue;
+    if (q != xcc && !checked) {
+      checked = true;
+      const int64_t n_items = a.n_whole + (int64_t)(a.B * a.H * a.n_qtiles - a.n_whole) * a.parts;
+      if ((int64_t)__hip_atomic_load(a.queue + kTakenTotal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_items)
+        return -1;
+    }
     const QueueRange r = queue_range(a, q);
     const int64_t j = (int64_t)atomicAdd(a.queue + q, 1ull);
     if (j >= r.size) {
@@ -692,6 +706,7 @@ __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) 
       --k;                                          // this queue again
       continue;
     }
+    atomicAdd(a.queue + kTakenTotal, 1ull);
     return j < r.nw ? r.w0 + j : a.n_whole + r.p0 + (j - r.nw);
   }
   return -1;
@@ -739,7 +754,7 @@ __global__ __launch_bounds__(256) void prep_kernel(AttnArgs a, int64_t lists) {
   if (blockIdx.x == 0) {
     __shared__ unsigned int n_slow;
     if (threadIdx.x == 0) n_slow = 0;
-    if (threadIdx.x <= kSlowTaken) a.queue[threadIdx.x] = 0ull;
+    if (threadIdx.x <= kTakenTotal) a.queue[threadIdx.x] = 0ull;
     __syncthreads();
     for (int64_t t = threadIdx.x; t < a.n_whole; t += blockDim.x)
       if (tile_is_slow(a, t)) a.slow_list[atomicAdd(&n_slow, 1u)] = (int32_t)t;

@@ -162,7 +162,8 @@ struct AttnArgs {
   int32_t accumulate;  // 0: these keys open the run (initialise); 1: merge into workspace
   int32_t n_whole, parts;      // split plan (bf16 kernel)
   unsigned long long* queue;   // bf16 kernel: 8 work-queue counters, the slow-list length and
-                               // take counter (set up before each launch)
+                               // take counter, the count of items taken (set up before each
+                               // launch; 16 slots)
   int32_t* slow_list;          // bf16 kernel: whole tiles taken first (room for every tile)
   uint32_t* ptable;            // bf16 kernel: chunk-piece descriptor lists [B*H][kPieceLists]
                                // [kPieceSlots][kPieceWords] (written before each launch)
