@@ -271,6 +271,18 @@ def test_split_grid_tail(F):
     assert ob.elig.any() and not ob.elig.all()
 
 
+def test_split_part_without_keys_in_a_later_call(F):
+    """The split grid tail again (37 heads x 8 query tiles: the last 40 tiles in 4 parts), with
+    a 60-key chunk (2 tiles) as the second of three per-chunk calls: parts 0 and 2 of every
+    split tile (key tiles [2 p / 4, 2 (p + 1) / 4)) get none in a call that continues the run,
+    so they take their saved state and store it back unchanged; the result must still be the
+    whole sequence's (loud rows put online-softmax waves into those parts too)."""
+    say("edge: a split part with no keys in a continuing call")
+    ob, _ = _generic(F, 48, "bf16", 1, 37, 128, 2048, (700, 60, 1301), q_block=64,
+                     loud_rows=(35, 0, 64, 14.0))
+    assert ob.elig.any() and not ob.elig.all()
+
+
 @pytest.mark.parametrize("chunks", [
     (448, 480, 481),          # 14, 15 and 15 + 1 tiles: no assembly group, one group, one + partial
     (735, 0, 736, 1000),      # 22 and 23 full tiles (one / two groups) and an empty chunk
