@@ -39,6 +39,10 @@
 //   * Persistent workgroups (one per compute unit) take work items from per-XCD queues:
 //     each XCD works through consecutive tiles of the same heads (sharing the K/V stream in
 //     its L2) and, once its queue is empty, takes work from the others.
+//   * A call that continues a run starts each work item from the state the previous call
+//     saved in the workspace (the loop loads it straight into its accumulation registers);
+//     the run's last call writes O itself, each wave staging its rows through the idle ring
+//     so that every store instruction writes whole rows.
 #include <math.h>
 
 #include "fixedm_internal.h"
