@@ -419,6 +419,15 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   // Every load of the set-up is issued before any of its results is used (the item's
   // set-up then costs one memory round trip): the block's flags, shift and bound, the query
   // rows and k_mean.
+  // The pass starts by reading the item's first chunk-piece descriptor with scalar loads: its
+  // two cache lines are requested here, beside the set-up's loads, so that read hits the scalar
+  // cache instead of adding a memory round trip of its own.
+  const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
+  // (every list of the table is written before the launch, so this read is in bounds also for
+  // an item without tiles; the table does not change during the launch)
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32;
+  const const_u32 pieces_u = reinterpret_cast<const_u32>(uniform_u64((uint64_t)(uintptr_t)pieces));
+  const uint32_t prefetched = pieces_u[0] ^ pieces_u[16];
   const uint32_t elig_raw = a.elig[bq];
   const int m_raw = a.m[bq];
   const double u_raw = a.u[bq];
@@ -437,6 +446,9 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
     for (int i = 0; i < 2; ++i) kmv[kk][i] = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * hh + 4 * i);
+  // (the descriptor lines are taken here, after every set-up load has been issued: their wait
+  // overlaps the set-up's own)
+  asm volatile("" ::"s"(prefetched));
   // The body is chosen per wave: make the choice visibly wave-uniform (a scalar branch), so
   // no wave steps through the other body's code with an empty exec mask (that code holds
   // barriers and assembly that keeps its state in fixed registers).
@@ -444,7 +456,9 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   const int mshift = __builtin_amdgcn_readfirstlane(m_raw);
   // Eligible blocks with a bound above kR17MaxU take the fixed-m body with the logit factor
   // applied in fp32: the rounding of bf16(alpha q) moves a base-2 logit by up to 2^-8 U.
-  const bool r17 = fixed && __builtin_amdgcn_readfirstlane((int)(u_raw <= kR17MaxU)) != 0;
+  // (a branch-free test: the bound's load then stays beside the other set-up loads instead of
+  // being issued, and waited for, only after the eligibility flag has arrived)
+  const bool r17 = __builtin_amdgcn_readfirstlane((int)((elig_raw != 0) & (u_raw <= kR17MaxU))) != 0;
 
   // resident query fragments (B operand of S^T = K Q^T) and the centring term q . k_mean.
   // The fixed-m assembly body takes its logits in base 2 straight from the MFMA: its query
@@ -533,7 +547,6 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   // kept in registers across it; an item without tiles only takes the saved state.
   const float* saved = a.accumulate ? acc_t + tb + wave * 8192 : nullptr;
   if (n_tiles > 0) {
-    const uint32_t* pieces = a.ptable + ((int64_t)bh * kPieceLists + (split ? 1 + part : 0)) * kPieceSlots * kPieceWords;
     run_pass(a, smem, pieces, n_tiles, qf, o, lsum, shift, fixed ? (r17 ? kFixedR17 : kFixedF32) : kOnline, wave,
              lane, saved);
     wait_vmcnt<0>();   // the ring's trailing loads land before the workgroup's LDS is reused
@@ -545,8 +558,8 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
   if (a.final_out && !split) {
     // The run ends with this launch (the accumulators already hold any earlier calls' keys):
     // normalise once ([CM] "Accumulate, then normalize once") and write O, and lse, from the accumulator
-    // registers.  The arithmetic is the finalize kernel's: O = acc / l (IEEE division), bf16 by
-    // round-to-nearest-even, lse = ln 2 (r + log2 l).  A lane holds pieces of 4 elements of one
+    // registers.  The arithmetic is the finalize kernel's: O = acc times the correctly rounded
+    // 1 / l, bf16 by round-to-nearest-even, lse = ln 2 (r + log2 l).  A lane holds pieces of 4 elements of one
     // query row, rows 10 KB apart across a wave in the usual layout: stored directly, each
     // instruction would touch 64 rows.  So each wave stages its 64 rows in its own 32 KB of the
     // (now idle) ring, 32 pieces a row at piece p ^ (row mod 32), and stores whole rows: lane L
@@ -563,15 +576,14 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
     for (int n = 0; n < 2; ++n) {
       const float other = __shfl_xor(lsum[n], 32, 64);
       const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
-      const float lnew = ltot, rnew = shift[n];
+      const float lnew = ltot, rnew = shift[n], rl = row_recip(lnew);
       const int q = q0 + 32 * n + lq;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
-          const float x0 = __fdiv_rn(v[0], lnew), x1 = __fdiv_rn(v[1], lnew);
-          const float x2 = __fdiv_rn(v[2], lnew), x3 = __fdiv_rn(v[3], lnew);
+          const float x0 = v[0] * rl, x1 = v[1] * rl, x2 = v[2] * rl, x3 = v[3] * rl;
           const int r = 32 * n + s_lq, pc = 8 * m + 2 * jj + s_hh;
           uint8_t* dst = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
           if (f32out) {
@@ -678,18 +690,24 @@ __device__ inline bool tile_is_slow(const AttnArgs& a, int64_t tile) {
 
 // Takes the next item for a workgroup on XCD `xcc` (one thread calls it): a listed slow tile,
 // else the front of its own queue, else the front of the others in turn.  `dead` marks
-// queues seen empty (bit kQueues: the slow list).  -1: none left.
+// queues seen empty (bit kQueues: the slow list; bit kQueues + 1: the launch has no slow
+// tile, so a queue take needs no look at the tile's blocks).  -1: none left.
 __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) {
   if (!((dead >> kQueues) & 1u)) {
     const unsigned long long n_slow = __hip_atomic_load(a.queue + kSlowCount, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long i = n_slow > 0 ? atomicAdd(a.queue + kSlowTaken, 1ull) : n_slow;
-    if (i < n_slow) {
-      atomicAdd(a.queue + kTakenTotal, 1ull);
-      return a.slow_list[i];
+    if (n_slow == 0) {
+      dead |= 3u << kQueues;
+    } else {
+      const unsigned long long i = atomicAdd(a.queue + kSlowTaken, 1ull);
+      if (i < n_slow) {
+        atomicAdd(a.queue + kTakenTotal, 1ull);
+        return a.slow_list[i];
+      }
+      dead |= 1u << kQueues;
     }
-    dead |= 1u << kQueues;
   }
+  const bool any_slow = !((dead >> (kQueues + 1)) & 1u);
   bool checked = false;
   for (int k = 0; k < kQueues; ++k) {
     const int q = (xcc + k) % kQueues;
@@ -706,7 +724,7 @@ __device__ inline int64_t take_item(const AttnArgs& a, int xcc, uint32_t& dead) 
       dead |= 1u << q;
       continue;
     }
-    if (j < r.nw && tile_is_slow(a, r.w0 + j)) {   // listed: taken from the slow list
+    if (any_slow && j < r.nw && tile_is_slow(a, r.w0 + j)) {   // listed: taken from the slow list
       --k;                                          // this queue again
       continue;
     }

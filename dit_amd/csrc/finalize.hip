@@ -1,4 +1,5 @@
-// Finalize: O = acc / l once at the end, cast to the output dtype, optional log-sum-exp.
+// Finalize: O = acc / l once at the end (acc times the correctly rounded 1 / l), cast to the
+// output dtype, optional log-sum-exp.
 //
 // Sources (page title, section):
 //   [CM] "Kernel reference: ring_attention_const_max_fwd const-max ring attention",
@@ -68,8 +69,8 @@ __global__ void finalize_reg_kernel(FinalizeArgs a) {
     }
     r = rm;
   }
-  const float4 v = make_float4(__fdiv_rn(acc.x, l), __fdiv_rn(acc.y, l), __fdiv_rn(acc.z, l), __fdiv_rn(acc.w, l));
-  store4(a, bh / a.H, q, bh % a.H, d0, v);
+  const float rl = row_recip(l);
+  store4(a, bh / a.H, q, bh % a.H, d0, make_float4(acc.x * rl, acc.y * rl, acc.z * rl, acc.w * rl));
   if (a.lse != nullptr && m == 0 && jj == 0 && lane < 32)
     a.lse[(int64_t)bh * a.Sq + q] = lse_of(r, l);
 }
@@ -87,8 +88,8 @@ __global__ void finalize_row_kernel(FinalizeArgs a) {
   const int64_t rowi = (int64_t)bh * a.sq_pad + q;
   const float l = a.l[rowi];
   const float4 acc = reinterpret_cast<const float4*>(a.acc + rowi * a.D)[c4];
-  const float4 v = make_float4(__fdiv_rn(acc.x, l), __fdiv_rn(acc.y, l), __fdiv_rn(acc.z, l), __fdiv_rn(acc.w, l));
-  store4(a, bh / a.H, q, bh % a.H, 4 * c4, v);
+  const float rl = row_recip(l);
+  store4(a, bh / a.H, q, bh % a.H, 4 * c4, make_float4(acc.x * rl, acc.y * rl, acc.z * rl, acc.w * rl));
   if (a.lse != nullptr && c4 == 0) a.lse[(int64_t)bh * a.Sq + q] = lse_of(a.r[rowi], l);
 }
 

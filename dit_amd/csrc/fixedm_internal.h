@@ -210,6 +210,12 @@ __device__ inline uint32_t bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The output row is acc times the correctly rounded reciprocal of its row sum l: within 1.5
+// ulp of the fp32 quotient acc / l, one multiply an element instead of a division each (the
+// reciprocal is formed once a row).  The fused epilogue of the bf16 attention kernel and the
+// finalize kernels all form it this way, so every output path gives the same bits.
+__device__ inline float row_recip(float l) { return __fdiv_rn(1.0f, l); }
+
 // Natural-log log-sum-exp of a row from its base-2 shift r and its row sum l under r.
 __device__ inline float lse_of(float r, float l) {
   return 0.69314718055994531f * (r + log2f(l));
