@@ -430,7 +430,8 @@ fixedm_status check_out_call(const fixedm_problem& p, fixedm_tensor out, int32_t
 
 SplitPlan plan_of(const fixedm_problem& p, const WorkspaceLayout& wl) {
   const int64_t tiles = p.batch * p.heads * wl.n_qtiles;
-  return p.dtype == FIXEDM_BF16 ? split_plan(tiles, device_cus()) : SplitPlan{(int32_t)tiles, 1};
+  return p.dtype == FIXEDM_BF16 ? split_plan(tiles, device_cus(), (p.sk_total + 31) / 32)
+                                : SplitPlan{(int32_t)tiles, 1};
 }
 
 AttnArgs attn_args(const fixedm_bounds_t* bounds, fixedm_tensor q, void* workspace) {

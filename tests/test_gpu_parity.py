@@ -261,10 +261,11 @@ def test_mixed_bodies_with_assembly_loop(F):
 
 
 def test_split_grid_tail(F):
-    """37 heads x 8 query tiles = 296 tiles: on a 256-CU device the last 40 run as 4 key-range
-    parts each.  The first chunk (60 keys) leaves parts 0 and 1 of every split tile empty on
-    the visit that initialises the workspace, and a loud query block puts online-softmax waves
-    into split tiles (tail tiles belong to heads 32-36), so the finalize merges both kinds."""
+    """37 heads x 8 query tiles = 296 tiles: on a 256-CU device the last 40 run as 6 key-range
+    parts each.  In the per-chunk runs the first chunk (60 keys, 2 tiles) leaves parts 0, 1, 3
+    and 4 of every split tile empty on the visit that initialises the workspace, and a loud
+    query block puts online-softmax waves into split tiles (tail tiles belong to heads 32-36),
+    so the finalize merges both kinds."""
     say("edge: split grid tail")
     ob, _ = _generic(F, 47, "bf16", 1, 37, 128, 2048, (60, 700, 1301), q_block=64,
                      loud_rows=(35, 0, 64, 14.0))
@@ -272,9 +273,9 @@ def test_split_grid_tail(F):
 
 
 def test_split_part_without_keys_in_a_later_call(F):
-    """The split grid tail again (37 heads x 8 query tiles: the last 40 tiles in 4 parts), with
-    a 60-key chunk (2 tiles) as the second of three per-chunk calls: parts 0 and 2 of every
-    split tile (key tiles [2 p / 4, 2 (p + 1) / 4)) get none in a call that continues the run,
+    """The split grid tail again (37 heads x 8 query tiles: the last 40 tiles in 6 parts on a
+    256-CU device), with a 60-key chunk (2 tiles) as the second of three per-chunk calls: parts
+    0, 1, 3 and 4 of every split tile (key tiles [2 p / 6, 2 (p + 1) / 6)) get none in a call that continues the run,
     so they take their saved state and store it back unchanged; the result must still be the
     whole sequence's (loud rows put online-softmax waves into those parts too)."""
     say("edge: a split part with no keys in a continuing call")
