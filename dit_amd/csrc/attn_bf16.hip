@@ -45,6 +45,8 @@
 //     so that every store instruction writes whole rows.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fixedm_internal.h"
 
 namespace fixedm {
@@ -565,53 +567,56 @@ __device__ __attribute__((always_inline)) void process_item(const AttnArgs& a, u
     // (now idle) ring, 32 pieces a row at piece p ^ (row mod 32), and stores whole rows: lane L
     // of instruction i writes piece L mod 32 of row 2 i + L / 32 (8 bytes bf16, 16 bytes fp32).
     const int64_t tb = (int64_t)tile * (kQTile * kD);
-    const bool f32out = a.out_dtype == FIXEDM_F32;
-    const uint32_t pbytes = f32out ? 16u : 8u;
     // staging offsets from an id the compiler cannot hoist above the assembly block
     int sid = threadIdx.x;
     asm volatile("" : "+v"(sid));
     const int s_lane = sid & 63, s_lq = s_lane & 31, s_hh = s_lane >> 5;
     uint8_t* stage = smem + (sid >> 6) * 32768;
+    // one code path per output type (no test of the type inside the loops)
+    const auto write_out = [&](auto f32tag) {
+      constexpr bool f32out = decltype(f32tag)::value;
+      constexpr uint32_t pbytes = f32out ? 16u : 8u;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const float other = __shfl_xor(lsum[n], 32, 64);
-      const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
-      const float lnew = ltot, rnew = shift[n], rl = row_recip(lnew);
-      const int q = q0 + 32 * n + lq;
+      for (int n = 0; n < 2; ++n) {
+        const float other = __shfl_xor(lsum[n], 32, 64);
+        const float ltot = hh == 0 ? lsum[n] + other : other + lsum[n];
+        const float lnew = ltot, rnew = shift[n], rl = row_recip(lnew);
+        const int q = q0 + 32 * n + lq;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 4; ++m) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 v = {o[n][m][4 * jj], o[n][m][4 * jj + 1], o[n][m][4 * jj + 2], o[n][m][4 * jj + 3]};
-          const float x0 = v[0] * rl, x1 = v[1] * rl, x2 = v[2] * rl, x3 = v[3] * rl;
-          const int r = 32 * n + s_lq, pc = 8 * m + 2 * jj + s_hh;
-          uint8_t* dst = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
-          if (f32out) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{x0, x1, x2, x3};
-          } else {
-            uint2 w;
-            w.x = bf16_rne(x0) | (bf16_rne(x1) << 16);
-            w.y = bf16_rne(x2) | (bf16_rne(x3) << 16);
-            *reinterpret_cast<uint2*>(dst) = w;
+          for (int jj = 0; jj < 4; ++jj) {
+            const float x0 = o[n][m][4 * jj] * rl, x1 = o[n][m][4 * jj + 1] * rl;
+            const float x2 = o[n][m][4 * jj + 2] * rl, x3 = o[n][m][4 * jj + 3] * rl;
+            const int r = 32 * n + s_lq, pc = 8 * m + 2 * jj + s_hh;
+            uint8_t* dst = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
+            if constexpr (f32out)
+              *reinterpret_cast<f32x4*>(dst) = f32x4{x0, x1, x2, x3};
+            else
+              *reinterpret_cast<uint2*>(dst) = uint2{bf16x2_rne(x0, x1), bf16x2_rne(x2, x3)};
           }
         }
+        if (a.lse != nullptr && hh == 0 && q < a.Sq) a.lse[(int64_t)bh * a.Sq + q] = lse_of(rnew, lnew);
       }
-      if (a.lse != nullptr && hh == 0 && q < a.Sq) a.lse[(int64_t)bh * a.Sq + q] = lse_of(rnew, lnew);
-    }
-    // the wave's own rows only: its LDS writes complete before its reads of them
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // the wave's own rows only: its LDS writes complete before its reads of them
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 8
-    for (int i = 0; i < 32; ++i) {
-      const int r = 2 * i + s_hh, pc = s_lq, q = q0 + r;
-      const uint8_t* src = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
-      if (q < a.Sq) {
-        const int64_t off = b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + 4 * pc;
-        if (f32out)
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = *reinterpret_cast<const f32x4*>(src);
-        else
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = *reinterpret_cast<const uint2*>(src);
+      for (int i = 0; i < 32; ++i) {
+        const int r = 2 * i + s_hh, pc = s_lq, q = q0 + r;
+        const uint8_t* src = stage + (uint32_t)(r * 32 + (pc ^ (r & 31))) * pbytes;
+        if (q < a.Sq) {
+          const int64_t off = b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + 4 * pc;
+          if constexpr (f32out)
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = *reinterpret_cast<const f32x4*>(src);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = *reinterpret_cast<const uint2*>(src);
+        }
       }
-    }
+    };
+    if (a.out_dtype == FIXEDM_F32)
+      write_out(std::true_type{});
+    else
+      write_out(std::false_type{});
     return;
   }
 

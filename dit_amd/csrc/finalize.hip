@@ -25,8 +25,8 @@ __device__ inline void store4(const FinalizeArgs& a, int b, int q, int h, int d0
   } else {
     uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + b * a.o_sb + (int64_t)q * a.o_ss + h * a.o_sh + d0;
     uint2 w;
-    w.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
-    w.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+    w.x = bf16x2_rne(v.x, v.y);
+    w.y = bf16x2_rne(v.z, v.w);
     *reinterpret_cast<uint2*>(o) = w;
   }
 }

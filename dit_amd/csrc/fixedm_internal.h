@@ -215,12 +215,19 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 int device_cus();   // compute units of the current device (cached per device)
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN -> quiet NaN); the output cast of both the
-// finalize kernel and the fused finalize of the bf16 attention kernel.
-__device__ inline uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values to a packed bf16 pair (lo in bits 0..15) by the hardware conversion
+// (v_cvt_pk_bf16_f32): round-to-nearest-even for every value that is not a NaN (subnormals, ties
+// and the overflow to infinity included; checked against the bit formula on 2^20 values), and a
+// NaN stays a quiet NaN of the same sign.  The output cast of both the finalize kernel and the
+// fused finalize of the bf16 attention kernel.
+__device__ inline uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t x = {lo, hi};
+  const bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+  uint32_t w;
+  __builtin_memcpy(&w, &y, 4);
+  return w;
 }
 
 // The output row is acc times the correctly rounded reciprocal of its row sum l: within 1.5

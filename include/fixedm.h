@@ -244,7 +244,7 @@ fixedm_status fixedm_attn_fwd_final(const fixedm_bounds_t* bounds, fixedm_run_t*
 
 /* O = acc / l (in fp32 as acc times the correctly rounded 1 / l, within 1.5 ulp of the
  * quotient; fixedm_attn_fwd_final forms it the same way), cast to out_dtype (bf16 by
- * round-to-nearest-even, or fp32), written to
+ * round-to-nearest-even, a NaN staying a quiet NaN; or fp32), written to
  * out [B, sq, H, D]; if lse is non-NULL also lse[b, h, i] = ln2 * (r_i + log2 l_i), the
  * natural-log log-sum-exp of row i ([CM] Interface table, training output), as a
  * contiguous fp32 [B, H, sq] device array.  Requires run->kv_visited == sk_total

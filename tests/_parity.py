@@ -141,3 +141,12 @@ def out_bound_bf16(q, k_all, v_all, scale: float, ref) -> np.ndarray:
 def bf16_rne_bits(x_f32: np.ndarray) -> np.ndarray:
     from dit_amd.workloads import bf16_bits_from_f32
     return bf16_bits_from_f32(x_f32)
+
+
+def assert_bf16_is_rne(bits: np.ndarray, x_f32: np.ndarray):
+    """bf16 output bits are the round-to-nearest-even of the fp32 output wherever that is not a
+    NaN; where it is a NaN they are a NaN too (the payload is not fixed)."""
+    nan = np.isnan(x_f32)
+    assert np.array_equal(bits[~nan], bf16_rne_bits(x_f32)[~nan])
+    b = bits[nan].astype(np.uint32)
+    assert np.all(((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0))

@@ -13,7 +13,7 @@ import pytest
 import oracle as O
 from dit_amd import workloads as WL
 
-from _parity import (LSE_TOL, bf16_rne_bits, check_bounds, check_output, device_inputs,
+from _parity import (LSE_TOL, assert_bf16_is_rne, check_bounds, check_output, device_inputs,
                      gpu_bounds_dict, lse_bound_bf16, out_bound_bf16, say)
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,7 @@ def test_config2_wan_block_bf16(F):
     out16, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, center="none",
                                out_dtype=torch.bfloat16)
     bits = out16.cpu().view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(bits, bf16_rne_bits(got))
+    assert_bf16_is_rne(bits, got)
 
 
 def _sample_rows(sq, q_block, seed=7):
@@ -516,7 +516,7 @@ def test_config2_fused(F):
     # the fused bf16 output is the round-to-nearest-even of the fused fp32 output
     out16, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, out_dtype=torch.bfloat16, **FUSED)
     bits = out16.cpu().view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(bits, bf16_rne_bits(got))
+    assert_bf16_is_rne(bits, got)
     # per-chunk folds through the workspace: the same result up to fp32 summation order
     unfused, _, _, _ = F.forward(dev[0], dev[1], dev[2], q_block=256, out_dtype=torch.float32)
     assert np.abs(unfused.cpu().numpy() - got).max() <= 1e-5
