@@ -926,3 +926,71 @@ def test_key_mean_nonfinite_keys(F):
     assert np.isnan(ob.k_mean[0, 0, 5]) and np.isnan(ob.k_mean[0, 1, 2]) and ob.k_mean[0, 2, 9] == np.inf
     assert not ob.elig[0, :3].any() and ob.elig[0, 3].all()
     check_bounds(gpu_bounds_dict(desc, buf), ob)
+
+
+def _bf16_keys_test(F, seed, chunks, make_keys, H=2, Sq=96, check_out=True):
+    """bf16, COMPUTE centring, keys from make_keys(rng, shape) (fp32, rounded to bf16): the
+    bounds (k_mean, K2, U, m, mask) bit-exact against the oracle, and the output within
+    tolerance where check_out."""
+    import torch
+    B, D = 1, 128
+    inp = WL.generic_inputs(seed, "bf16", B, H, D, Sq, chunks, q_block=64, center="compute")
+    rng = np.random.default_rng(seed + 1000)
+    k = make_keys(rng, (B, sum(chunks), H, D)).astype(np.float32)
+    kb = WL.bf16_bits_from_f32(k)
+    inp.k_store = [np.ascontiguousarray(c) for c in np.split(kb, np.cumsum(chunks)[:-1], axis=1)]
+    q, ks, vs, _ = device_inputs(inp)
+    out, lse, desc, buf = F.forward(q, ks, vs, q_block=64, center="compute", out_dtype=torch.float32,
+                                    want_lse=True)
+    torch.cuda.synchronize()
+    ob = O.bounds(inp.q, inp.k, inp.v, scale=O.default_scale(D), q_block=64, center="compute", dtype="bf16")
+    check_bounds(gpu_bounds_dict(desc, buf), ob)
+    if check_out:
+        ref, _ = O.attention(inp.q, np.concatenate(inp.k, 1), np.concatenate(inp.v, 1), O.default_scale(D))
+        check_output(out.cpu().numpy(), ref, "bf16")
+    return ob
+
+
+def test_k2_keys_at_one_distance(F):
+    """bf16 keys all at (nearly) the same distance from their mean, as RMS-normalised keys are:
+    the largest centred norm is decided by the last bits of the fp64 sums; k_mean, K2, U, m and
+    the mask bit-exact, the output within tolerance."""
+    say("K2: keys at one distance from the mean")
+
+    def keys(rng, shape):
+        u = rng.standard_normal(shape)
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        return 0.5 + 8.0 * u
+
+    _bf16_keys_test(F, 91, (9000, 7000), keys)
+
+
+def test_k2_keys_with_a_shifted_first_part(F):
+    """The first 2,048 keys sit 3 units above the rest in every dimension (a mean far from both
+    groups, the largest centred norms in the first group): bounds bit-exact, output within
+    tolerance."""
+    say("K2: keys with a shifted first part")
+
+    def keys(rng, shape):
+        k = rng.standard_normal(shape)
+        k[:, :2048] += 3.0
+        return k
+
+    _bf16_keys_test(F, 92, (3000, 2500), keys)
+
+
+def test_k2_nonfinite_bf16_keys(F):
+    """bf16 keys with a NaN (head 0) and an infinity (head 1) under COMPUTE centring: those
+    heads' key means and K2 are not finite, as the oracle has them; head 2 is finite: bounds
+    bit-exact, its blocks eligible."""
+    say("K2: non-finite bf16 keys")
+
+    def keys(rng, shape):
+        k = rng.standard_normal(shape)
+        k[0, 100, 0, 7] = np.nan
+        k[0, 3000, 1, 40] = np.inf
+        return k
+
+    ob = _bf16_keys_test(F, 93, (2500, 1700), keys, H=3, check_out=False)
+    assert not np.isfinite(ob.k2[0, 0]) and not np.isfinite(ob.k2[0, 1]) and np.isfinite(ob.k2[0, 2])
+    assert ob.elig[0, 2].all()
