@@ -5,6 +5,7 @@
 
 #include "../../include/fixedm.h"
 #include "pieces.h"
+#include "split_plan.h"
 
 namespace fixedm {
 
@@ -12,50 +13,12 @@ constexpr int kMaxChunksPerLaunch = 8;   // K/V chunks folded by one attention l
 constexpr int kMaxBoundsChunks = 32;     // chunks one fixedm_bounds call accepts
 constexpr int kBoundsHeads = 64;         // heads one bounds workgroup covers (LDS staging)
 constexpr int kQTile = 256;              // query rows per attention workgroup (4 waves x 64)
-constexpr int kMaxParts = 8;             // key-range parts of a split tail tile (bf16 kernel)
 constexpr int kPieceWords = kPieceDescWords;   // dwords of one chunk-piece descriptor (bf16 kernel)
 constexpr int kPieceSlots = kMaxChunksPerLaunch + 1;   // descriptors of a list, terminator included
 constexpr int kPieceLists = 1 + kMaxParts;            // lists per (b, h): whole tiles, then each part
-constexpr int kMaxSplitTail = 255;       // most tail tiles that are split
 constexpr int64_t kMaxKeys = (int64_t)1 << 38;   // most keys of a problem (and of a chunk)
 constexpr int64_t kMaxKeysBf16 = (int64_t)1 << 35;   // most keys of a bf16 problem
 constexpr int64_t kMaxRowStrideBf16 = (int64_t)1 << 26;   // largest sequence stride of a bf16 tensor
-
-// Grid-tail split of the bf16 attention launch.  The tiles fill whole rounds of one
-// workgroup per compute unit; the remaining `tail` tiles would leave most CUs idle for a
-// whole round, so each is cut into `parts` key ranges run by separate workgroups, whose
-// partial sums the finalize merges.  parts minimises the expected end of the launch past
-// its whole rounds, in tiles:
-//   eps rounds + max(rounds / parts, tail / cus + min(drift, 1 / (2 parts)))
-// with rounds = ceil(tail parts / cus), the parts a CU runs; eps the fixed cost of a work item
-// (taking it, its set-up, the ring fill, the state store: ~24 key-tile steps, measured) over
-// the tile's key tiles; and drift the spread of the CUs' finishing times after the whole
-// rounds (the XCDs' clocks differ under load: ~2% of the elapsed rounds, measured), which the
-// dynamic taking of the parts evens out down to about half a part.  Depends on the tile
-// count, the run's key count and the CU count only, so every launch of a run and its finalize
-// agree.
-struct SplitPlan {
-  int32_t n_whole, parts;
-};
-inline SplitPlan split_plan(int64_t tiles, int cus, int64_t key_tiles) {
-  SplitPlan sp{(int32_t)tiles, 1};
-  if (cus <= 0) return sp;
-  const int64_t tail = tiles % cus;
-  if (tail == 0 || tail > kMaxSplitTail) return sp;
-  const double w = (double)tail / cus;
-  const double drift = 0.02 * (double)(tiles / cus);
-  const double eps = 24.0 / (double)(key_tiles > 1 ? key_tiles : 1);
-  double best = 0.0;
-  for (int p = 1; p <= kMaxParts; ++p) {
-    const int64_t rounds = (tail * p + cus - 1) / cus;
-    const double spread = drift < 0.5 / p ? drift : 0.5 / p;
-    const double end = (double)rounds / p > w + spread ? (double)rounds / p : w + spread;
-    const double cost = eps * (double)rounds + end;
-    if (p == 1 || cost < best - 1e-9) { best = cost; sp.parts = p; }
-  }
-  if (sp.parts > 1) sp.n_whole = (int32_t)(tiles - tail);
-  return sp;
-}
 
 // Key slabs of the k_mean reduction: about 256 workgroups of B x head groups (with 640-thread
 // workgroups that fills the chip; more slabs only lengthen the final reduction), at most one
